@@ -1,0 +1,18 @@
+"""Plain fp64 CPU oracle for the causal MLA attention core (test infrastructure).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg use this
+package. The library under ``attention_mla_causal_amd`` never imports it, and
+this package imports nothing from the library.
+"""
+
+from .mla_oracle import (  # noqa: F401
+    QK_NOPE_HEAD_DIM,
+    QK_ROPE_HEAD_DIM,
+    V_HEAD_DIM,
+    Q_HEAD_DIM,
+    bf16_bits_to_f64,
+    causal_mask_4d,
+    attention_probs,
+    mla_attention,
+    mla_attention_rows,
+)

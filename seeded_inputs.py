@@ -1,0 +1,135 @@
+"""Seeded synthetic inputs for the MLA attention core, shared by tests and bench.
+
+This module only draws numbers; it holds none of the attention arithmetic, so
+both the fp64 oracle and the HIP library can be fed from it without sharing
+any code with each other.
+
+Workloads are shaped like the tensors on the Kimi K2 pages: 64 heads, 128
+non-rotary + 64 rotary query/key dims with one rotary key shared by all heads,
+128 value dims, bf16. The pages never give the distribution of these
+activations, so they are i.i.d. normal draws.
+
+Host recipe (all small and medium workloads):
+  SeedSequence(seed).spawn(5) -> one child per tensor, in the order
+  q_nope, q_pe, k_nope, k_pe, v; each child spawns one grandchild per batch
+  index b; PCG64(grandchild).standard_normal(float32) * std; rounded to bf16
+  with round-to-nearest-even on the fp32 bits; kept as uint16 bit patterns.
+  Per-batch streams let a test regenerate a single batch of a large workload.
+
+Device recipe (workloads whose inputs exceed a few GiB of host work, i.e. the
+batched decode): torch.Generator on the device seeded with `seed`, then for
+each tensor in the same order torch.randn(float32) * std rounded to bf16 by
+torch's round-to-nearest-even conversion. Tests copy the sampled slices of
+these inputs back to the host for the oracle.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+NOPE, ROPE, VDIM = 128, 64, 128
+TENSORS = ("q_nope", "q_pe", "k_nope", "k_pe", "v")
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    T: int
+    past_len: int
+    std: float = 1.0
+    # 192^-0.5 rounded to fp32; the scale is a 32-bit float at the C ABI.
+    softmax_scale: float = float(np.float32(192.0 ** -0.5))
+
+    @property
+    def S(self) -> int:
+        return self.past_len + self.T
+
+    def shapes(self) -> dict:
+        B, H, T, S = self.B, self.H, self.T, self.S
+        return {
+            "q_nope": (B, H, T, NOPE),
+            "q_pe": (B, H, T, ROPE),
+            "k_nope": (B, H, S, NOPE),
+            "k_pe": (B, 1, S, ROPE),
+            "v": (B, H, S, VDIM),
+        }
+
+
+# The five workloads: a tiny prefill, decode exactly as the "Similarities"
+# page shows it (64 heads, 1 query, p=1000 -> 1001 keys), a batched decode, a
+# causal prefill and a chunked prefill on top of a cache. "N(0,2)" for the
+# chunked prefill is read as variance 2 (std sqrt 2).
+WORKLOADS = {
+    "tiny_prefill": Workload("tiny_prefill", B=1, H=4, T=16, past_len=0),
+    "decode_p1000": Workload("decode_p1000", B=1, H=64, T=1, past_len=1000),
+    "batched_decode": Workload("batched_decode", B=32, H=64, T=1, past_len=8191),
+    "causal_prefill": Workload("causal_prefill", B=1, H=64, T=4096, past_len=0),
+    "chunked_prefill": Workload("chunked_prefill", B=1, H=64, T=2048, past_len=14336,
+                                std=float(np.sqrt(2.0))),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (round to nearest, ties to even); uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    nan = (u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    r = np.where(nan, (u >> np.uint32(16)) | np.uint32(0x40), r)
+    return r.astype(np.uint16)
+
+
+def _batch_rng(seed: int, tensor: str, B: int, b: int) -> np.random.Generator:
+    child = np.random.SeedSequence(seed).spawn(len(TENSORS))[TENSORS.index(tensor)]
+    grand = child.spawn(B)[b]
+    return np.random.Generator(np.random.PCG64(grand))
+
+
+def tensor_batch(shape, tensor: str, b: int, seed: int = 0, std: float = 1.0) -> np.ndarray:
+    """One batch slice [shape[1:]] of one tensor as bf16 bits (host recipe)."""
+    g = _batch_rng(seed, tensor, shape[0], b)
+    x = g.standard_normal(shape[1:], dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return f32_to_bf16_bits(x)
+
+
+def host_inputs(wl: Workload, seed: int = 0, std: float | None = None) -> dict:
+    """All five inputs of a workload as uint16 bf16 bit arrays (host recipe)."""
+    std = wl.std if std is None else std
+    out = {}
+    for name, shape in wl.shapes().items():
+        arr = np.empty(shape, dtype=np.uint16)
+        for b in range(shape[0]):
+            arr[b] = tensor_batch(shape, name, b, seed, std)
+        out[name] = arr
+    return out
+
+
+def random_inputs(B, H, T, past_len, seed=0, std=1.0) -> dict:
+    """Host-recipe inputs for an arbitrary shape (edge-case tests)."""
+    return host_inputs(Workload("custom", B, H, T, past_len, std), seed)
+
+
+def device_inputs(wl: Workload, device, seed: int = 0, std: float | None = None) -> dict:
+    """All five inputs drawn on a torch device (device recipe), bf16 tensors."""
+    import torch
+
+    std = wl.std if std is None else std
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = {}
+    for name, shape in wl.shapes().items():
+        t = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        # draw per batch so the fp32 temporary stays at one batch's size
+        for b in range(shape[0]):
+            x = torch.randn(shape[1:], generator=g, dtype=torch.float32, device=device)
+            if std != 1.0:
+                x.mul_(std)
+            t[b].copy_(x)
+            del x
+        out[name] = t
+    return out
