@@ -1,0 +1,195 @@
+"""Causal multi-head latent attention (MLA) core for AMD Instinct MI355X.
+
+A thin ctypes binding over libmla_attn.so (the C ABI in include/mla_attn.h).
+The functions below only check and marshal arguments: torch supplies device
+memory and the current HIP stream; every step of the attention runs in the
+library's HIP kernels. There is no fallback path: if the library has not been
+built (``python -m attention_mla_causal_amd.build``) importing this package
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla_attn.so")
+
+QK_NOPE_HEAD_DIM = 128
+QK_ROPE_HEAD_DIM = 64
+V_HEAD_DIM = 128
+
+STATUS_NAMES = {
+    0: "MLA_OK",
+    1: "MLA_ERR_NULL",
+    2: "MLA_ERR_SHAPE",
+    3: "MLA_ERR_ALIGN",
+    4: "MLA_ERR_SCALE",
+    5: "MLA_ERR_WORKSPACE",
+    6: "MLA_ERR_DEVICE",
+}
+MLA_ERR_SHAPE = 2
+
+# Exported C symbols and their signatures (kept in step with include/mla_attn.h).
+_VP, _I32, _F32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "mla_attn_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _F32, _VP]),
+    "mla_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "mla_attn_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _F32, _VP]),
+    "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "mla_last_error": (ctypes.c_char_p, []),
+}
+
+
+class MLAError(RuntimeError):
+    """A non-shape failure reported by the library (status code attached)."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build the HIP library first "
+            "(python -m attention_mla_causal_amd.build); there is no non-GPU fallback")
+    try:
+        import torch  # noqa: F401  (load torch's HIP runtime first so the library binds to it)
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = load_library()
+
+
+def _raise_for(status: int, where: str):
+    if status == 0:
+        return
+    detail = _lib.mla_last_error().decode(errors="replace")
+    name = STATUS_NAMES.get(status, f"status {status}")
+    msg = f"{where} failed with {name}: {detail}"
+    if status == MLA_ERR_SHAPE:
+        raise ValueError(msg)
+    raise MLAError(status, msg)
+
+
+def _check_tensor(t, name: str):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4D, got shape {tuple(t.shape)}")
+
+
+def _stream_handle(device):
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _shapes(q_nope, q_pe, k_nope, k_pe, v):
+    for t, n in ((q_nope, "q_nope"), (q_pe, "q_pe"), (k_nope, "k_nope"), (k_pe, "k_pe"), (v, "v")):
+        _check_tensor(t, n)
+    B, H, T, dn = q_nope.shape
+    S = k_nope.shape[2]
+    want = {
+        "q_nope": (B, H, T, QK_NOPE_HEAD_DIM),
+        "q_pe": (B, H, T, QK_ROPE_HEAD_DIM),
+        "k_nope": (B, H, S, QK_NOPE_HEAD_DIM),
+        "k_pe": (B, 1, S, QK_ROPE_HEAD_DIM),
+        "v": (B, H, S, V_HEAD_DIM),
+    }
+    for t, n in ((q_nope, "q_nope"), (q_pe, "q_pe"), (k_nope, "k_nope"), (k_pe, "k_pe"), (v, "v")):
+        if tuple(t.shape) != want[n]:
+            raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {want[n]}")
+    devs = {t.device for t in (q_nope, q_pe, k_nope, k_pe, v)}
+    if len(devs) != 1:
+        raise ValueError(f"inputs are on different devices: {devs}")
+    return B, H, T, S
+
+
+def mla_attn_prefill(q_nope, q_pe, k_nope, k_pe, v, past_len: int, softmax_scale: float, out=None):
+    """Causal MLA attention of T new queries over S = past_len + T keys.
+
+    q_nope [B,H,T,128], q_pe [B,H,T,64], k_nope [B,H,S,128], k_pe [B,1,S,64]
+    (one rotary key for all heads), v [B,H,S,128]; bf16, contiguous, on one
+    GPU. Returns out [B,H,T,128] bf16, enqueued on the current stream.
+    """
+    import torch
+
+    B, H, T, S = _shapes(q_nope, q_pe, k_nope, k_pe, v)
+    if out is None:
+        out = torch.empty((B, H, T, V_HEAD_DIM), dtype=torch.bfloat16, device=q_nope.device)
+    else:
+        _check_tensor(out, "out")
+        if tuple(out.shape) != (B, H, T, V_HEAD_DIM) or out.device != q_nope.device:
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, T, V_HEAD_DIM)}")
+    st = _lib.mla_attn_prefill(
+        q_nope.data_ptr(), q_pe.data_ptr(), k_nope.data_ptr(), k_pe.data_ptr(), v.data_ptr(),
+        out.data_ptr(), B, H, T, S, int(past_len), float(softmax_scale), _stream_handle(q_nope.device))
+    _raise_for(st, "mla_attn_prefill")
+    return out
+
+
+def mla_attn_decode_workspace_bytes(B: int, H: int, S: int) -> int:
+    """Bytes of zero-initialised workspace mla_attn_decode needs for (B, H, S)."""
+    return int(_lib.mla_attn_decode_workspace_bytes(int(B), int(H), int(S)))
+
+
+def mla_attn_decode(q_nope, q_pe, k_nope, k_pe, v, past_len: int, softmax_scale: float,
+                    out=None, workspace=None):
+    """One new query per sequence (T = 1) against S = past_len + 1 keys.
+
+    workspace: a zero-filled uint8 GPU tensor of at least
+    mla_attn_decode_workspace_bytes(B, H, S) bytes, reusable across calls
+    (the library leaves it zero-filled); allocated here when omitted.
+    """
+    import torch
+
+    B, H, T, S = _shapes(q_nope, q_pe, k_nope, k_pe, v)
+    if T != 1:
+        raise ValueError(f"decode takes one query per sequence, got T={T}")
+    if out is None:
+        out = torch.empty((B, H, 1, V_HEAD_DIM), dtype=torch.bfloat16, device=q_nope.device)
+    else:
+        _check_tensor(out, "out")
+        if tuple(out.shape) != (B, H, 1, V_HEAD_DIM) or out.device != q_nope.device:
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, 1, V_HEAD_DIM)}")
+    need = mla_attn_decode_workspace_bytes(B, H, S)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q_nope.device)
+    if not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.mla_attn_decode(
+        q_nope.data_ptr(), q_pe.data_ptr(), k_nope.data_ptr(), k_pe.data_ptr(), v.data_ptr(),
+        out.data_ptr(), workspace.data_ptr(), ws_bytes, B, H, S, int(past_len),
+        float(softmax_scale), _stream_handle(q_nope.device))
+    _raise_for(st, "mla_attn_decode")
+    return out
+
+
+__all__ = [
+    "mla_attn_prefill",
+    "mla_attn_decode",
+    "mla_attn_decode_workspace_bytes",
+    "MLAError",
+    "LIB_PATH",
+    "SIGNATURES",
+    "load_library",
+]

@@ -1,0 +1,61 @@
+"""Build libmla_attn.so in-tree with hipcc for gfx950.
+
+    python -m attention_mla_causal_amd.build
+
+Compiles every HIP source under csrc/ into one shared library next to this
+file. Always recompiles (it is the "does it build" step); loading the
+library never builds it.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB_NAME = "libmla_attn.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+
+SOURCES = ["mla_attn_abi.hip", "mla_prefill.hip", "mla_decode.hip"]
+
+HIP_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-Wall",
+    # Keep the compiler from forming packed-fp32 VALU instructions.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC or install ROCm under /opt/rocm)")
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, *(extra_flags or []), *srcs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(line for line in res.stdout.splitlines()
+                    if "packed-fp32-ops" not in line and "not a recognized feature" not in line)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
+    if verbose and out.strip():
+        print(out, flush=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

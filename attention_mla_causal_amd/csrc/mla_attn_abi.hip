@@ -1,0 +1,119 @@
+// C ABI of the MLA attention core: argument checks on the host, then one
+// kernel launch on the caller's stream. See include/mla_attn.h for the
+// contract of each entry point.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/mla_attn.h"
+#include "mla_host_checks.h"
+#include "mla_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[320] = {0};
+
+void set_error(const char* where, const char* msg) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s", where, msg);
+}
+
+mla_status report(const char* where, const mla::CheckResult& r) {
+  if (r.status != MLA_OK) set_error(where, r.msg);
+  return r.status;
+}
+
+mla_status device_error(const char* where, hipError_t e) {
+  char msg[256];
+  std::snprintf(msg, sizeof(msg), "launch failed: %s", hipGetErrorString(e));
+  set_error(where, msg);
+  return MLA_ERR_DEVICE;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_attn_prefill(const void* q_nope, const void* q_pe, const void* k_nope,
+                            const void* k_pe, const void* v, void* out, int32_t B, int32_t H,
+                            int32_t T, int32_t S, int32_t past_len, float softmax_scale,
+                            void* stream) {
+  const mla::CheckResult r =
+      mla::check_prefill(q_nope, q_pe, k_nope, k_pe, v, out, B, H, T, S, past_len, softmax_scale);
+  if (r.status != MLA_OK) return report("mla_attn_prefill", r);
+  if (r.empty) return MLA_OK;
+  mla::PrefillArgs a;
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.k_nope = static_cast<const uint16_t*>(k_nope);
+  a.k_pe = static_cast<const uint16_t*>(k_pe);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<uint16_t*>(out);
+  a.B = B;
+  a.H = H;
+  a.T = T;
+  a.S = S;
+  a.past_len = past_len;
+  a.ntiles = (int32_t)((T + mla::kPrefillBlockM - 1) / mla::kPrefillBlockM);
+  a.scale_log2 = softmax_scale * kLog2e;
+  const hipError_t e = mla::launch_prefill(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error("mla_attn_prefill", e);
+  return MLA_OK;
+}
+
+size_t mla_attn_decode_workspace_bytes(int32_t B, int32_t H, int32_t S) {
+  return mla::plan_decode(B, H, S).workspace_bytes;
+}
+
+mla_status mla_attn_decode(const void* q_nope, const void* q_pe, const void* k_nope,
+                           const void* k_pe, const void* v, void* out, void* workspace,
+                           size_t workspace_bytes, int32_t B, int32_t H, int32_t S,
+                           int32_t past_len, float softmax_scale, void* stream) {
+  mla::DecodePlan plan;
+  const mla::CheckResult r = mla::check_decode(q_nope, q_pe, k_nope, k_pe, v, out, workspace,
+                                               workspace_bytes, B, H, S, past_len,
+                                               softmax_scale, &plan);
+  if (r.status != MLA_OK) return report("mla_attn_decode", r);
+  if (r.empty) return MLA_OK;
+  mla::DecodeArgs a;
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.k_nope = static_cast<const uint16_t*>(k_nope);
+  a.k_pe = static_cast<const uint16_t*>(k_pe);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<uint16_t*>(out);
+  char* ws = static_cast<char*>(workspace);
+  a.ws_o = plan.nsplit > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ws_ml = plan.nsplit > 1 ? reinterpret_cast<float*>(ws + plan.ws_o_bytes) : nullptr;
+  a.ws_cnt = plan.nsplit > 1
+                 ? reinterpret_cast<uint32_t*>(ws + plan.ws_o_bytes + plan.ws_ml_bytes)
+                 : nullptr;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.nsplit = (int32_t)plan.nsplit;
+  a.keys_per_split = (int32_t)plan.keys_per_split;
+  a.scale_log2 = softmax_scale * kLog2e;
+  const hipError_t e = mla::launch_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error("mla_attn_decode", e);
+  return MLA_OK;
+}
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE";
+    case MLA_ERR_ALIGN: return "MLA_ERR_ALIGN";
+    case MLA_ERR_SCALE: return "MLA_ERR_SCALE";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_DEVICE: return "MLA_ERR_DEVICE";
+  }
+  return "unknown status";
+}
+
+const char* mla_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,293 @@
+// Causal MLA attention, decode (one new query per sequence, S = past_len + 1 keys).
+//
+// The same computation as prefill with T = 1 (the Kimi K2 "Similarities"
+// page shows it in decode mode with p = 1000: scores [B, 64, 1, 1001]); the
+// single query sees every key, so the causal mask is all zeros here. The work
+// is a pair of matrix-vector products per (b, h) and is bound by HBM
+// bandwidth: it reads k_nope and v once (256 + 256 bytes per key and head)
+// and the shared rotary key k_pe (128 bytes per key, once per sequence).
+//
+// gfx950 design:
+//  * A quarter-wave (16 lanes x 16 bytes) covers one 128-dim bf16 key row, so
+//    every wave-wide 128-bit load reads 4 consecutive rows (1 KiB) of k_nope or
+//    v; k_pe rows are 16 lanes x 8 bytes. Streaming loads are non-temporal.
+//  * Each lane keeps 8 query dims (+4 rotary dims) in fp32, forms partial dot
+//    products, and a 4-step DPP reduction inside the quarter-wave gives the
+//    score. Each quarter-wave runs its own online softmax (fp32, exp2 domain)
+//    over the keys it sees and accumulates 8 output dims per lane.
+//  * Quarter-waves, then waves, are merged by log-sum-exp; when the key range
+//    of a (b, h) is split over several workgroups, each writes an fp32
+//    partial (o[128], max, sum) to the workspace and the last workgroup to
+//    arrive (device-scope counter) merges them and writes the bf16 output,
+//    then re-arms the counter to zero. One launch, no second pass.
+//  * Workgroups of one sequence are placed on one XCD so the shared k_pe rows
+//    are served from that XCD's L2 for all heads.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_kernels.h"
+
+namespace mla {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int DN = 128, DR = 64, DV = 128;
+constexpr int NW = 4;            // waves per workgroup
+constexpr int NT = NW * 64;
+constexpr int KEYS_PER_LANE = 4; // keys each quarter-wave takes per trip
+constexpr int KEYS_PER_WAVE = 4 * KEYS_PER_LANE;   // 16
+constexpr int KEYS_PER_TRIP = NW * KEYS_PER_WAVE;  // 64
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xf, 0xf, false));
+}
+
+// Sum over the 16 lanes of a row (quarter-wave); every lane gets the total.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  x += dpp<0x140>(x);  // row_mirror
+  return x;
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) {
+  return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+
+__device__ __forceinline__ uint16_t to_bf16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// exp2(m - ref) that is 0 for an empty partial (m = -inf)
+__device__ __forceinline__ float rescale(float m, float ref) {
+  return m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - ref);
+}
+
+// Merge this lane's (m, l, o[8]) with the lane `mask` away (xor shuffle).
+__device__ __forceinline__ void merge_xor(float& m, float& l, float (&o)[8], int mask) {
+  const float m2 = __shfl_xor(m, mask);
+  const float l2 = __shfl_xor(l, mask);
+  float o2[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(o[e], mask);
+  const float M = fmaxf(m, m2);
+  const float a1 = rescale(m, M), a2 = rescale(m2, M);
+  l = l * a1 + l2 * a2;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = o[e] * a1 + o2[e] * a2;
+  m = M;
+}
+
+__global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
+  __shared__ float red_o[NW][DV];
+  __shared__ float red_ml[NW][2];
+  __shared__ int last_flag;
+
+  const int nwg = gridDim.x;
+  const int wg = blockIdx.x;
+  const int logical = (nwg % 8 == 0) ? (wg % 8) * (nwg / 8) + wg / 8 : wg;
+  const int bh = logical / a.nsplit;
+  const int split = logical % a.nsplit;
+  const int b = bh / a.H;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int cl = lane & 15;   // column slot: dims 8cl..8cl+7 (rotary 4cl..4cl+3)
+  const int qq = lane >> 4;   // quarter-wave
+
+  const int64_t S = a.S;
+  const uint16_t* kn_g = a.k_nope + (int64_t)bh * S * DN + 8 * cl;
+  const uint16_t* v_g = a.v + (int64_t)bh * S * DV + 8 * cl;
+  const uint16_t* kp_g = a.k_pe + (int64_t)b * S * DR + 4 * cl;
+
+  float qn[8], qp[4];
+  {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(a.q_nope + (int64_t)bh * DN + 8 * cl);
+    const u32x2 wp = *reinterpret_cast<const u32x2*>(a.q_pe + (int64_t)bh * DR + 4 * cl);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qn[2 * e] = lo_bf16(w[e]);
+      qn[2 * e + 1] = hi_bf16(w[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      qp[2 * e] = lo_bf16(wp[e]);
+      qp[2 * e + 1] = hi_bf16(wp[e]);
+    }
+  }
+
+  const float c = a.scale_log2;
+  const int64_t s0 = (int64_t)split * a.keys_per_split;
+  const int64_t s1 = (s0 + a.keys_per_split < S) ? s0 + a.keys_per_split : S;
+
+  float m = -INFINITY, l = 0.0f, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.0f;
+
+  for (int64_t base = s0 + wave * KEYS_PER_WAVE; base < s1; base += KEYS_PER_TRIP) {
+    u32x4 kn[KEYS_PER_LANE], vv[KEYS_PER_LANE];
+    u32x2 kp[KEYS_PER_LANE];
+    bool ok[KEYS_PER_LANE];
+#pragma unroll
+    for (int u = 0; u < KEYS_PER_LANE; ++u) {
+      const int64_t key = base + 4 * u + qq;
+      ok[u] = key < s1;
+      if (ok[u]) {
+        kn[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kn_g + key * DN));
+        kp[u] = *reinterpret_cast<const u32x2*>(kp_g + key * DR);
+        vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_g + key * DV));
+      } else {
+        kn[u] = u32x4{0, 0, 0, 0};
+        kp[u] = u32x2{0, 0};
+        vv[u] = u32x4{0, 0, 0, 0};
+      }
+    }
+    float t[KEYS_PER_LANE];
+#pragma unroll
+    for (int u = 0; u < KEYS_PER_LANE; ++u) {
+      float d = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        d = __builtin_fmaf(qn[2 * e], lo_bf16(kn[u][e]), d);
+        d = __builtin_fmaf(qn[2 * e + 1], hi_bf16(kn[u][e]), d);
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        d = __builtin_fmaf(qp[2 * e], lo_bf16(kp[u][e]), d);
+        d = __builtin_fmaf(qp[2 * e + 1], hi_bf16(kp[u][e]), d);
+      }
+      d = row_sum16(d);
+      t[u] = ok[u] ? d * c : -INFINITY;
+    }
+    float mt = t[0];
+#pragma unroll
+    for (int u = 1; u < KEYS_PER_LANE; ++u) mt = fmaxf(mt, t[u]);
+    const float m_new = fmaxf(m, mt);
+    const float ref = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m - ref);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int u = 0; u < KEYS_PER_LANE; ++u) {
+      const float p = __builtin_amdgcn_exp2f(t[u] - ref);
+      l += p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] = __builtin_fmaf(p, lo_bf16(vv[u][e]), o[2 * e]);
+        o[2 * e + 1] = __builtin_fmaf(p, hi_bf16(vv[u][e]), o[2 * e + 1]);
+      }
+    }
+  }
+
+  // ---- merge the four quarter-waves, then the waves
+  merge_xor(m, l, o, 16);
+  merge_xor(m, l, o, 32);
+  if (qq == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red_o[wave][8 * cl + e] = o[e];
+    if (cl == 0) {
+      red_ml[wave][0] = m;
+      red_ml[wave][1] = l;
+    }
+  }
+  __syncthreads();
+
+  // wave 0, lanes 0..15: the workgroup's (m, l, o) for dims 8cl..8cl+7
+  float M = -INFINITY, L = 0.0f, O[8];
+  if (wave == 0 && qq == 0) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, red_ml[w][0]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) O[e] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float sc = rescale(red_ml[w][0], M);
+      L += red_ml[w][1] * sc;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) O[e] += red_o[w][8 * cl + e] * sc;
+    }
+  }
+
+  if (a.nsplit == 1) {
+    if (wave == 0 && qq == 0) {
+      const float inv = 1.0f / L;
+      uint16_t* dst = a.out + (int64_t)bh * DV + 8 * cl;
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (uint32_t)to_bf16_rne(O[2 * e] * inv) | ((uint32_t)to_bf16_rne(O[2 * e + 1] * inv) << 16);
+      *reinterpret_cast<u32x4*>(dst) = w;
+    }
+    return;
+  }
+
+  // ---- split-KV: publish this workgroup's partial, the last arrival merges
+  const int64_t slot = (int64_t)bh * a.nsplit + split;
+  if (wave == 0 && qq == 0) {
+    float* dst = a.ws_o + slot * DV + 8 * cl;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e] = O[e];
+    if (cl == 0) {
+      a.ws_ml[2 * slot] = M;
+      a.ws_ml[2 * slot + 1] = L;
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = atomicAdd(a.ws_cnt + bh, 1u);
+    last_flag = (prev == (uint32_t)(a.nsplit - 1));
+  }
+  __syncthreads();
+  if (!last_flag) return;
+  __threadfence();
+
+  // wave 0: quarter-wave qq merges splits qq, qq+4, ...; then the quarters merge
+  if (wave != 0) return;
+  float mm = -INFINITY, ll = 0.0f, oo[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) oo[e] = 0.0f;
+  for (int sp = qq; sp < a.nsplit; sp += 4) {
+    const int64_t sl = (int64_t)bh * a.nsplit + sp;
+    const float ms = __builtin_nontemporal_load(a.ws_ml + 2 * sl);
+    const float ls = __builtin_nontemporal_load(a.ws_ml + 2 * sl + 1);
+    const float Mn = fmaxf(mm, ms);
+    const float a1 = rescale(mm, Mn), a2 = rescale(ms, Mn);
+    const float* src = a.ws_o + sl * DV + 8 * cl;
+    ll = ll * a1 + ls * a2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) oo[e] = oo[e] * a1 + __builtin_nontemporal_load(src + e) * a2;
+    mm = Mn;
+  }
+  merge_xor(mm, ll, oo, 16);
+  merge_xor(mm, ll, oo, 32);
+  if (qq == 0) {
+    const float inv = 1.0f / ll;
+    uint16_t* dst = a.out + (int64_t)bh * DV + 8 * cl;
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)to_bf16_rne(oo[2 * e] * inv) | ((uint32_t)to_bf16_rne(oo[2 * e + 1] * inv) << 16);
+    *reinterpret_cast<u32x4*>(dst) = w;
+    if (cl == 0) a.ws_cnt[bh] = 0u;  // re-arm for the next call
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  const int grid = a.B * a.H * a.nsplit;
+  hipLaunchKernelGGL(mla_decode_kernel, dim3(grid), dim3(NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

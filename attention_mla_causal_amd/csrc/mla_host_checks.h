@@ -1,0 +1,180 @@
+// Host-side argument checks and launch planning for the MLA attention core.
+//
+// Plain C++17, no HIP headers: the library uses it before any HIP call, and a
+// g++ unit test (with sanitizers) exercises every status code on the CPU.
+//
+// The shape rules follow the attention-core excerpt on the Kimi K2
+// "Similarities" page ("Query-key similarity"): scores must be
+// (B, H, T, kv_seq_len) and the mask (B, 1, T, kv_seq_len), with
+// kv_seq_len = past_len + T, else the call is rejected.
+#ifndef MLA_HOST_CHECKS_H_
+#define MLA_HOST_CHECKS_H_
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/mla_attn.h"
+
+namespace mla {
+
+// Prefill tiling: queries per workgroup. The kernel assumes this value.
+constexpr int64_t kPrefillBlockM = 128;
+// Decode: keys one workgroup consumes per loop trip (4 waves x 4 quarter-waves x 4 keys).
+constexpr int64_t kDecodeKeysPerTrip = 64;
+// Decode split heuristic: aim for this many workgroups (4 per CU on 256 CUs).
+constexpr int64_t kDecodeTargetWorkgroups = 1024;
+constexpr int64_t kMaxGrid = 2147483647;  // grid.x limit
+
+struct DecodePlan {
+  int64_t nsplit = 1;          // workgroups per (b, h)
+  int64_t keys_per_split = 0;  // multiple of kDecodeKeysPerTrip
+  size_t ws_o_bytes = 0;       // fp32 [B*H, nsplit, 128]
+  size_t ws_ml_bytes = 0;      // fp32 pairs (max, sum) [B*H, nsplit]
+  size_t ws_cnt_bytes = 0;     // uint32 arrival counters [B*H]
+  size_t workspace_bytes = 0;  // total, each region 256-byte aligned
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Split the key range of each (b, h) over enough workgroups to fill the chip
+// when B*H alone is too small, never making a split smaller than one trip.
+inline DecodePlan plan_decode(int64_t B, int64_t H, int64_t S) {
+  DecodePlan p;
+  if (B <= 0 || H <= 0 || S <= 0) return p;
+  const int64_t bh = B * H;
+  int64_t nsplit = 1;
+  if (bh < kDecodeTargetWorkgroups / 2) {
+    nsplit = (kDecodeTargetWorkgroups + bh - 1) / bh;
+    const int64_t max_split = (S + kDecodeKeysPerTrip - 1) / kDecodeKeysPerTrip;
+    if (nsplit > max_split) nsplit = max_split;
+    if (nsplit < 1) nsplit = 1;
+  }
+  int64_t kps = (S + nsplit - 1) / nsplit;
+  kps = (kps + kDecodeKeysPerTrip - 1) / kDecodeKeysPerTrip * kDecodeKeysPerTrip;
+  nsplit = (S + kps - 1) / kps;  // every split owns at least one key
+  p.nsplit = nsplit;
+  p.keys_per_split = kps;
+  if (nsplit > 1) {
+    p.ws_o_bytes = align256(size_t(bh) * size_t(nsplit) * 128 * sizeof(float));
+    p.ws_ml_bytes = align256(size_t(bh) * size_t(nsplit) * 2 * sizeof(float));
+    p.ws_cnt_bytes = align256(size_t(bh) * sizeof(uint32_t));
+    p.workspace_bytes = p.ws_o_bytes + p.ws_ml_bytes + p.ws_cnt_bytes;
+  }
+  return p;
+}
+
+struct CheckResult {
+  mla_status status = MLA_OK;
+  bool empty = false;  // valid call with nothing to compute
+  char msg[256] = {0};
+};
+
+inline CheckResult fail(mla_status s, const char* what) {
+  CheckResult r;
+  r.status = s;
+  std::snprintf(r.msg, sizeof(r.msg), "%s", what);
+  return r;
+}
+
+inline bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// Common part of both entry points. T is the number of new queries.
+inline CheckResult check_common(const void* q_nope, const void* q_pe, const void* k_nope,
+                                const void* k_pe, const void* v, const void* out, int64_t B,
+                                int64_t H, int64_t T, int64_t S, int64_t past_len, float scale) {
+  CheckResult r;
+  if (B < 0 || H < 0 || T < 0 || S < 0 || past_len < 0) {
+    std::snprintf(r.msg, sizeof(r.msg),
+                  "negative size: B=%lld H=%lld T=%lld S=%lld past_len=%lld", (long long)B,
+                  (long long)H, (long long)T, (long long)S, (long long)past_len);
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  if (S != past_len + T) {
+    std::snprintf(r.msg, sizeof(r.msg),
+                  "kv_seq_len S=%lld must equal past_len %lld + query length %lld", (long long)S,
+                  (long long)past_len, (long long)T);
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  if (B == 0 || H == 0 || T == 0) {
+    r.empty = true;
+    return r;
+  }
+  // every tensor is non-empty from here on (S >= T >= 1)
+  const void* ptrs[6] = {q_nope, q_pe, k_nope, k_pe, v, out};
+  const char* names[6] = {"q_nope", "q_pe", "k_nope", "k_pe", "v", "out"};
+  for (int i = 0; i < 6; ++i) {
+    if (ptrs[i] == nullptr) {
+      std::snprintf(r.msg, sizeof(r.msg), "%s is NULL", names[i]);
+      r.status = MLA_ERR_NULL;
+      return r;
+    }
+  }
+  for (int i = 0; i < 6; ++i) {
+    if (misaligned(ptrs[i])) {
+      std::snprintf(r.msg, sizeof(r.msg), "%s is not 16-byte aligned", names[i]);
+      r.status = MLA_ERR_ALIGN;
+      return r;
+    }
+  }
+  const float c = scale * 1.4426950408889634f;
+  if (!std::isfinite(scale) || !(scale > 0.0f) || !std::isfinite(c)) {
+    std::snprintf(r.msg, sizeof(r.msg), "softmax_scale %g must be finite and positive",
+                  (double)scale);
+    r.status = MLA_ERR_SCALE;
+    return r;
+  }
+  return r;
+}
+
+inline CheckResult check_prefill(const void* q_nope, const void* q_pe, const void* k_nope,
+                                 const void* k_pe, const void* v, const void* out, int64_t B,
+                                 int64_t H, int64_t T, int64_t S, int64_t past_len, float scale) {
+  CheckResult r = check_common(q_nope, q_pe, k_nope, k_pe, v, out, B, H, T, S, past_len, scale);
+  if (r.status != MLA_OK || r.empty) return r;
+  const int64_t tiles = (T + kPrefillBlockM - 1) / kPrefillBlockM;
+  if (B * H > kMaxGrid / tiles) {
+    std::snprintf(r.msg, sizeof(r.msg), "B*H*ceil(T/128) = %lld*%lld exceeds the grid limit",
+                  (long long)(B * H), (long long)tiles);
+    r.status = MLA_ERR_SHAPE;
+  }
+  return r;
+}
+
+inline CheckResult check_decode(const void* q_nope, const void* q_pe, const void* k_nope,
+                                const void* k_pe, const void* v, const void* out,
+                                const void* workspace, size_t workspace_bytes, int64_t B,
+                                int64_t H, int64_t S, int64_t past_len, float scale,
+                                DecodePlan* plan_out) {
+  CheckResult r = check_common(q_nope, q_pe, k_nope, k_pe, v, out, B, H, 1, S, past_len, scale);
+  if (r.status != MLA_OK || r.empty) return r;
+  const DecodePlan plan = plan_decode(B, H, S);
+  if (B * H > kMaxGrid / plan.nsplit) {
+    std::snprintf(r.msg, sizeof(r.msg), "B*H*nsplit exceeds the grid limit");
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  if (plan.workspace_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) {
+      std::snprintf(r.msg, sizeof(r.msg), "workspace %s: %zu bytes given, %zu needed",
+                    workspace == nullptr ? "is NULL" : "too small", workspace_bytes,
+                    plan.workspace_bytes);
+      r.status = MLA_ERR_WORKSPACE;
+      return r;
+    }
+    if (misaligned(workspace)) {
+      std::snprintf(r.msg, sizeof(r.msg), "workspace is not 16-byte aligned");
+      r.status = MLA_ERR_ALIGN;
+      return r;
+    }
+  }
+  if (plan_out) *plan_out = plan;
+  return r;
+}
+
+}  // namespace mla
+
+#endif  // MLA_HOST_CHECKS_H_

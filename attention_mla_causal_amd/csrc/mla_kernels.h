@@ -1,0 +1,42 @@
+// Device-side launch interface shared by the HIP kernels and the C ABI layer.
+#ifndef MLA_KERNELS_H_
+#define MLA_KERNELS_H_
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct PrefillArgs {
+  const uint16_t* q_nope;  // [B,H,T,128] bf16 bits
+  const uint16_t* q_pe;    // [B,H,T,64]
+  const uint16_t* k_nope;  // [B,H,S,128]
+  const uint16_t* k_pe;    // [B,1,S,64], shared by every head
+  const uint16_t* v;       // [B,H,S,128]
+  uint16_t* out;           // [B,H,T,128]
+  int32_t B, H, T, S, past_len;
+  int32_t ntiles;          // ceil(T / 128)
+  float scale_log2;        // softmax_scale * log2(e)
+};
+
+struct DecodeArgs {
+  const uint16_t* q_nope;  // [B,H,1,128]
+  const uint16_t* q_pe;    // [B,H,1,64]
+  const uint16_t* k_nope;  // [B,H,S,128]
+  const uint16_t* k_pe;    // [B,1,S,64]
+  const uint16_t* v;       // [B,H,S,128]
+  uint16_t* out;           // [B,H,1,128]
+  float* ws_o;             // [B*H, nsplit, 128] partial outputs (nsplit > 1)
+  float* ws_ml;            // [B*H, nsplit, 2] partial (max, sum)
+  uint32_t* ws_cnt;        // [B*H] arrival counters, zero between calls
+  int32_t B, H, S;
+  int32_t nsplit, keys_per_split;
+  float scale_log2;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace mla
+
+#endif  // MLA_KERNELS_H_

@@ -1,0 +1,114 @@
+/*
+ * mla_attn.h - C ABI of the causal multi-head latent attention (MLA) core
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (Kimi K2 pages, "Similarities" page, section "Query-key
+ * similarity", and "Weighted sum of values" page): for every batch b, head h
+ * and new query i < T, with S = past_len + T keys,
+ *
+ *   s[i,j] = sum_{d<128} q_nope[b,h,i,d] * k_nope[b,h,j,d]
+ *          + sum_{d<64}  q_pe[b,h,i,d]   * k_pe[b,0,j,d]
+ *   z[i,j] = softmax_scale * s[i,j]  + (0 if j <= past_len + i else -inf)
+ *   p[i,:] = softmax(z[i,:])                   (fp32)
+ *   out[b,h,i,:] = sum_j p[i,j] * v[b,h,j,:]   (bf16 result)
+ *
+ * The rotary key k_pe is one tensor shared by all heads (the "Scale scores"
+ * section: the joint key-value down-projection emits a single rotary key);
+ * queries sit at absolute positions past_len + i ("Causal mask" page,
+ * "Construct causal mask": positions are numbered from the cached length and
+ * the 4D causal mask is built with it). Head dims are fixed by the released
+ * config ("Embedded state" page, config.json): 128 non-rotary, 64 rotary and
+ * 128 value dims per head. Dropout is the identity (p = 0.0, inference).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensors are bf16, contiguous, row-major, in device memory owned by
+ *    the caller. Shapes: q_nope [B,H,T,128], q_pe [B,H,T,64],
+ *    k_nope [B,H,S,128], k_pe [B,1,S,64], v [B,H,S,128], out [B,H,T,128].
+ *  - Every non-empty tensor pointer must be 16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
+ *    work on it and return without synchronising; ordering against other
+ *    work is the caller's job. The library never allocates or frees memory.
+ *  - All argument checks run on the host before any HIP call; a failing
+ *    call returns a status and enqueues nothing. No exceptions cross the ABI.
+ *    mla_last_error() gives a thread-local description of the last failure.
+ *  - B == 0, H == 0 or T == 0 is a valid empty call: it returns MLA_OK.
+ *  - softmax_scale is taken as a 32-bit float.
+ */
+#ifndef MLA_ATTN_H_
+#define MLA_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_QK_NOPE_HEAD_DIM 128
+#define MLA_QK_ROPE_HEAD_DIM 64
+#define MLA_V_HEAD_DIM 128
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,      /* a pointer to a non-empty tensor is NULL */
+  MLA_ERR_SHAPE = 2,     /* negative size, S != past_len + T, or size beyond the launch limits */
+  MLA_ERR_ALIGN = 3,     /* a tensor pointer is not 16-byte aligned */
+  MLA_ERR_SCALE = 4,     /* softmax_scale is NaN or infinite */
+  MLA_ERR_WORKSPACE = 5, /* decode workspace missing or smaller than required */
+  MLA_ERR_DEVICE = 6     /* the HIP runtime reported an error at launch */
+} mla_status;
+
+/*
+ * Causal MLA attention for T new queries against S = past_len + T keys
+ * (prefill, chunked prefill on top of a cache of past_len keys, or any T).
+ * Shape contract mirrors the attention-core excerpt ("Similarities" page):
+ * the scores must be (B,H,T,kv_seq_len) and the mask (B,1,T,kv_seq_len) with
+ * kv_seq_len = past_len + T; a mismatch is MLA_ERR_SHAPE (ValueError there).
+ * The causal mask is generated from indices and never read from memory.
+ */
+mla_status mla_attn_prefill(const void* q_nope, const void* q_pe,
+                            const void* k_nope, const void* k_pe,
+                            const void* v, void* out,
+                            int32_t B, int32_t H, int32_t T, int32_t S,
+                            int32_t past_len, float softmax_scale,
+                            void* stream);
+
+/*
+ * Bytes of device workspace mla_attn_decode needs for (B, H, S). A pure
+ * function of its arguments (no device query); 0 means no workspace is
+ * needed. Returns 0 for negative sizes.
+ */
+size_t mla_attn_decode_workspace_bytes(int32_t B, int32_t H, int32_t S);
+
+/*
+ * Decode: one new query per sequence (T = 1) against S = past_len + 1 keys;
+ * the same result as mla_attn_prefill with T = 1 (the pages run one code path
+ * for both, the "Similarities" page showing decode with p = 1000, S = 1001).
+ * Shapes as above with T = 1.
+ *
+ * The key range of each (b, h) may be split across workgroups whose partial
+ * results (fp32) are merged by a log-sum-exp combine inside the same launch.
+ * workspace: caller-owned device memory of at least
+ * mla_attn_decode_workspace_bytes(B, H, S) bytes (may be NULL when that is 0).
+ * It must be zero-filled before its first use; every completed call leaves
+ * its counters zero again, so one zero-filled buffer can be reused by any
+ * sequence of calls. Calls that overlap in time must not share a workspace.
+ */
+mla_status mla_attn_decode(const void* q_nope, const void* q_pe,
+                           const void* k_nope, const void* k_pe,
+                           const void* v, void* out,
+                           void* workspace, size_t workspace_bytes,
+                           int32_t B, int32_t H, int32_t S, int32_t past_len,
+                           float softmax_scale, void* stream);
+
+/* Static name of a status code ("MLA_OK", ...); "unknown status" otherwise. */
+const char* mla_status_string(mla_status s);
+
+/* Thread-local message for the last failing call on this thread ("" if none). */
+const char* mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_ATTN_H_ */

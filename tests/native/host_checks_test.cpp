@@ -1,0 +1,103 @@
+// CPU unit test of the host-side argument checks and decode planning
+// (attention_mla_causal_amd/csrc/mla_host_checks.h). Built with g++ and
+// sanitizers by tests/test_host_checks.py; no HIP headers involved.
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <initializer_list>
+#include <limits>
+
+#include "../../attention_mla_causal_amd/csrc/mla_host_checks.h"
+
+static int failures = 0;
+#define EXPECT(cond)                                                   \
+  do {                                                                 \
+    if (!(cond)) {                                                     \
+      std::printf("FAIL %s:%d: %s\n", __FILE__, __LINE__, #cond);      \
+      ++failures;                                                      \
+    }                                                                  \
+  } while (0)
+
+int main() {
+  alignas(16) static char buf[4096];
+  const void* p = buf;        // aligned
+  const void* bad = buf + 2;  // misaligned
+  const float sc = 0.07216878f;
+  using namespace mla;
+
+  // valid prefill
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 16, 16, 0, sc).status == MLA_OK);
+  EXPECT(!check_prefill(p, p, p, p, p, p, 1, 4, 16, 16, 0, sc).empty);
+  // shapes
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 16, 17, 0, sc).status == MLA_ERR_SHAPE);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 16, 20, 5, sc).status == MLA_ERR_SHAPE);
+  EXPECT(check_prefill(p, p, p, p, p, p, -1, 4, 16, 16, 0, sc).status == MLA_ERR_SHAPE);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 16, 15, -1, sc).status == MLA_ERR_SHAPE);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 1, 2147483647LL + 1, 2147483647LL, sc).status == MLA_OK);
+  EXPECT(check_prefill(p, p, p, p, p, p, 65536, 65536, 2048, 2048, 0, sc).status == MLA_ERR_SHAPE);
+  // empty calls are valid no-ops, even with NULL pointers
+  {
+    CheckResult r = check_prefill(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 4, 16, 16, 0, sc);
+    EXPECT(r.status == MLA_OK && r.empty);
+    r = check_prefill(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 1, 4, 0, 7, 7, sc);
+    EXPECT(r.status == MLA_OK && r.empty);
+  }
+  // NULL and alignment, each argument in turn
+  for (int i = 0; i < 6; ++i) {
+    const void* a[6] = {p, p, p, p, p, p};
+    a[i] = nullptr;
+    EXPECT(check_prefill(a[0], a[1], a[2], a[3], a[4], a[5], 1, 2, 3, 3, 0, sc).status == MLA_ERR_NULL);
+    a[i] = bad;
+    EXPECT(check_prefill(a[0], a[1], a[2], a[3], a[4], a[5], 1, 2, 3, 3, 0, sc).status == MLA_ERR_ALIGN);
+  }
+  // scale
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, NAN).status == MLA_ERR_SCALE);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, INFINITY).status == MLA_ERR_SCALE);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, 0.0f).status == MLA_ERR_SCALE);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, -0.5f).status == MLA_ERR_SCALE);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, 3.0e38f).status == MLA_ERR_SCALE);
+
+  // decode planning
+  {
+    DecodePlan pl = plan_decode(1, 64, 1001);
+    EXPECT(pl.nsplit == 16 && pl.keys_per_split == 64);
+    EXPECT(pl.workspace_bytes == pl.ws_o_bytes + pl.ws_ml_bytes + pl.ws_cnt_bytes);
+    EXPECT(pl.ws_o_bytes == size_t(64) * 16 * 128 * 4);
+    EXPECT(pl.workspace_bytes % 256 == 0);
+    pl = plan_decode(32, 64, 8192);
+    EXPECT(pl.nsplit == 1 && pl.workspace_bytes == 0 && pl.keys_per_split >= 8192);
+    pl = plan_decode(1, 1, 1);
+    EXPECT(pl.nsplit == 1 && pl.workspace_bytes == 0);
+    for (long long S : {1LL, 63LL, 64LL, 65LL, 1001LL, 4096LL, 100001LL, 2000000LL}) {
+      for (long long bh : {1LL, 3LL, 64LL, 511LL, 512LL, 2048LL}) {
+        pl = plan_decode(1, bh, S);
+        EXPECT(pl.nsplit >= 1);
+        EXPECT(pl.keys_per_split % kDecodeKeysPerTrip == 0);
+        EXPECT(pl.keys_per_split * pl.nsplit >= S);               // covers every key
+        EXPECT(pl.keys_per_split * (pl.nsplit - 1) < S);          // no empty split
+      }
+    }
+    EXPECT(plan_decode(-1, 4, 10).workspace_bytes == 0);
+  }
+  // decode checks
+  {
+    DecodePlan pl;
+    const size_t need = plan_decode(1, 64, 1001).workspace_bytes;
+    EXPECT(check_decode(p, p, p, p, p, p, p, need, 1, 64, 1001, 1000, sc, &pl).status == MLA_OK);
+    EXPECT(pl.nsplit == 16);
+    EXPECT(check_decode(p, p, p, p, p, p, p, need - 1, 1, 64, 1001, 1000, sc, &pl).status == MLA_ERR_WORKSPACE);
+    EXPECT(check_decode(p, p, p, p, p, p, nullptr, need, 1, 64, 1001, 1000, sc, &pl).status == MLA_ERR_WORKSPACE);
+    EXPECT(check_decode(p, p, p, p, p, p, bad, need, 1, 64, 1001, 1000, sc, &pl).status == MLA_ERR_ALIGN);
+    EXPECT(check_decode(p, p, p, p, p, p, p, need, 1, 64, 1001, 999, sc, &pl).status == MLA_ERR_SHAPE);
+    EXPECT(check_decode(p, p, p, p, p, p, nullptr, 0, 32, 64, 8192, 8191, sc, &pl).status == MLA_OK);
+    EXPECT(check_decode(p, p, p, p, p, p, nullptr, 0, 1, 64, 0, -1, sc, &pl).status == MLA_ERR_SHAPE);
+    CheckResult r = check_decode(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 64, 5, 4, sc, &pl);
+    EXPECT(r.status == MLA_OK && r.empty);
+  }
+  if (failures) {
+    std::printf("%d failures\n", failures);
+    return 1;
+  }
+  std::printf("host checks OK\n");
+  return 0;
+}

@@ -1,0 +1,101 @@
+"""The C-ABI library loads and exports every symbol include/mla_attn.h declares.
+
+CPU only: every call below is rejected by the host-side checks (or is an empty
+call), so nothing reaches the GPU. Calls that would pass the checks are never
+made here.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_attn.h")
+
+SC = 192.0 ** -0.5
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import attention_mla_causal_amd as m
+    return m._lib
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == sorted([
+        "mla_attn_decode", "mla_attn_decode_workspace_bytes", "mla_attn_prefill",
+        "mla_last_error", "mla_status_string"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    import attention_mla_causal_amd as m
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert name in m.SIGNATURES, name
+
+
+def test_status_strings(lib):
+    import attention_mla_causal_amd as m
+    for code, name in m.STATUS_NAMES.items():
+        assert lib.mla_status_string(code).decode() == name
+    assert lib.mla_status_string(99).decode() == "unknown status"
+
+
+ALIGNED = ctypes.c_void_p(0x10000)    # never dereferenced: every call below fails its checks
+MISALIGNED = ctypes.c_void_p(0x10002)
+
+
+def _prefill(lib, ptrs, B, H, T, S, P, scale=SC):
+    return lib.mla_attn_prefill(*ptrs, B, H, T, S, P, scale, None)
+
+
+@pytest.mark.parametrize("B,H,T,S,P", [(1, 4, 16, 17, 0), (1, 4, 16, 20, 5), (-1, 4, 16, 16, 0),
+                                       (1, 4, 16, 15, -1), (1, -2, 3, 3, 0)])
+def test_prefill_shape_errors(lib, B, H, T, S, P):
+    assert _prefill(lib, [ALIGNED] * 6, B, H, T, S, P) == 2
+    assert "mla_attn_prefill" in lib.mla_last_error().decode()
+
+
+def test_prefill_null_align_scale_errors(lib):
+    for i in range(6):
+        ptrs = [ALIGNED] * 6
+        ptrs[i] = None
+        assert _prefill(lib, ptrs, 1, 2, 3, 3, 0) == 1
+        ptrs[i] = MISALIGNED
+        assert _prefill(lib, ptrs, 1, 2, 3, 3, 0) == 3
+    for bad in (float("nan"), float("inf"), 0.0, -1.0):
+        assert _prefill(lib, [ALIGNED] * 6, 1, 2, 3, 3, 0, bad) == 4
+    assert "softmax_scale" in lib.mla_last_error().decode()
+
+
+def test_empty_calls_are_ok(lib):
+    assert _prefill(lib, [None] * 6, 0, 4, 16, 16, 0) == 0
+    assert _prefill(lib, [None] * 6, 1, 4, 0, 9, 9) == 0
+    assert lib.mla_attn_decode(*([None] * 7), 0, 0, 64, 10, 9, SC, None) == 0
+
+
+def test_decode_errors(lib):
+    need = lib.mla_attn_decode_workspace_bytes(1, 64, 1001)
+    assert need > 0 and need % 256 == 0
+    assert lib.mla_attn_decode_workspace_bytes(32, 64, 8192) == 0
+    assert lib.mla_attn_decode_workspace_bytes(-1, 64, 8192) == 0
+    args = [ALIGNED] * 6
+    assert lib.mla_attn_decode(*args, ALIGNED, need - 1, 1, 64, 1001, 1000, SC, None) == 5
+    assert lib.mla_attn_decode(*args, None, need, 1, 64, 1001, 1000, SC, None) == 5
+    assert lib.mla_attn_decode(*args, MISALIGNED, need, 1, 64, 1001, 1000, SC, None) == 3
+    assert lib.mla_attn_decode(*args, ALIGNED, need, 1, 64, 1001, 999, SC, None) == 2
+    assert lib.mla_attn_decode(*args, ALIGNED, need, 1, 64, 1001, 1000, float("nan"), None) == 4
+
+
+def test_binding_has_no_fallback(tmp_path):
+    import attention_mla_causal_amd as m
+    with pytest.raises(ImportError):
+        m.load_library(str(tmp_path / "missing.so"))

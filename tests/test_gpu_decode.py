@@ -1,0 +1,137 @@
+"""GPU parity of mla_attn_decode against the fp64 oracle (through the C ABI)."""
+
+import numpy as np
+import pytest
+
+from oracle import mla_attention
+from seeded_inputs import WORKLOADS, device_inputs, host_inputs, random_inputs
+
+from _gpu_util import assert_parity, log, to_host_bits, to_host_f64, upload
+
+pytestmark = pytest.mark.gpu
+
+ALPHA = WORKLOADS["decode_p1000"].softmax_scale
+
+
+def _lib():
+    import attention_mla_causal_amd as m
+    return m
+
+
+def _gpu_decode(d, P, scale=ALPHA, out=None, workspace=None):
+    import torch
+    o = _lib().mla_attn_decode(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], P, scale,
+                               out=out, workspace=workspace)
+    torch.cuda.synchronize()
+    return o
+
+
+def _oracle(x, P, scale=ALPHA):
+    return mla_attention(x["q_nope"], x["q_pe"], x["k_nope"], x["k_pe"], x["v"], P, scale)
+
+
+def test_decode_as_on_the_pages():
+    wl = WORKLOADS["decode_p1000"]
+    log(f"case decode_p1000 B={wl.B} H={wl.H} P={wl.past_len}")
+    x = host_inputs(wl, seed=0)
+    out = _gpu_decode(upload(x), wl.past_len, wl.softmax_scale)
+    assert_parity(to_host_f64(out), _oracle(x, wl.past_len, wl.softmax_scale), "decode_p1000")
+
+
+# (B, H, past_len): a single key; key counts below, at and above a 64-key trip;
+# many splits with a ragged last split; B*H large enough for one split.
+EDGE = [(1, 1, 0), (1, 4, 62), (2, 3, 63), (1, 2, 64), (3, 5, 4095), (1, 1, 100000),
+        (2, 64, 777), (8, 64, 1500)]
+
+
+@pytest.mark.parametrize("B,H,P", EDGE)
+def test_decode_edge_shapes(B, H, P):
+    log(f"case decode edge B={B} H={H} P={P} ws={_lib().mla_attn_decode_workspace_bytes(B, H, P + 1)}")
+    x = random_inputs(B, H, 1, P, seed=B * 7 + H * 3 + P)
+    out = _gpu_decode(upload(x), P)
+    assert_parity(to_host_f64(out), _oracle(x, P), f"decode {B},{H},{P}")
+
+
+def test_decode_sharp_softmax():
+    B, H, P = 1, 8, 3000
+    log("case decode sharp")
+    x = random_inputs(B, H, 1, P, seed=77, std=2.0)
+    out = _gpu_decode(upload(x), P)
+    assert_parity(to_host_f64(out), _oracle(x, P), "decode sharp")
+
+
+def test_decode_equals_last_row_of_prefill():
+    B, H, S = 2, 4, 700
+    log("case decode == last prefill row")
+    x = random_inputs(B, H, S, 0, seed=31)
+    d = upload(x)
+    import torch
+    pre = _lib().mla_attn_prefill(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], 0, ALPHA)
+    dq = dict(d)
+    dq["q_nope"] = d["q_nope"][:, :, -1:].contiguous()
+    dq["q_pe"] = d["q_pe"][:, :, -1:].contiguous()
+    dec = _gpu_decode(dq, S - 1)
+    torch.cuda.synchronize()
+    assert_parity(to_host_f64(dec)[:, :, 0], to_host_f64(pre)[:, :, -1], "decode vs prefill last row")
+    assert_parity(to_host_f64(dec)[:, :, 0], _oracle(x, 0)[:, :, -1], "decode vs oracle")
+
+
+def test_workspace_reuse_and_rearm():
+    """One zero-filled workspace serves many calls (the counters re-arm)."""
+    import torch
+    B, H, P = 1, 16, 2999
+    x = random_inputs(B, H, 1, P, seed=8)
+    d = upload(x)
+    need = _lib().mla_attn_decode_workspace_bytes(B, H, P + 1)
+    log(f"case workspace reuse need={need}")
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ref = _oracle(x, P)
+    first = None
+    for it in range(4):
+        out = torch.full((B, H, 1, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+        _gpu_decode(d, P, out=out, workspace=ws)
+        bits = to_host_bits(out)
+        if first is None:
+            first = bits
+            assert_parity(to_host_f64(out), ref, "workspace first call")
+        assert np.array_equal(bits, first), f"call {it} differs"
+    cnt_off = need - 256  # counters live in the last 256-byte-aligned region
+    assert int(ws[cnt_off:].count_nonzero().item()) == 0
+
+
+def test_decode_future_independence_and_determinism():
+    B, H, P = 1, 4, 1234
+    log("case decode determinism")
+    x = random_inputs(B, H, 1, P, seed=10)
+    d = upload(x)
+    a = to_host_bits(_gpu_decode(d, P))
+    b = to_host_bits(_gpu_decode(d, P))
+    assert np.array_equal(a, b)
+
+
+def test_batched_decode_full_size_sampled():
+    """The full batched decode (B=32, H=64, S=8192; 8.6 GB of keys and values),
+    inputs drawn on the device; the oracle checks sampled (b, h) rows."""
+    import torch
+    wl = WORKLOADS["batched_decode"]
+    log(f"case batched_decode B={wl.B} H={wl.H} P={wl.past_len}")
+    d = device_inputs(wl, "cuda", seed=0)
+    out = _gpu_decode(d, wl.past_len, wl.softmax_scale)
+    assert torch.isfinite(out).all().item()
+    rng = np.random.default_rng(0)
+    picks = {(0, 0), (wl.B - 1, wl.H - 1)}
+    while len(picks) < 12:
+        picks.add((int(rng.integers(wl.B)), int(rng.integers(wl.H))))
+    got, ref = [], []
+    for b, h in sorted(picks):
+        xs = {
+            "q_nope": to_host_bits(d["q_nope"][b:b + 1, h:h + 1]),
+            "q_pe": to_host_bits(d["q_pe"][b:b + 1, h:h + 1]),
+            "k_nope": to_host_bits(d["k_nope"][b:b + 1, h:h + 1]),
+            "k_pe": to_host_bits(d["k_pe"][b:b + 1]),
+            "v": to_host_bits(d["v"][b:b + 1, h:h + 1]),
+        }
+        ref.append(_oracle(xs, wl.past_len, wl.softmax_scale)[0, 0, 0])
+        got.append(to_host_f64(out[b, h, 0]))
+    assert_parity(np.stack(got), np.stack(ref), "batched_decode sampled")
