@@ -147,7 +147,7 @@ def mla_attn_prefill(q_nope, q_pe, k_nope, k_pe, v, past_len: int, softmax_scale
 
 
 def mla_attn_decode_workspace_bytes(B: int, H: int, S: int) -> int:
-    """Bytes of zero-initialised workspace mla_attn_decode needs for (B, H, S)."""
+    """Bytes of device scratch mla_attn_decode needs for (B, H, S) (0: none)."""
     return int(_lib.mla_attn_decode_workspace_bytes(int(B), int(H), int(S)))
 
 
@@ -155,9 +155,9 @@ def mla_attn_decode(q_nope, q_pe, k_nope, k_pe, v, past_len: int, softmax_scale:
                     out=None, workspace=None):
     """One new query per sequence (T = 1) against S = past_len + 1 keys.
 
-    workspace: a zero-filled uint8 GPU tensor of at least
-    mla_attn_decode_workspace_bytes(B, H, S) bytes, reusable across calls
-    (the library leaves it zero-filled); allocated here when omitted.
+    workspace: a GPU tensor of at least mla_attn_decode_workspace_bytes(B, H, S)
+    bytes of scratch (contents irrelevant, reusable by non-overlapping calls);
+    allocated here when omitted.
     """
     import torch
 
@@ -172,7 +172,7 @@ def mla_attn_decode(q_nope, q_pe, k_nope, k_pe, v, past_len: int, softmax_scale:
             raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, 1, V_HEAD_DIM)}")
     need = mla_attn_decode_workspace_bytes(B, H, S)
     if workspace is None:
-        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q_nope.device)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_nope.device)
     if not (workspace.is_cuda and workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous GPU tensor")
     ws_bytes = workspace.numel() * workspace.element_size()

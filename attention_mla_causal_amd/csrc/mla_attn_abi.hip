@@ -87,9 +87,6 @@ mla_status mla_attn_decode(const void* q_nope, const void* q_pe, const void* k_n
   char* ws = static_cast<char*>(workspace);
   a.ws_o = plan.nsplit > 1 ? reinterpret_cast<float*>(ws) : nullptr;
   a.ws_ml = plan.nsplit > 1 ? reinterpret_cast<float*>(ws + plan.ws_o_bytes) : nullptr;
-  a.ws_cnt = plan.nsplit > 1
-                 ? reinterpret_cast<uint32_t*>(ws + plan.ws_o_bytes + plan.ws_ml_bytes)
-                 : nullptr;
   a.B = B;
   a.H = H;
   a.S = S;

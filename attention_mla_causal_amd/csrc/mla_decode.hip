@@ -15,11 +15,14 @@
 //    products, and a 4-step DPP reduction inside the quarter-wave gives the
 //    score. Each quarter-wave runs its own online softmax (fp32, exp2 domain)
 //    over the keys it sees and accumulates 8 output dims per lane.
-//  * Quarter-waves, then waves, are merged by log-sum-exp; when the key range
-//    of a (b, h) is split over several workgroups, each writes an fp32
-//    partial (o[128], max, sum) to the workspace and the last workgroup to
-//    arrive (device-scope counter) merges them and writes the bf16 output,
-//    then re-arms the counter to zero. One launch, no second pass.
+//  * Quarter-waves, then waves, are merged by log-sum-exp. When the key range
+//    of a (b, h) is split over several workgroups (to fill the chip when B*H
+//    is small), each writes an fp32 partial (o[128], max, sum) to the
+//    workspace and a second, tiny kernel merges the partials of each (b, h)
+//    and writes bf16. The kernel boundary orders the two; no device-scope
+//    fences or counters are needed (on this chip a device-scope release or
+//    acquire writes back or invalidates the whole L2, which costs far more
+//    than a second launch).
 //  * Workgroups of one sequence are placed on one XCD so the shared k_pe rows
 //    are served from that XCD's L2 for all heads.
 #include <hip/hip_runtime.h>
@@ -32,13 +35,15 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int DN = 128, DR = 64, DV = 128;
 constexpr int NW = 4;            // waves per workgroup
 constexpr int NT = NW * 64;
-constexpr int KEYS_PER_LANE = 4; // keys each quarter-wave takes per trip
-constexpr int KEYS_PER_WAVE = 4 * KEYS_PER_LANE;   // 16
-constexpr int KEYS_PER_TRIP = NW * KEYS_PER_WAVE;  // 64
+constexpr int KEYS_PER_LANE = 8; // keys each quarter-wave takes per trip (loads in flight)
+constexpr int KEYS_PER_WAVE = 4 * KEYS_PER_LANE;   // 32
+constexpr int KEYS_PER_TRIP = NW * KEYS_PER_WAVE;  // 128
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -87,7 +92,6 @@ __device__ __forceinline__ void merge_xor(float& m, float& l, float (&o)[8], int
 __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
   __shared__ float red_o[NW][DV];
   __shared__ float red_ml[NW][2];
-  __shared__ int last_flag;
 
   const int nwg = gridDim.x;
   const int wg = blockIdx.x;
@@ -230,42 +234,38 @@ __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
     return;
   }
 
-  // ---- split-KV: publish this workgroup's partial, the last arrival merges
-  const int64_t slot = (int64_t)bh * a.nsplit + split;
+  // ---- split-KV: publish this workgroup's partial for the combine kernel
   if (wave == 0 && qq == 0) {
+    const int64_t slot = (int64_t)bh * a.nsplit + split;
     float* dst = a.ws_o + slot * DV + 8 * cl;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dst[e] = O[e];
-    if (cl == 0) {
-      a.ws_ml[2 * slot] = M;
-      a.ws_ml[2 * slot + 1] = L;
-    }
+    *reinterpret_cast<f32x4*>(dst) = f32x4{O[0], O[1], O[2], O[3]};
+    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{O[4], O[5], O[6], O[7]};
+    if (cl == 0) *reinterpret_cast<f32x2*>(a.ws_ml + 2 * slot) = f32x2{M, L};
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = atomicAdd(a.ws_cnt + bh, 1u);
-    last_flag = (prev == (uint32_t)(a.nsplit - 1));
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
+}
 
-  // wave 0: quarter-wave qq merges splits qq, qq+4, ...; then the quarters merge
-  if (wave != 0) return;
+// Log-sum-exp merge of the nsplit partials of each (b, h): one wave per (b, h);
+// quarter-wave qq merges splits qq, qq+4, ..., then the quarters merge.
+__global__ __launch_bounds__(64) void mla_decode_combine_kernel(DecodeArgs a) {
+  const int bh = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int cl = lane & 15, qq = lane >> 4;
   float mm = -INFINITY, ll = 0.0f, oo[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) oo[e] = 0.0f;
   for (int sp = qq; sp < a.nsplit; sp += 4) {
     const int64_t sl = (int64_t)bh * a.nsplit + sp;
-    const float ms = __builtin_nontemporal_load(a.ws_ml + 2 * sl);
-    const float ls = __builtin_nontemporal_load(a.ws_ml + 2 * sl + 1);
-    const float Mn = fmaxf(mm, ms);
-    const float a1 = rescale(mm, Mn), a2 = rescale(ms, Mn);
-    const float* src = a.ws_o + sl * DV + 8 * cl;
-    ll = ll * a1 + ls * a2;
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.ws_ml + 2 * sl);
+    const float Mn = fmaxf(mm, ml[0]);
+    const float a1 = rescale(mm, Mn), a2 = rescale(ml[0], Mn);
+    const f32x4 p0 = *reinterpret_cast<const f32x4*>(a.ws_o + sl * DV + 8 * cl);
+    const f32x4 p1 = *reinterpret_cast<const f32x4*>(a.ws_o + sl * DV + 8 * cl + 4);
+    ll = ll * a1 + ml[1] * a2;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) oo[e] = oo[e] * a1 + __builtin_nontemporal_load(src + e) * a2;
+    for (int e = 0; e < 4; ++e) {
+      oo[e] = oo[e] * a1 + p0[e] * a2;
+      oo[4 + e] = oo[4 + e] * a1 + p1[e] * a2;
+    }
     mm = Mn;
   }
   merge_xor(mm, ll, oo, 16);
@@ -278,7 +278,6 @@ __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
     for (int e = 0; e < 4; ++e)
       w[e] = (uint32_t)to_bf16_rne(oo[2 * e] * inv) | ((uint32_t)to_bf16_rne(oo[2 * e + 1] * inv) << 16);
     *reinterpret_cast<u32x4*>(dst) = w;
-    if (cl == 0) a.ws_cnt[bh] = 0u;  // re-arm for the next call
   }
 }
 
@@ -287,6 +286,8 @@ __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const int grid = a.B * a.H * a.nsplit;
   hipLaunchKernelGGL(mla_decode_kernel, dim3(grid), dim3(NT), 0, stream, a);
+  if (a.nsplit > 1)
+    hipLaunchKernelGGL(mla_decode_combine_kernel, dim3(a.B * a.H), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -21,10 +21,10 @@ namespace mla {
 
 // Prefill tiling: queries per workgroup. The kernel assumes this value.
 constexpr int64_t kPrefillBlockM = 128;
-// Decode: keys one workgroup consumes per loop trip (4 waves x 4 quarter-waves x 4 keys).
-constexpr int64_t kDecodeKeysPerTrip = 64;
-// Decode split heuristic: aim for this many workgroups (4 per CU on 256 CUs).
-constexpr int64_t kDecodeTargetWorkgroups = 1024;
+// Decode: keys one workgroup consumes per loop trip (4 waves x 4 quarter-waves x 8 keys).
+constexpr int64_t kDecodeKeysPerTrip = 128;
+// Decode split heuristic: aim for this many workgroups (2 per CU on 256 CUs).
+constexpr int64_t kDecodeTargetWorkgroups = 512;
 constexpr int64_t kMaxGrid = 2147483647;  // grid.x limit
 
 struct DecodePlan {
@@ -32,7 +32,6 @@ struct DecodePlan {
   int64_t keys_per_split = 0;  // multiple of kDecodeKeysPerTrip
   size_t ws_o_bytes = 0;       // fp32 [B*H, nsplit, 128]
   size_t ws_ml_bytes = 0;      // fp32 pairs (max, sum) [B*H, nsplit]
-  size_t ws_cnt_bytes = 0;     // uint32 arrival counters [B*H]
   size_t workspace_bytes = 0;  // total, each region 256-byte aligned
 };
 
@@ -59,8 +58,7 @@ inline DecodePlan plan_decode(int64_t B, int64_t H, int64_t S) {
   if (nsplit > 1) {
     p.ws_o_bytes = align256(size_t(bh) * size_t(nsplit) * 128 * sizeof(float));
     p.ws_ml_bytes = align256(size_t(bh) * size_t(nsplit) * 2 * sizeof(float));
-    p.ws_cnt_bytes = align256(size_t(bh) * sizeof(uint32_t));
-    p.workspace_bytes = p.ws_o_bytes + p.ws_ml_bytes + p.ws_cnt_bytes;
+    p.workspace_bytes = p.ws_o_bytes + p.ws_ml_bytes;
   }
   return p;
 }

@@ -28,7 +28,6 @@ struct DecodeArgs {
   uint16_t* out;           // [B,H,1,128]
   float* ws_o;             // [B*H, nsplit, 128] partial outputs (nsplit > 1)
   float* ws_ml;            // [B*H, nsplit, 2] partial (max, sum)
-  uint32_t* ws_cnt;        // [B*H] arrival counters, zero between calls
   int32_t B, H, S;
   int32_t nsplit, keys_per_split;
   float scale_log2;

@@ -49,20 +49,26 @@ constexpr int BN = 64;    // keys per tile
 constexpr int NW = 4;     // waves per workgroup
 constexpr int NT = NW * 64;
 
-// LDS rows, in bf16 elements, padded so that 16-byte reads of 16 consecutive
-// rows at one column fall in distinct banks.
-constexpr int KN_LD = DN + 8;   // 272 B
-constexpr int KP_LD = DR + 8;   // 144 B
-constexpr int V_LD = DV + 16;   // 288 B
-constexpr int KN_ELEMS = BN * KN_LD;
-constexpr int KP_ELEMS = BN * KP_LD;
-constexpr int V_ELEMS = BN * V_LD;
-constexpr int LDS_ELEMS = KN_ELEMS + KP_ELEMS + V_ELEMS;
+// One LDS stage holds a 64-key tile: k_nope, k_pe, v. Rows are unpadded and
+// their 16-byte chunks are XOR-swizzled by row, so that the direct
+// global->LDS loads (which fill 1 KiB contiguously per instruction) and the
+// MFMA operand reads (16 rows at one logical column) are both conflict-free.
+constexpr int KN_OFF = 0;
+constexpr int KP_OFF = BN * DN * 2;             // 16384
+constexpr int V_OFF = KP_OFF + BN * DR * 2;     // 24576
+constexpr int STAGE_BYTES = V_OFF + BN * DV * 2;  // 40960
 
-// 16-byte chunks per tile each thread moves: k_nope 64x128, k_pe 64x64, v 64x128
-constexpr int KN_CHUNKS = BN * DN / 8 / NT;  // 4
-constexpr int KP_CHUNKS = BN * DR / 8 / NT;  // 2
-constexpr int V_CHUNKS = BN * DV / 8 / NT;   // 4
+// physical 16-byte chunk of logical chunk c in row r
+__device__ __forceinline__ int kn_chunk(int r, int c) { return r * 16 + (c ^ (r & 15)); }
+__device__ __forceinline__ int kp_chunk(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+__device__ __forceinline__ int v_chunk(int r, int c) { return r * 16 + (c ^ ((r & 3) << 2)); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void glb_void;
+
+__device__ __forceinline__ void load_lds16(const uint16_t* src, char* lds_dst) {
+  __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)lds_dst, 16, 0, 0);
+}
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -72,16 +78,155 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
-__device__ __forceinline__ bf16x4 lds_tr_read(const uint16_t* p) {
+__device__ __forceinline__ bf16x4 lds_tr_read(const char* p) {
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
+// Wait until this wave's global->LDS copies have landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+struct Ctx {
+  const uint16_t* kn_g;
+  const uint16_t* kp_g;
+  const uint16_t* v_g;
+  int64_t S, P;
+  int tid, lane, wave, hi, l32;
+};
+
+// Issue the 10 direct global->LDS copies (per wave) of key tile j into `stage`.
+// Rows past the last key are clamped to it: they are masked out of the
+// softmax, and clamping keeps every LDS value finite.
+__device__ __forceinline__ void issue_tile(const Ctx& c, int j, char* stage) {
+  const int64_t kb = (int64_t)j * BN;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int t = u * NW + c.wave;
+    const int pc = t * 64 + c.lane;
+    const int r = pc >> 4, p = pc & 15;
+    const int64_t key = (kb + r < c.S) ? kb + r : c.S - 1;
+    load_lds16(c.kn_g + key * DN + ((p ^ (r & 15)) << 3), stage + KN_OFF + t * 1024);
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int t = u * NW + c.wave;
+    const int pc = t * 64 + c.lane;
+    const int r = pc >> 3, p = pc & 7;
+    const int64_t key = (kb + r < c.S) ? kb + r : c.S - 1;
+    load_lds16(c.kp_g + key * DR + ((p ^ ((r >> 1) & 7)) << 3), stage + KP_OFF + t * 1024);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int t = u * NW + c.wave;
+    const int pc = t * 64 + c.lane;
+    const int r = pc >> 4, p = pc & 15;
+    const int64_t key = (kb + r < c.S) ? kb + r : c.S - 1;
+    load_lds16(c.v_g + key * DV + ((p ^ ((r & 3) << 2)) << 3), stage + V_OFF + t * 1024);
+  }
+}
+
+struct State {
+  f32x16 o[4];   // O^T accumulators: lane owns query l32, 64 of its 128 dims
+  float m_run;   // running max, scaled log2 domain
+  float l_run;   // this lane's share of the running sum
+};
+
+// One 64-key tile for one wave's 32 queries.
+__device__ __forceinline__ void compute_tile(const Ctx& c, const bf16x8 (&qf)[12], State& st,
+                                             const char* stage, int64_t kb, int64_t q0w,
+                                             int64_t wave_kfull, float cl2) {
+  // ---- S^T = K Q^T: two 32-key halves interleaved for independent MFMA chains
+  f32x16 s0, s1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s0[r] = 0.0f;
+    s1[r] = 0.0f;
+  }
+  const int r0 = c.l32, r1 = 32 + c.l32;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const int lc = 2 * kk + c.hi;
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(stage + KN_OFF + kn_chunk(r0, lc) * 16);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(stage + KN_OFF + kn_chunk(r1, lc) * 16);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], s1, 0, 0, 0);
+  }
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int lc = 2 * kk + c.hi;
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(stage + KP_OFF + kp_chunk(r0, lc) * 16);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(stage + KP_OFF + kp_chunk(r1, lc) * 16);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[8 + kk], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[8 + kk], s1, 0, 0, 0);
+  }
+
+  // ---- causal mask, only on tiles that cross this wave's diagonal
+  if (kb + BN > wave_kfull) {
+    const int64_t lim = c.P + q0w + c.l32;  // last key this lane's query sees
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t key = kb + 8 * (r >> 2) + 4 * c.hi + (r & 3);
+      if (key > lim || key >= c.S) s0[r] = -INFINITY;
+      if (key + 32 > lim || key + 32 >= c.S) s1[r] = -INFINITY;
+    }
+  }
+
+  // ---- online softmax (scale > 0: the max of scaled scores is scale * max)
+  float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+  mx = fmaxf(mx, xor32(mx));
+  const float m_new = fmaxf(st.m_run, mx * cl2);
+  const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_ref);
+  st.m_run = m_new;
+  float psum = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], cl2, -m_ref));
+    s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], cl2, -m_ref));
+    psum += s0[r] + s1[r];
+  }
+  st.l_run = st.l_run * alpha + psum;
+  // rescale O only when some query of the wave raised its max
+  if (__builtin_amdgcn_read_exec() && __any(alpha != 1.0f)) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[n][r] *= alpha;
+  }
+
+  // ---- O^T += V^T P^T over 4 K-steps of 16 keys
+  const int sl = c.lane & 15;
+  const int grp = (c.lane >> 4) & 1;
+  // byte offset of this lane's 8-byte piece of V, K-step 0, dims 32n + ...
+  const int vrow = 4 * c.hi + (sl >> 2);
+  const int vcol = 2 * grp + ((sl & 3) >> 1);  // logical chunk within a 32-dim group
+  const int vhalf = 8 * (sl & 1);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const f32x16& sp = (ks >> 1) ? s1 : s0;
+    const int h8 = 8 * (ks & 1);
+    bf16x8 pb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sp[h8 + e];
+    const int kr = 32 * (ks >> 1) + 16 * (ks & 1) + vrow;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const char* vp = stage + V_OFF + v_chunk(kr, 4 * n + vcol) * 16 + vhalf;
+      const bf16x4 lo4 = lds_tr_read(vp);
+      const bf16x4 hi4 = lds_tr_read(vp + 8 * 16 * 16);  // row kr + 8: same swizzle
+      const bf16x8 va = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      st.o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, st.o[n], 0, 0, 0);
+    }
+  }
+}
+
 __global__ __launch_bounds__(NT, 2) void mla_prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
-  uint16_t* lds_kn = lds;
-  uint16_t* lds_kp = lds + KN_ELEMS;
-  uint16_t* lds_v = lds + KN_ELEMS + KP_ELEMS;
+  // two stages, separate objects so the compiler can tell the in-flight copy
+  // into one from reads of the other
+  __shared__ __attribute__((aligned(1024))) char stage0[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char stage1[STAGE_BYTES];
 
   // ---- which (batch, head, query tile) this workgroup owns
   const int nwg = gridDim.x;
@@ -92,25 +237,34 @@ __global__ __launch_bounds__(NT, 2) void mla_prefill_kernel(PrefillArgs a) {
   const int b = bh / a.H;
   const int q0 = qt * BM;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int hi = lane >> 5;     // which half of the wave
-  const int l32 = lane & 31;
-  const int q0w = q0 + wave * 32;
+  Ctx c;
+  c.tid = threadIdx.x;
+  c.lane = c.tid & 63;
+  c.wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
+  c.hi = c.lane >> 5;
+  c.l32 = c.lane & 31;
+  c.S = a.S;
+  c.P = a.past_len;
+  const int64_t T = a.T;
+  c.kn_g = a.k_nope + (int64_t)bh * c.S * DN;
+  c.kp_g = a.k_pe + (int64_t)b * c.S * DR;
+  c.v_g = a.v + (int64_t)bh * c.S * DV;
+  const int64_t q0w = q0 + c.wave * 32;
 
-  const int64_t T = a.T, S = a.S, P = a.past_len;
+  // ---- key range of the workgroup: [0, P + last query + 1)
+  const int64_t q_last = (q0 + BM < T ? q0 + BM : T) - 1;
+  const int64_t kend = c.P + q_last + 1;
+  const int nblocks = (int)((kend + BN - 1) / BN);
+
+  issue_tile(c, 0, stage0);
+
+  // ---- query fragment (B operand of S^T = K Q^T): 8 dims of the lane's query per K-step
   const uint16_t* qn_g = a.q_nope + (int64_t)bh * T * DN;
   const uint16_t* qp_g = a.q_pe + (int64_t)bh * T * DR;
-  const uint16_t* kn_g = a.k_nope + (int64_t)bh * S * DN;
-  const uint16_t* kp_g = a.k_pe + (int64_t)b * S * DR;
-  const uint16_t* v_g = a.v + (int64_t)bh * S * DV;
-
-  // ---- query fragment (B operand of S^T = K Q^T): lane holds 8 dims of its query per K-step
   bf16x8 qf[12];
   {
-    const int64_t myq = q0w + l32;
-    const int koff = 8 * hi;
+    const int64_t myq = q0w + c.l32;
+    const int koff = 8 * c.hi;
     const bool ok = myq < T;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
@@ -120,183 +274,62 @@ __global__ __launch_bounds__(NT, 2) void mla_prefill_kernel(PrefillArgs a) {
       qf[8 + kk] = as_bf16x8(ok ? ldg16(qp_g + myq * DR + 16 * kk + koff) : u32x4{0, 0, 0, 0});
   }
 
-  // ---- key range: the workgroup needs keys [0, P + last query + 1)
-  const int64_t q_last = (q0 + BM < T ? q0 + BM : T) - 1;
-  const int64_t kend = P + q_last + 1;
-  const int nblocks = (int)((kend + BN - 1) / BN);
   const bool wave_live = q0w < T;
   const int64_t wave_q_last = (q0w + 31 < T ? q0w + 31 : T - 1);
-  const int64_t wave_kend = P + wave_q_last + 1;  // keys beyond are hidden from the whole wave
-  const int64_t wave_kfull = P + q0w + 1;         // keys below are visible to the whole wave
+  const int64_t wave_kend = c.P + wave_q_last + 1;  // keys from here on are hidden from the wave
+  const int64_t wave_kfull = c.P + q0w + 1;         // keys below are visible to the whole wave
+  const float cl2 = a.scale_log2;
 
-  const float c = a.scale_log2;
-  f32x16 o[4];
+  State st;
 #pragma unroll
   for (int n = 0; n < 4; ++n)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[n][r] = 0.0f;
-  float m_run = -INFINITY;  // running max in the scaled log2 domain
-  float l_run = 0.0f;       // this lane's share of the running sum
+    for (int r = 0; r < 16; ++r) st.o[n][r] = 0.0f;
+  st.m_run = -INFINITY;
+  st.l_run = 0.0f;
 
-  // ---- register prefetch of one K/V tile
-  u32x4 rkn[KN_CHUNKS], rkp[KP_CHUNKS], rv[V_CHUNKS];
-  auto load_tile = [&](int j) {
-    const int64_t kb = (int64_t)j * BN;
-#pragma unroll
-    for (int u = 0; u < KN_CHUNKS; ++u) {
-      const int ch = tid + u * NT;
-      const int row = ch >> 4, col = (ch & 15) * 8;
-      const int64_t key = kb + row;
-      rkn[u] = key < S ? ldg16(kn_g + key * DN + col) : u32x4{0, 0, 0, 0};
+  // ---- main loop, two tiles per trip so each stage is a fixed LDS object
+  for (int j = 0; j < nblocks; j += 2) {
+    wait_vmem();
+    __syncthreads();  // tile j is in stage0 for everyone; stage1 is free
+    if (j + 1 < nblocks) issue_tile(c, j + 1, stage1);
+    {
+      const int64_t kb = (int64_t)j * BN;
+      if (wave_live && kb < wave_kend) compute_tile(c, qf, st, stage0, kb, q0w, wave_kfull, cl2);
     }
-#pragma unroll
-    for (int u = 0; u < KP_CHUNKS; ++u) {
-      const int ch = tid + u * NT;
-      const int row = ch >> 3, col = (ch & 7) * 8;
-      const int64_t key = kb + row;
-      rkp[u] = key < S ? ldg16(kp_g + key * DR + col) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < V_CHUNKS; ++u) {
-      const int ch = tid + u * NT;
-      const int row = ch >> 4, col = (ch & 15) * 8;
-      const int64_t key = kb + row;
-      rv[u] = key < S ? ldg16(v_g + key * DV + col) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int u = 0; u < KN_CHUNKS; ++u) {
-      const int ch = tid + u * NT;
-      *reinterpret_cast<u32x4*>(lds_kn + (ch >> 4) * KN_LD + (ch & 15) * 8) = rkn[u];
-    }
-#pragma unroll
-    for (int u = 0; u < KP_CHUNKS; ++u) {
-      const int ch = tid + u * NT;
-      *reinterpret_cast<u32x4*>(lds_kp + (ch >> 3) * KP_LD + (ch & 7) * 8) = rkp[u];
-    }
-#pragma unroll
-    for (int u = 0; u < V_CHUNKS; ++u) {
-      const int ch = tid + u * NT;
-      *reinterpret_cast<u32x4*>(lds_v + (ch >> 4) * V_LD + (ch & 15) * 8) = rv[u];
-    }
-  };
-
-  load_tile(0);
-  for (int j = 0; j < nblocks; ++j) {
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();
-    if (j + 1 < nblocks) load_tile(j + 1);  // lands while this tile is computed
-
-    const int64_t kb = (int64_t)j * BN;
-    if (!wave_live || kb >= wave_kend) continue;  // wave-uniform
-
-    // ---- S^T tile: 64 keys x 32 queries, two 32x32 accumulators
-    f32x16 s[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[mt][r] = 0.0f;
-      const int krow = 32 * mt + l32;
-      const uint16_t* kn_row = lds_kn + krow * KN_LD + 8 * hi;
-      const uint16_t* kp_row = lds_kp + krow * KP_LD + 8 * hi;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kn_row + 16 * kk);
-        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[mt], 0, 0, 0);
-      }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kp_row + 16 * kk);
-        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[8 + kk], s[mt], 0, 0, 0);
-      }
-    }
-
-    // ---- causal mask, only on tiles that cross this wave's diagonal
-    if (kb + BN > wave_kfull) {
-      const int64_t lim = P + q0w + l32;  // last visible key of this lane's query
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t key = kb + 32 * mt + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key > lim || key >= S) s[mt][r] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax (scale > 0, so max of scaled = scale * max)
-    float mx = s[0][0];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m_run, mx * c);
-    const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-    m_run = m_new;
-    float psum = 0.0f;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][r], c, -m_ref));
-        s[mt][r] = p;
-        psum += p;
-      }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int n = 0; n < 4; ++n)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[n][r] *= alpha;
-
-    // ---- O^T += V^T P^T over 4 K-steps of 16 keys
-    const int sl = lane & 15;
-    const int grp = (lane >> 4) & 1;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int mt = ks >> 1, half = ks & 1;
-      bf16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[mt][8 * half + e];
-      const int kr = 32 * mt + 16 * half + 4 * hi + (sl >> 2);
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const uint16_t* vp = lds_v + kr * V_LD + 32 * n + 16 * grp + 4 * (sl & 3);
-        const bf16x4 lo4 = lds_tr_read(vp);
-        const bf16x4 hi4 = lds_tr_read(vp + 8 * V_LD);
-        const bf16x8 va = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[n], 0, 0, 0);
-      }
+    if (j + 1 >= nblocks) break;
+    wait_vmem();
+    __syncthreads();  // tile j+1 is in stage1; stage0 is free
+    if (j + 2 < nblocks) issue_tile(c, j + 2, stage0);
+    {
+      const int64_t kb = (int64_t)(j + 1) * BN;
+      if (wave_live && kb < wave_kend) compute_tile(c, qf, st, stage1, kb, q0w, wave_kfull, cl2);
     }
   }
 
   // ---- epilogue: divide by the full row sum and store bf16
   if (!wave_live) return;
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = st.l_run + xor32(st.l_run);
   const float inv = 1.0f / l_tot;
-  const int64_t myq = q0w + l32;
+  const int64_t myq = q0w + c.l32;
   if (myq >= T) return;
   uint16_t* out_row = a.out + ((int64_t)bh * T + myq) * DV;
 #pragma unroll
   for (int n = 0; n < 4; ++n)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int dv0 = 32 * n + 8 * g + 4 * hi;
+      const int dv0 = 32 * n + 8 * g + 4 * c.hi;
       bf16x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[n][4 * g + e] * inv);
+      for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[n][4 * g + e] * inv);
       *reinterpret_cast<bf16x4*>(out_row + dv0) = w;
     }
 }
 
 }  // namespace
 
-int prefill_grid(const PrefillArgs& a) { return a.B * a.H * a.ntiles; }
-
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-  const int grid = prefill_grid(a);
+  const int grid = a.B * a.H * a.ntiles;
   hipLaunchKernelGGL(mla_prefill_kernel, dim3(grid), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }

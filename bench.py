@@ -1,0 +1,331 @@
+"""Benchmark of the MLA attention core on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extra]
+
+One step is one pass of the attention core over one batch of synthetic input:
+one mla_attn_decode call for the decode workloads, one mla_attn_prefill call
+for the prefill workloads. The headline workload is decode exactly as the
+"Similarities" page shows it (B=1, 64 heads, 1 query, past_len=1000, S=1001
+keys); its K timed steps rotate over enough input copies that the 256 MB
+Infinity Cache cannot hold them, and are replayed from a HIP graph so the GPU
+never waits on the Python launcher. The other full-size workloads (batched
+decode, causal prefill, chunked prefill) are measured in the same run and
+reported under "workloads".
+
+Prints one JSON line. `value` is algorithmic work / time: decode counts the
+bytes the method must read and write (k_nope and v per head, the shared k_pe
+once per sequence, q and out), prefill counts 2*(192+128) flops per visible
+(query, key) pair. `roofline` puts the dominant kernel against MI355X's
+published peak; `cpu_baseline` times the fp64 oracle on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from seeded_inputs import WORKLOADS, device_inputs, host_inputs  # noqa: E402
+
+METRIC = "prefill attn TFLOP/s & decode HBM GB/s, 1 MI355X, as fraction of peak"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, published
+CACHE_BYTES = 256 << 20      # Infinity Cache
+
+KERNEL_SOURCES = {
+    "mla_decode_kernel": "attention_mla_causal_amd/csrc/mla_decode.hip",
+    "mla_prefill_kernel": "attention_mla_causal_amd/csrc/mla_prefill.hip",
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def decode_bytes(wl) -> int:
+    B, H, S = wl.B, wl.H, wl.S
+    return B * (H * S * (128 + 128) * 2 + S * 64 * 2 + H * 192 * 2 + H * 128 * 2)
+
+
+def prefill_flops(wl) -> int:
+    T, P = wl.T, wl.past_len
+    n_vis = T * P + T * (T + 1) // 2
+    return 2 * wl.B * wl.H * (192 + 128) * n_vis
+
+
+def source_hash(kernel: str) -> str:
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get(kernel, {}).get(workload)
+    if not ent or ent.get("source_sha256_16") != source_hash(kernel):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return int(max(n)) if n else 1
+    except Exception:
+        return 1
+
+
+def to_dev(bits, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def time_graph(fn, steps, warmup):
+    """Warm up, capture `steps` calls in one HIP graph, time one replay."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0)  # one eager call on the capture stream before capturing
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i)
+    g.replay()  # untimed replay: graph upload
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
+
+
+def time_eager(fn, steps, warmup):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
+
+
+def run_decode(wl, steps, warmup, seed=0, graph=True, copies=None):
+    import torch
+    import attention_mla_causal_amd as mla
+    dev = torch.device("cuda:0")
+    nbytes = decode_bytes(wl)
+    if copies is None:
+        # enough distinct inputs that the rotation cannot live in the Infinity Cache
+        copies = 1 if nbytes >= 2 * CACHE_BYTES else min(64, -(-2 * CACHE_BYTES // nbytes) + 1)
+    log(f"[bench] {wl.name}: B={wl.B} H={wl.H} S={wl.S} copies={copies} steps={steps}")
+    if wl.B * wl.H * wl.S * 256 * 2 > (1 << 31):
+        sets = [device_inputs(wl, dev, seed=seed + c) for c in range(copies)]
+        recipe = "device"
+    else:
+        sets = [{k: to_dev(v, dev) for k, v in host_inputs(wl, seed=seed + c).items()} for c in range(copies)]
+        recipe = "host"
+    out = torch.empty((wl.B, wl.H, 1, 128), dtype=torch.bfloat16, device=dev)
+    need = mla.mla_attn_decode_workspace_bytes(wl.B, wl.H, wl.S)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        d = sets[i % copies]
+        mla.mla_attn_decode(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], wl.past_len,
+                            wl.softmax_scale, out=out, workspace=ws)
+
+    if graph:
+        ms, wall_ms = time_graph(step, steps, warmup)
+    else:
+        ms, wall_ms = time_eager(step, steps, warmup)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    kernel = "mla_decode_kernel"
+    res = {
+        "workload": wl.name, "B": wl.B, "H": wl.H, "T": 1, "past_len": wl.past_len, "S": wl.S,
+        "std": wl.std, "inputs": recipe, "input_copies": copies, "steps": steps,
+        "timing": "hip_graph" if graph else "eager",
+        "ms_per_step": ms, "wall_ms_per_step": wall_ms, "value": gbs, "unit": "GB/s",
+        "algorithmic_bytes": nbytes,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(kernel, wl.name)},
+    }
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_prefill(wl, steps, warmup, seed=0):
+    import torch
+    import attention_mla_causal_amd as mla
+    dev = torch.device("cuda:0")
+    log(f"[bench] {wl.name}: B={wl.B} H={wl.H} T={wl.T} P={wl.past_len} steps={steps}")
+    x = host_inputs(wl, seed=seed)
+    d = {k: to_dev(v, dev) for k, v in x.items()}
+    out = torch.empty((wl.B, wl.H, wl.T, 128), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        mla.mla_attn_prefill(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], wl.past_len,
+                             wl.softmax_scale, out=out)
+
+    ms, wall_ms = time_eager(step, steps, warmup)
+    flops = prefill_flops(wl)
+    tfs = flops / (ms * 1e-3) / 1e12
+    kernel = "mla_prefill_kernel"
+    res = {
+        "workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "past_len": wl.past_len, "S": wl.S,
+        "std": wl.std, "inputs": "host", "steps": steps, "timing": "eager",
+        "ms_per_step": ms, "wall_ms_per_step": wall_ms, "value": tfs, "unit": "TFLOP/s",
+        "algorithmic_flops": flops,
+        "roofline": {"bound": "mfma", "kernel": kernel, "achieved": tfs, "peak": MFMA_BF16_PEAK_TFS,
+                     "unit": "TFLOP/s", "frac": tfs / MFMA_BF16_PEAK_TFS,
+                     "traffic": measured_traffic(kernel, wl.name)},
+    }
+    del d
+    torch.cuda.empty_cache()
+    return res, x
+
+
+def cpu_baseline_decode(wl, seconds):
+    """The fp64 oracle on the whole decode workload, repeated for ~`seconds`."""
+    from oracle import mla_attention
+    x = host_inputs(wl, seed=0)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        mla_attention(x["q_nope"], x["q_pe"], x["k_nope"], x["k_pe"], x["v"], wl.past_len, wl.softmax_scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    per = el / reps
+    return {"value": decode_bytes(wl) / per / 1e9, "unit": "GB/s", "cores": blas_threads(),
+            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"whole workload (B={wl.B} H={wl.H} S={wl.S}), {reps} repetitions, {el:.1f} s",
+            "s_per_step": per}
+
+
+def cpu_baseline_prefill(wl, x, seconds):
+    """The fp64 oracle on the first heads of the workload until ~`seconds` pass;
+    effective rate = algorithmic flops of the heads done / time."""
+    from oracle import mla_attention
+    heads, t0 = 0, time.perf_counter()
+    while heads < wl.H:
+        h = heads
+        mla_attention(x["q_nope"][:, h:h + 1], x["q_pe"][:, h:h + 1], x["k_nope"][:, h:h + 1], x["k_pe"],
+                      x["v"][:, h:h + 1], wl.past_len, wl.softmax_scale)
+        heads += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per_head_flops = prefill_flops(wl) / (wl.B * wl.H)
+    return {"value": per_head_flops * heads * wl.B / el / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{heads} of {wl.H} heads (batch 0), all {wl.T} queries, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_p1000", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--extra-steps", type=int, default=10)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the attention core has no cross-GPU path in this library; heads shard with no "
+              "communication, so per-GPU throughput is the single-GPU figure.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    wl = WORKLOADS[args.workload]
+    torch.cuda.synchronize()
+    if wl.T == 1:
+        head = run_decode(wl, args.steps, args.warmup)
+        cpu = None if args.no_cpu else cpu_baseline_decode(wl, args.cpu_seconds)
+    else:
+        head, x = run_prefill(wl, args.steps, args.warmup)
+        cpu = None if args.no_cpu else cpu_baseline_prefill(wl, x, args.cpu_seconds)
+        del x
+
+    workloads = {}
+    if not args.no_extra:
+        for name in ("decode_p1000", "batched_decode", "causal_prefill", "chunked_prefill"):
+            if name == wl.name:
+                continue
+            w = WORKLOADS[name]
+            if w.T == 1:
+                r = run_decode(w, args.extra_steps, 3)
+            else:
+                r, x = run_prefill(w, args.extra_steps, 2)
+                if not args.no_cpu:
+                    r["cpu_baseline"] = cpu_baseline_prefill(w, x, min(args.cpu_seconds, 5.0))
+                del x
+            workloads[name] = r
+
+    line = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": head["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {k: head[k] for k in ("workload", "B", "H", "T", "past_len", "S", "std", "inputs",
+                                        "timing") if k in head},
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+        "workloads": workloads,
+    }
+    if "input_copies" in head:
+        line["config"]["input_copies"] = head["input_copies"]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

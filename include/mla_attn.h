@@ -32,7 +32,8 @@
  *    call returns a status and enqueues nothing. No exceptions cross the ABI.
  *    mla_last_error() gives a thread-local description of the last failure.
  *  - B == 0, H == 0 or T == 0 is a valid empty call: it returns MLA_OK.
- *  - softmax_scale is taken as a 32-bit float.
+ *  - softmax_scale is taken as a 32-bit float and must be finite and > 0
+ *    (the model's scale is an inverse square root, always positive).
  */
 #ifndef MLA_ATTN_H_
 #define MLA_ATTN_H_
@@ -53,7 +54,7 @@ typedef enum mla_status {
   MLA_ERR_NULL = 1,      /* a pointer to a non-empty tensor is NULL */
   MLA_ERR_SHAPE = 2,     /* negative size, S != past_len + T, or size beyond the launch limits */
   MLA_ERR_ALIGN = 3,     /* a tensor pointer is not 16-byte aligned */
-  MLA_ERR_SCALE = 4,     /* softmax_scale is NaN or infinite */
+  MLA_ERR_SCALE = 4,     /* softmax_scale is NaN, infinite, zero or negative */
   MLA_ERR_WORKSPACE = 5, /* decode workspace missing or smaller than required */
   MLA_ERR_DEVICE = 6     /* the HIP runtime reported an error at launch */
 } mla_status;
@@ -86,13 +87,13 @@ size_t mla_attn_decode_workspace_bytes(int32_t B, int32_t H, int32_t S);
  * for both, the "Similarities" page showing decode with p = 1000, S = 1001).
  * Shapes as above with T = 1.
  *
- * The key range of each (b, h) may be split across workgroups whose partial
- * results (fp32) are merged by a log-sum-exp combine inside the same launch.
- * workspace: caller-owned device memory of at least
- * mla_attn_decode_workspace_bytes(B, H, S) bytes (may be NULL when that is 0).
- * It must be zero-filled before its first use; every completed call leaves
- * its counters zero again, so one zero-filled buffer can be reused by any
- * sequence of calls. Calls that overlap in time must not share a workspace.
+ * When B*H is too small to fill the GPU, the key range of each (b, h) is
+ * split across workgroups whose fp32 partial results (o, max, sum) are merged
+ * by a log-sum-exp combine kernel enqueued right after on the same stream.
+ * workspace: caller-owned device scratch of at least
+ * mla_attn_decode_workspace_bytes(B, H, S) bytes (may be NULL when that is 0),
+ * 16-byte aligned. Its contents on entry do not matter and are overwritten.
+ * Calls that may run at the same time must not share a workspace.
  */
 mla_status mla_attn_decode(const void* q_nope, const void* q_pe,
                            const void* k_nope, const void* k_pe,

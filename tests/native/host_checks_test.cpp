@@ -60,9 +60,9 @@ int main() {
   // decode planning
   {
     DecodePlan pl = plan_decode(1, 64, 1001);
-    EXPECT(pl.nsplit == 16 && pl.keys_per_split == 64);
-    EXPECT(pl.workspace_bytes == pl.ws_o_bytes + pl.ws_ml_bytes + pl.ws_cnt_bytes);
-    EXPECT(pl.ws_o_bytes == size_t(64) * 16 * 128 * 4);
+    EXPECT(pl.nsplit == 8 && pl.keys_per_split == 128);
+    EXPECT(pl.workspace_bytes == pl.ws_o_bytes + pl.ws_ml_bytes);
+    EXPECT(pl.ws_o_bytes == size_t(64) * 8 * 128 * 4);
     EXPECT(pl.workspace_bytes % 256 == 0);
     pl = plan_decode(32, 64, 8192);
     EXPECT(pl.nsplit == 1 && pl.workspace_bytes == 0 && pl.keys_per_split >= 8192);
@@ -84,7 +84,7 @@ int main() {
     DecodePlan pl;
     const size_t need = plan_decode(1, 64, 1001).workspace_bytes;
     EXPECT(check_decode(p, p, p, p, p, p, p, need, 1, 64, 1001, 1000, sc, &pl).status == MLA_OK);
-    EXPECT(pl.nsplit == 16);
+    EXPECT(pl.nsplit == 8);
     EXPECT(check_decode(p, p, p, p, p, p, p, need - 1, 1, 64, 1001, 1000, sc, &pl).status == MLA_ERR_WORKSPACE);
     EXPECT(check_decode(p, p, p, p, p, p, nullptr, need, 1, 64, 1001, 1000, sc, &pl).status == MLA_ERR_WORKSPACE);
     EXPECT(check_decode(p, p, p, p, p, p, bad, need, 1, 64, 1001, 1000, sc, &pl).status == MLA_ERR_ALIGN);

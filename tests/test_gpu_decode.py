@@ -76,19 +76,19 @@ def test_decode_equals_last_row_of_prefill():
     assert_parity(to_host_f64(dec)[:, :, 0], _oracle(x, 0)[:, :, -1], "decode vs oracle")
 
 
-def test_workspace_reuse_and_rearm():
-    """One zero-filled workspace serves many calls (the counters re-arm)."""
+def test_workspace_contents_do_not_matter():
+    """The workspace is scratch: garbage (NaN bytes) on entry, reuse across calls."""
     import torch
     B, H, P = 1, 16, 2999
     x = random_inputs(B, H, 1, P, seed=8)
     d = upload(x)
     need = _lib().mla_attn_decode_workspace_bytes(B, H, P + 1)
-    log(f"case workspace reuse need={need}")
+    log(f"case workspace scratch need={need}")
     assert need > 0
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
     ref = _oracle(x, P)
     first = None
-    for it in range(4):
+    for it in range(3):
         out = torch.full((B, H, 1, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
         _gpu_decode(d, P, out=out, workspace=ws)
         bits = to_host_bits(out)
@@ -96,8 +96,7 @@ def test_workspace_reuse_and_rearm():
             first = bits
             assert_parity(to_host_f64(out), ref, "workspace first call")
         assert np.array_equal(bits, first), f"call {it} differs"
-    cnt_off = need - 256  # counters live in the last 256-byte-aligned region
-    assert int(ws[cnt_off:].count_nonzero().item()) == 0
+        ws.fill_(0xFF)
 
 
 def test_decode_future_independence_and_determinism():
