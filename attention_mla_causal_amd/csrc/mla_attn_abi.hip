@@ -41,7 +41,8 @@ mla_status mla_attn_prefill(const void* q_nope, const void* q_pe, const void* k_
                             int32_t T, int32_t S, int32_t past_len, float softmax_scale,
                             void* stream) {
   const mla::CheckResult r =
-      mla::check_prefill(q_nope, q_pe, k_nope, k_pe, v, out, B, H, T, S, past_len, softmax_scale);
+      mla::check_prefill(q_nope, q_pe, k_nope, k_pe, v, out, B, H, T, S, past_len, softmax_scale,
+                         mla::prefill_block_m());
   if (r.status != MLA_OK) return report("mla_attn_prefill", r);
   if (r.empty) return MLA_OK;
   mla::PrefillArgs a;
@@ -56,7 +57,7 @@ mla_status mla_attn_prefill(const void* q_nope, const void* q_pe, const void* k_
   a.T = T;
   a.S = S;
   a.past_len = past_len;
-  a.ntiles = (int32_t)((T + mla::kPrefillBlockM - 1) / mla::kPrefillBlockM);
+  a.ntiles = (int32_t)((T + mla::prefill_block_m() - 1) / mla::prefill_block_m());
   a.scale_log2 = softmax_scale * kLog2e;
   const hipError_t e = mla::launch_prefill(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error("mla_attn_prefill", e);

@@ -19,8 +19,6 @@
 
 namespace mla {
 
-// Prefill tiling: queries per workgroup. The kernel assumes this value.
-constexpr int64_t kPrefillBlockM = 128;
 // Decode: keys one workgroup consumes per loop trip (4 waves x 4 quarter-waves x 8 keys).
 constexpr int64_t kDecodeKeysPerTrip = 128;
 // Decode split heuristic: aim for this many workgroups (2 per CU on 256 CUs).
@@ -128,15 +126,17 @@ inline CheckResult check_common(const void* q_nope, const void* q_pe, const void
   return r;
 }
 
+// block_m: queries per prefill workgroup (a property of the kernel build).
 inline CheckResult check_prefill(const void* q_nope, const void* q_pe, const void* k_nope,
                                  const void* k_pe, const void* v, const void* out, int64_t B,
-                                 int64_t H, int64_t T, int64_t S, int64_t past_len, float scale) {
+                                 int64_t H, int64_t T, int64_t S, int64_t past_len, float scale,
+                                 int64_t block_m) {
   CheckResult r = check_common(q_nope, q_pe, k_nope, k_pe, v, out, B, H, T, S, past_len, scale);
   if (r.status != MLA_OK || r.empty) return r;
-  const int64_t tiles = (T + kPrefillBlockM - 1) / kPrefillBlockM;
+  const int64_t tiles = (T + block_m - 1) / block_m;
   if (B * H > kMaxGrid / tiles) {
-    std::snprintf(r.msg, sizeof(r.msg), "B*H*ceil(T/128) = %lld*%lld exceeds the grid limit",
-                  (long long)(B * H), (long long)tiles);
+    std::snprintf(r.msg, sizeof(r.msg), "B*H*ceil(T/%lld) = %lld*%lld exceeds the grid limit",
+                  (long long)block_m, (long long)(B * H), (long long)tiles);
     r.status = MLA_ERR_SHAPE;
   }
   return r;

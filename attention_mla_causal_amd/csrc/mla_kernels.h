@@ -15,7 +15,7 @@ struct PrefillArgs {
   const uint16_t* v;       // [B,H,S,128]
   uint16_t* out;           // [B,H,T,128]
   int32_t B, H, T, S, past_len;
-  int32_t ntiles;          // ceil(T / 128)
+  int32_t ntiles;          // ceil(T / prefill_block_m())
   float scale_log2;        // softmax_scale * log2(e)
 };
 
@@ -33,6 +33,8 @@ struct DecodeArgs {
   float scale_log2;
 };
 
+// Queries per prefill workgroup.
+int prefill_block_m();
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

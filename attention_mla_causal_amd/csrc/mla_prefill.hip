@@ -6,25 +6,34 @@
 // values" page, with the mask of the "Causal mask" page: query i sits at
 // absolute position past_len + i and sees keys 0..past_len+i.
 //
-// gfx950 design (one workgroup = 4 wave64s = 128 queries of one head):
+// gfx950 design: one workgroup = 4 wave64s, one per SIMD, each owning 64
+// queries of one head (256 queries per workgroup), with the whole 512-entry
+// register file per wave.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
-//    K rows come from LDS as the A operand, Q stays in VGPRs as the B operand.
-//    In the 32x32 accumulator every lane then owns one query (lane % 32) and
-//    16 of the 32 keys of the tile; lane and lane^32 share a query. Row max
-//    and row sum are register reductions plus one exchange with lane^32.
+//    K rows come from LDS as the A operand, Q stays in registers as the B
+//    operand. In each 32x32 accumulator a lane owns one query (lane % 32) and
+//    16 of 32 keys; lane and lane^32 share the query, so the row max and row
+//    sum are register reductions plus one exchange with lane^32. A K fragment
+//    read from LDS feeds two MFMAs (two groups of 32 queries).
 //  * The 192-wide contraction is split 128 + 64: the last 4 K-steps read the
-//    rotary key k_pe, one [S,64] tensor shared by every head, so the query
-//    and key of the pages are never concatenated in memory.
-//  * The output is formed transposed too, O^T = V^T P^T: P^T is exactly the
-//    score accumulator (converted to bf16), so the probabilities never leave
-//    registers; the V^T operand is read from a row-major V tile in LDS with
-//    ds_read_b64_tr_b16, whose key order matches the accumulator's.
-//  * Online softmax in fp32 in the exp2 domain (scale * log2 e folded into one
-//    FMA); causal tiles beyond the diagonal are never visited and only tiles
-//    that straddle it compare indices.
-//  * K/V tiles of 64 keys are prefetched into registers while the previous
-//    tile is computed, then stored to padded LDS rows (no bank conflicts on
-//    the 16-byte row reads).
+//    rotary key k_pe, one [S,64] tensor shared by every head; the joined
+//    query/key of the pages are never built in memory.
+//  * O^T = V^T P^T: P^T is the score accumulator converted to bf16, so the
+//    probabilities never leave registers; V^T fragments are read from a
+//    row-major V tile with ds_read_b64_tr_b16, whose key order matches the
+//    accumulator's. Each V fragment feeds two MFMAs.
+//  * Software pipeline: the QK^T MFMAs of tile j+1 are issued in the same
+//    block as the softmax of tile j, so the matrix cores and the VALU work of
+//    one wave overlap; then the PV MFMAs of tile j run.
+//  * Online softmax in fp32 in the exp2 domain (scale * log2 e folded into
+//    one FMA); O is rescaled only when a running max moved. Causal tiles past
+//    a wave's last query are skipped; only tiles on the diagonal are masked.
+//  * K and V tiles (32 keys) are copied straight from HBM into LDS with
+//    buffer_load_dwordx4 ... lds, double-buffered separately (K one tile ahead of
+//    V, as the pipeline needs): one barrier per tile. Rows are stored in
+//    64-byte column blocks whose 16-byte chunks are XOR-swizzled by row, which
+//    keeps both the copies and the operand reads free of bank conflicts and
+//    makes every operand read an immediate offset from two base registers.
 //  * Workgroup order: all query tiles of one head are placed on one XCD and
 //    dispatched together, heaviest (latest) tile first, so K/V blocks stream
 //    through that XCD's L2 once for all of them.
@@ -44,30 +53,35 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int DN = 128;   // non-rotary query/key dims
 constexpr int DR = 64;    // rotary dims (shared key)
 constexpr int DV = 128;   // value dims
-constexpr int BM = 128;   // queries per workgroup
-constexpr int BN = 64;    // keys per tile
 constexpr int NW = 4;     // waves per workgroup
 constexpr int NT = NW * 64;
+constexpr int QW = 32;        // queries per wave (one MFMA column group)
+constexpr int BM = NW * QW;   // 128 queries per workgroup
+constexpr int BN = 32;        // keys per tile (one 32-key MFMA row group)
 
-// One LDS stage holds a 64-key tile: k_nope, k_pe, v. Rows are unpadded and
-// their 16-byte chunks are XOR-swizzled by row, so that the direct
-// global->LDS loads (which fill 1 KiB contiguously per instruction) and the
-// MFMA operand reads (16 rows at one logical column) are both conflict-free.
-constexpr int KN_OFF = 0;
-constexpr int KP_OFF = BN * DN * 2;             // 16384
-constexpr int V_OFF = KP_OFF + BN * DR * 2;     // 24576
-constexpr int STAGE_BYTES = V_OFF + BN * DV * 2;  // 40960
-
-// physical 16-byte chunk of logical chunk c in row r
-__device__ __forceinline__ int kn_chunk(int r, int c) { return r * 16 + (c ^ (r & 15)); }
-__device__ __forceinline__ int kp_chunk(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
-__device__ __forceinline__ int v_chunk(int r, int c) { return r * 16 + (c ^ ((r & 3) << 2)); }
+// LDS tile regions, bytes. A region of BN rows of 16-byte chunks is stored
+// as column blocks of 4 chunks (64 bytes): block cb = c / 4 holds chunks
+// 4cb..4cb+3 of every row, row r at offset r * 64 within the block, and the
+// chunk c & 3 of row r at position (c & 3) ^ ((r >> 2) & 3) in that row.
+constexpr int KN_BYTES = BN * DN * 2;  // 4 column blocks
+constexpr int KP_BYTES = BN * DR * 2;  // 2 column blocks
+constexpr int K_BYTES = KN_BYTES + KP_BYTES;
+constexpr int V_BYTES = BN * DV * 2;   // 4 column blocks
+constexpr int CB_BYTES = BN * 64;      // one column block of a tile
+constexpr int CB_CHUNKS = BN * 4;
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void glb_void;
 
-__device__ __forceinline__ void load_lds16(const uint16_t* src, char* lds_dst) {
-  __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)lds_dst, 16, 0, 0);
+// Buffer resource over rows [kb, S) of one (batch, head) slice of a row-major
+// [S, ROWBYTES/2] bf16 tensor. Loads past the last row return zeros (hardware
+// range check), so the tile copies need no clamping. Built from uniform values
+// only: scalar instructions.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* slice, int64_t kb,
+                                                           int64_t S, int rowbytes) {
+  const int64_t left = S - kb;
+  const int records = left > 0 ? (int)(left * rowbytes) : 0;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)slice + kb * rowbytes), (short)0,
+                                           records, 0x00020000);
 }
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
@@ -76,157 +90,237 @@ __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+// max / sum of x over lanes l and l^32 (the two halves holding one query's keys)
+__device__ __forceinline__ float max_pair32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float sum_pair32(float x) { return x + __shfl_xor(x, 32); }
 
 __device__ __forceinline__ bf16x4 lds_tr_read(const char* p) {
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
+__device__ __forceinline__ bf16x8 lds_read16(const char* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// hard scheduling fence: nothing moves across it
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // Wait until this wave's global->LDS copies have landed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
-struct Ctx {
+// Copy rows [kb, kb+BN) of a row-major [S, ROWLEN] bf16 tensor into an LDS
+// region of NCB column blocks, in 1-KiB copies spread over the waves
+// (buffer_load_dwordx4 ... lds). Each lane's source offset within the tile is a
+// loop constant (voff[u]); rows past the last key read as zeros.
+template <int ROWLEN, int NCB>
+struct Region {
+  static constexpr int NCOPY = NCB * CB_CHUNKS / 64 / NW;  // copies per wave
+  static_assert(NCB * CB_CHUNKS % (64 * NW) == 0, "copies must divide evenly over the waves");
+  int voff[NCOPY];
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int u = 0; u < NCOPY; ++u) {
+      const int t = u * NW + wave;
+      const int pc = t * 64 + lane;  // physical chunk within the region
+      const int cb = pc / CB_CHUNKS;
+      const int r = (pc >> 2) % BN;
+      const int c4 = (pc & 3) ^ ((r >> 2) & 3);
+      voff[u] = r * ROWLEN * 2 + (cb * 4 + c4) * 16;
+    }
+  }
+  __device__ __forceinline__ void copy(const uint16_t* slice, int64_t kb, int64_t S, char* lds,
+                                       int wave) const {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(slice, kb, S, ROWLEN * 2);
+#pragma unroll
+    for (int u = 0; u < NCOPY; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (u * NW + wave) * 1024), 16,
+                                               voff[u], 0, 0, 0);
+  }
+};
+
+struct Geo {
   const uint16_t* kn_g;
   const uint16_t* kp_g;
   const uint16_t* v_g;
   int64_t S, P;
-  int tid, lane, wave, hi, l32;
+  int wave, lane;
+  Region<DN, 4> kn;
+  Region<DR, 2> kp;
+  Region<DV, 4> vv;
 };
 
-// Issue the 10 direct global->LDS copies (per wave) of key tile j into `stage`.
-// Rows past the last key are clamped to it: they are masked out of the
-// softmax, and clamping keeps every LDS value finite.
-__device__ __forceinline__ void issue_tile(const Ctx& c, int j, char* stage) {
+__device__ __forceinline__ void copy_k(const Geo& g, int j, char* kbuf) {
   const int64_t kb = (int64_t)j * BN;
+  g.kn.copy(g.kn_g, kb, g.S, kbuf, g.wave);
+  g.kp.copy(g.kp_g, kb, g.S, kbuf + KN_BYTES, g.wave);
+}
+
+__device__ __forceinline__ void copy_v(const Geo& g, int j, char* vbuf) {
+  g.vv.copy(g.v_g, (int64_t)j * BN, g.S, vbuf, g.wave);
+}
+
+// Per-lane LDS operand offsets (bytes) for the region layout above.
+struct Lane {
+  int ka_even, ka_odd;  // K fragment of rows l32 for even / odd K-steps
+  int va0, va1;         // V^T pieces: keys 16ks + 4hi + (l&15)/4 and + 8
+};
+
+// K fragment (A operand) for K-step kk (0..11) from a K tile.
+__device__ __forceinline__ bf16x8 k_frag(const char* kbuf, const Lane& ln, int kk) {
+  const int region = kk < 8 ? 0 : KN_BYTES;  // k_nope, then the shared k_pe
+  const int kq = kk < 8 ? kk : kk - 8;
+  return lds_read16(kbuf + region + (kq >> 1) * CB_BYTES + ((kq & 1) ? ln.ka_odd : ln.ka_even));
+}
+
+// V^T fragment (A operand) for K-step ks (16 keys) and dv tile n, from a V tile.
+__device__ __forceinline__ bf16x8 v_frag(const char* vbuf, const Lane& ln, int ks, int n) {
+  const char* p = vbuf + n * CB_BYTES + ks * 16 * 64;
+  const bf16x4 lo4 = lds_tr_read(p + ln.va0);
+  const bf16x4 hi4 = lds_tr_read(p + ln.va1);
+  return bf16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+}
+
+struct Acc {
+  f32x16 o[4];  // O^T accumulators: the lane's query, 64 of its 128 dims
+  float m_run;  // running max, scaled log2 domain
+  float l_run;  // this lane's share of the running sum
+};
+
+// Softmax of one tile (S^T in c: 32 keys x 32 queries; the lane holds 16
+// keys of its query), cut into slots of a few VALU ops that are spread between
+// the MFMAs of a pipeline step.
+struct Smx {
+  float mx, m_ref, alpha, psum;
+};
+constexpr int SMX_SLOTS = 19;
+
+template <int SLOT>
+__device__ __forceinline__ void smx_slot(Smx& st, f32x16& c, bf16x8 (&pc)[2], Acc& acc,
+                                         float cl2) {
+  if constexpr (SLOT < 4) {  // running max of the raw scores, 4 per slot
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int t = u * NW + c.wave;
-    const int pc = t * 64 + c.lane;
-    const int r = pc >> 4, p = pc & 15;
-    const int64_t key = (kb + r < c.S) ? kb + r : c.S - 1;
-    load_lds16(c.kn_g + key * DN + ((p ^ (r & 15)) << 3), stage + KN_OFF + t * 1024);
-  }
+    for (int r = 4 * SLOT; r < 4 * SLOT + 4; ++r) st.mx = fmaxf(st.mx, c[r]);
+  } else if constexpr (SLOT == 4) {  // new running max (scale > 0) and rescale factor
+    const float mx = max_pair32(st.mx);
+    const float m_new = fmaxf(acc.m_run, mx * cl2);
+    st.m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
+    st.alpha = __builtin_amdgcn_exp2f(acc.m_run - st.m_ref);
+    acc.m_run = m_new;
+  } else if constexpr (SLOT < 13) {  // p = 2^(scale*log2e*s - m), 2 per slot
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int t = u * NW + c.wave;
-    const int pc = t * 64 + c.lane;
-    const int r = pc >> 3, p = pc & 7;
-    const int64_t key = (kb + r < c.S) ? kb + r : c.S - 1;
-    load_lds16(c.kp_g + key * DR + ((p ^ ((r >> 1) & 7)) << 3), stage + KP_OFF + t * 1024);
-  }
+    for (int r = 2 * (SLOT - 5); r < 2 * (SLOT - 5) + 2; ++r)
+      c[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(c[r], cl2, -st.m_ref));
+  } else if constexpr (SLOT < 17) {  // row-sum share, 4 per slot
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int t = u * NW + c.wave;
-    const int pc = t * 64 + c.lane;
-    const int r = pc >> 4, p = pc & 15;
-    const int64_t key = (kb + r < c.S) ? kb + r : c.S - 1;
-    load_lds16(c.v_g + key * DV + ((p ^ ((r & 3) << 2)) << 3), stage + V_OFF + t * 1024);
+    for (int r = 4 * (SLOT - 13); r < 4 * (SLOT - 13) + 4; ++r) st.psum += c[r];
+    if constexpr (SLOT == 16) acc.l_run = acc.l_run * st.alpha + st.psum;
+  } else if constexpr (SLOT < SMX_SLOTS) {  // bf16 P^T operand for K-step ks
+    constexpr int ks = SLOT - 17;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pc[ks][e] = (__bf16)c[8 * ks + e];
   }
 }
 
-struct State {
-  f32x16 o[4];   // O^T accumulators: lane owns query l32, 64 of its 128 dims
-  float m_run;   // running max, scaled log2 domain
-  float l_run;   // this lane's share of the running sum
-};
-
-// One 64-key tile for one wave's 32 queries.
-__device__ __forceinline__ void compute_tile(const Ctx& c, const bf16x8 (&qf)[12], State& st,
-                                             const char* stage, int64_t kb, int64_t q0w,
-                                             int64_t wave_kfull, float cl2) {
-  // ---- S^T = K Q^T: two 32-key halves interleaved for independent MFMA chains
-  f32x16 s0, s1;
+// Hide keys past each lane's query (and past the last key) on a diagonal tile:
+// key kb + off is visible iff off <= min(lim, S - 1) - kb (computed once, 32-bit).
+__device__ __forceinline__ void mask_tile(f32x16& sc, int64_t kb, int64_t lim, int64_t S, int hi) {
+  const int64_t last = (lim < S - 1 ? lim : S - 1) - kb;
+  const int thr = last < -1 ? -1 : (last > BN ? BN : (int)last);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    s0[r] = 0.0f;
-    s1[r] = 0.0f;
+    const int off = 8 * (r >> 2) + 4 * hi + (r & 3);
+    if (off > thr) sc[r] = -INFINITY;
   }
-  const int r0 = c.l32, r1 = 32 + c.l32;
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    const int lc = 2 * kk + c.hi;
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(stage + KN_OFF + kn_chunk(r0, lc) * 16);
-    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(stage + KN_OFF + kn_chunk(r1, lc) * 16);
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], s1, 0, 0, 0);
-  }
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int lc = 2 * kk + c.hi;
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(stage + KP_OFF + kp_chunk(r0, lc) * 16);
-    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(stage + KP_OFF + kp_chunk(r1, lc) * 16);
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[8 + kk], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[8 + kk], s1, 0, 0, 0);
-  }
+}
 
-  // ---- causal mask, only on tiles that cross this wave's diagonal
-  if (kb + BN > wave_kfull) {
-    const int64_t lim = c.P + q0w + c.l32;  // last key this lane's query sees
+// One pipeline step's MFMA stream, 20 phases with one MFMA each: phases
+// 0..11 are the QK K-steps of the next tile (A = K fragment), phases 12..19
+// the PV MFMAs of the previous tile (A = V^T fragment, K-step (p-12)/4, dv
+// tile (p-12)%4). Operand fragments are read from LDS RING-1 phases ahead
+// through a ring of RING registers, so LDS latency hides behind MFMAs; the
+// softmax slot SLOT0+p is issued in phase p (SLOT0 < 0: none). WITH_QK /
+// WITH_PV select the parts that run.
+#ifndef MLA_PREFILL_RING
+#define MLA_PREFILL_RING 4
+#endif
+constexpr int RING = MLA_PREFILL_RING;
+
+template <bool WITH_QK, bool WITH_PV>
+__device__ __forceinline__ bf16x8 stream_frag(int p, const char* kbuf, const char* vbuf,
+                                              const Lane& ln) {
+  constexpr int first = WITH_QK ? 0 : 12;
+  (void)first;
+  if (p < 12) return k_frag(kbuf, ln, p);
+  const int q = p - 12;
+  return v_frag(vbuf, ln, q >> 2, q & 3);
+}
+
+template <int SLOT0, bool WITH_QK, bool WITH_PV>
+__device__ __forceinline__ void mfma_stream(f32x16& s, const char* kbuf, Acc& acc,
+                                            const char* vbuf, const Lane& ln,
+                                            const bf16x8 (&qf)[12], const bf16x8 (&pp)[2],
+                                            Smx& st, f32x16& c, bf16x8 (&pc)[2], float cl2) {
+  constexpr int P0 = WITH_QK ? 0 : 12;
+  constexpr int P1 = WITH_PV ? 20 : 12;
+  if constexpr (WITH_QK) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t key = kb + 8 * (r >> 2) + 4 * c.hi + (r & 3);
-      if (key > lim || key >= c.S) s0[r] = -INFINITY;
-      if (key + 32 > lim || key + 32 >= c.S) s1[r] = -INFINITY;
+    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+  }
+  bf16x8 fr[RING];
+#pragma unroll
+  for (int p = P0; p < P0 + RING - 1 && p < P1; ++p) fr[p % RING] = stream_frag<WITH_QK, WITH_PV>(p, kbuf, vbuf, ln);
+  fence();
+#pragma unroll
+  for (int p = P0; p < P1; ++p) {
+    if (p + RING - 1 < P1) fr[(p + RING - 1) % RING] = stream_frag<WITH_QK, WITH_PV>(p + RING - 1, kbuf, vbuf, ln);
+    if (p < 12)
+      s = mfma(fr[p % RING], qf[p], s);
+    else
+      acc.o[(p - 12) & 3] = mfma(fr[p % RING], pp[(p - 12) >> 2], acc.o[(p - 12) & 3]);
+    if constexpr (SLOT0 >= 0) {
+#define MLA_SLOT(K) if (p == K) smx_slot<SLOT0 + K>(st, c, pc, acc, cl2);
+      MLA_SLOT(0) MLA_SLOT(1) MLA_SLOT(2) MLA_SLOT(3) MLA_SLOT(4) MLA_SLOT(5) MLA_SLOT(6)
+      MLA_SLOT(7) MLA_SLOT(8) MLA_SLOT(9) MLA_SLOT(10) MLA_SLOT(11) MLA_SLOT(12) MLA_SLOT(13)
+      MLA_SLOT(14) MLA_SLOT(15) MLA_SLOT(16) MLA_SLOT(17) MLA_SLOT(18) MLA_SLOT(19)
+#undef MLA_SLOT
     }
+    fence();
   }
+}
 
-  // ---- online softmax (scale > 0: the max of scaled scores is scale * max)
-  float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-  mx = fmaxf(mx, xor32(mx));
-  const float m_new = fmaxf(st.m_run, mx * cl2);
-  const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_ref);
-  st.m_run = m_new;
-  float psum = 0.0f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], cl2, -m_ref));
-    s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], cl2, -m_ref));
-    psum += s0[r] + s1[r];
+// Remaining softmax slots, run back to back (no MFMA work to hide them behind).
+template <int SLOT, int END>
+__device__ __forceinline__ void smx_rest(Smx& st, f32x16& c, bf16x8 (&pc)[2], Acc& acc,
+                                         float cl2) {
+  if constexpr (SLOT < END) {
+    smx_slot<SLOT>(st, c, pc, acc, cl2);
+    smx_rest<SLOT + 1, END>(st, c, pc, acc, cl2);
   }
-  st.l_run = st.l_run * alpha + psum;
-  // rescale O only when some query of the wave raised its max
-  if (__builtin_amdgcn_read_exec() && __any(alpha != 1.0f)) {
+}
+
+// O *= alpha when some query of the wave raised its max (rare after the first tiles).
+__device__ __forceinline__ void rescale_o(Acc& acc, float alpha) {
+  if (__any(alpha != 1.0f)) {
 #pragma unroll
     for (int n = 0; n < 4; ++n)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st.o[n][r] *= alpha;
-  }
-
-  // ---- O^T += V^T P^T over 4 K-steps of 16 keys
-  const int sl = c.lane & 15;
-  const int grp = (c.lane >> 4) & 1;
-  // byte offset of this lane's 8-byte piece of V, K-step 0, dims 32n + ...
-  const int vrow = 4 * c.hi + (sl >> 2);
-  const int vcol = 2 * grp + ((sl & 3) >> 1);  // logical chunk within a 32-dim group
-  const int vhalf = 8 * (sl & 1);
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const f32x16& sp = (ks >> 1) ? s1 : s0;
-    const int h8 = 8 * (ks & 1);
-    bf16x8 pb;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sp[h8 + e];
-    const int kr = 32 * (ks >> 1) + 16 * (ks & 1) + vrow;
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const char* vp = stage + V_OFF + v_chunk(kr, 4 * n + vcol) * 16 + vhalf;
-      const bf16x4 lo4 = lds_tr_read(vp);
-      const bf16x4 hi4 = lds_tr_read(vp + 8 * 16 * 16);  // row kr + 8: same swizzle
-      const bf16x8 va = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-      st.o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, st.o[n], 0, 0, 0);
-    }
+      for (int r = 0; r < 16; ++r) acc.o[n][r] *= alpha;
   }
 }
 
 __global__ __launch_bounds__(NT, 2) void mla_prefill_kernel(PrefillArgs a) {
-  // two stages, separate objects so the compiler can tell the in-flight copy
-  // into one from reads of the other
-  __shared__ __attribute__((aligned(1024))) char stage0[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char stage1[STAGE_BYTES];
+  // separate LDS objects per buffer so the compiler can tell an in-flight copy
+  // into one from reads of another
+  __shared__ __attribute__((aligned(1024))) char kbuf0[K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[V_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[V_BYTES];
 
   // ---- which (batch, head, query tile) this workgroup owns
   const int nwg = gridDim.x;
@@ -237,96 +331,157 @@ __global__ __launch_bounds__(NT, 2) void mla_prefill_kernel(PrefillArgs a) {
   const int b = bh / a.H;
   const int q0 = qt * BM;
 
-  Ctx c;
-  c.tid = threadIdx.x;
-  c.lane = c.tid & 63;
-  c.wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
-  c.hi = c.lane >> 5;
-  c.l32 = c.lane & 31;
-  c.S = a.S;
-  c.P = a.past_len;
-  const int64_t T = a.T;
-  c.kn_g = a.k_nope + (int64_t)bh * c.S * DN;
-  c.kp_g = a.k_pe + (int64_t)b * c.S * DR;
-  c.v_g = a.v + (int64_t)bh * c.S * DV;
-  const int64_t q0w = q0 + c.wave * 32;
+  Geo geo;
+  const int tid = threadIdx.x;
+  geo.lane = tid & 63;
+  geo.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  geo.S = a.S;
+  geo.P = a.past_len;
+  geo.kn_g = a.k_nope + (int64_t)bh * geo.S * DN;
+  geo.kp_g = a.k_pe + (int64_t)b * geo.S * DR;
+  geo.v_g = a.v + (int64_t)bh * geo.S * DV;
+  geo.kn.init(geo.wave, geo.lane);
+  geo.kp.init(geo.wave, geo.lane);
+  geo.vv.init(geo.wave, geo.lane);
+  const int lane = geo.lane, hi = lane >> 5, l32 = lane & 31;
+  const int64_t T = a.T, S = geo.S, P = geo.P;
+  const int64_t q0w = q0 + geo.wave * QW;
 
   // ---- key range of the workgroup: [0, P + last query + 1)
   const int64_t q_last = (q0 + BM < T ? q0 + BM : T) - 1;
-  const int64_t kend = c.P + q_last + 1;
-  const int nblocks = (int)((kend + BN - 1) / BN);
+  const int nblocks = (int)((P + q_last + 1 + BN - 1) / BN);
+  const bool wave_live = q0w < T;
+  // last tile holding a key that some query of this wave sees (-1: none)
+  const int wave_last =
+      wave_live ? (int)((P + (q0w + QW - 1 < T ? q0w + QW - 1 : T - 1)) / BN) : -1;
+  const int64_t lim = P + q0w + l32;  // last key this lane's query sees
 
-  issue_tile(c, 0, stage0);
+  copy_k(geo, 0, kbuf0);
 
-  // ---- query fragment (B operand of S^T = K Q^T): 8 dims of the lane's query per K-step
-  const uint16_t* qn_g = a.q_nope + (int64_t)bh * T * DN;
-  const uint16_t* qp_g = a.q_pe + (int64_t)bh * T * DR;
+  // ---- query fragments (B operand): 8 dims of the lane's query per K-step
   bf16x8 qf[12];
   {
-    const int64_t myq = q0w + c.l32;
-    const int koff = 8 * c.hi;
+    const int64_t myq = q0w + l32;
     const bool ok = myq < T;
+    const uint16_t* qn = a.q_nope + ((int64_t)bh * T + myq) * DN + 8 * hi;
+    const uint16_t* qp = a.q_pe + ((int64_t)bh * T + myq) * DR + 8 * hi;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      qf[kk] = as_bf16x8(ok ? ldg16(qn_g + myq * DN + 16 * kk + koff) : u32x4{0, 0, 0, 0});
+    for (int kk = 0; kk < 8; ++kk) qf[kk] = as_bf16x8(ok ? ldg16(qn + 16 * kk) : u32x4{0, 0, 0, 0});
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      qf[8 + kk] = as_bf16x8(ok ? ldg16(qp_g + myq * DR + 16 * kk + koff) : u32x4{0, 0, 0, 0});
+    for (int kk = 0; kk < 4; ++kk) qf[8 + kk] = as_bf16x8(ok ? ldg16(qp + 16 * kk) : u32x4{0, 0, 0, 0});
   }
 
-  const bool wave_live = q0w < T;
-  const int64_t wave_q_last = (q0w + 31 < T ? q0w + 31 : T - 1);
-  const int64_t wave_kend = c.P + wave_q_last + 1;  // keys from here on are hidden from the wave
-  const int64_t wave_kfull = c.P + q0w + 1;         // keys below are visible to the whole wave
-  const float cl2 = a.scale_log2;
+  Lane ln;
+  {
+    const int x = (l32 >> 2) & 3;
+    ln.ka_even = l32 * 64 + ((hi) ^ x) * 16;
+    ln.ka_odd = l32 * 64 + ((2 + hi) ^ x) * 16;
+    const int sl = lane & 15, grp = (lane >> 4) & 1;
+    const int vrow = 4 * hi + (sl >> 2);
+    const int vc4 = 2 * grp + ((sl & 3) >> 1);
+    ln.va0 = vrow * 64 + ((vc4 ^ hi) * 16) + 8 * (sl & 1);
+    ln.va1 = (vrow + 8) * 64 + ((vc4 ^ (hi + 2)) * 16) + 8 * (sl & 1);
+  }
 
-  State st;
+  const float cl2 = a.scale_log2;
+  Acc acc;
 #pragma unroll
   for (int n = 0; n < 4; ++n)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st.o[n][r] = 0.0f;
-  st.m_run = -INFINITY;
-  st.l_run = 0.0f;
+    for (int r = 0; r < 16; ++r) acc.o[n][r] = 0.0f;
+  acc.m_run = -INFINITY;
+  acc.l_run = 0.0f;
 
-  // ---- main loop, two tiles per trip so each stage is a fixed LDS object
-  for (int j = 0; j < nblocks; j += 2) {
+  auto needs_mask = [&](int j) { return (int64_t)j * BN + BN > P + q0w + 1; };
+
+  // ---- pipeline. Step j: QK of tile j+1, softmax of tile j, PV of tile j-1.
+  // Tile t's K lives in kbuf[t % 2], its V in vbuf[t % 2]; step j issues the
+  // copies of K_{j+2} and V_j (V trails K by two tiles).
+  f32x16 sa, sb;         // scores of alternating tiles
+  bf16x8 pa[2], pb[2];   // P^T operands of alternating tiles
+  Smx st;
+  copy_k(geo, 1 < nblocks ? 1 : 0, kbuf1);
+  wait_vmem();
+  __syncthreads();
+  if (wave_live) {
+    mfma_stream<-1, true, false>(sa, kbuf0, acc, vbuf0, ln, qf, pa, st, sb, pb, cl2);
+    if (needs_mask(0)) mask_tile(sa, 0, lim, S, hi);
+  }
+
+  // step 0: QK of tile 1 with the softmax of tile 0; no PV yet
+  wait_vmem();
+  __syncthreads();
+  if (2 < nblocks) copy_k(geo, 2, kbuf0);
+  copy_v(geo, 0, vbuf0);
+  if (wave_live) {
+    st.mx = -INFINITY;
+    st.psum = 0.0f;
+    mfma_stream<0, true, false>(sb, kbuf1, acc, vbuf0, ln, qf, pb, st, sa, pa, cl2);
+    smx_rest<12, SMX_SLOTS>(st, sa, pa, acc, cl2);
+    rescale_o(acc, st.alpha);
+    if (needs_mask(1)) mask_tile(sb, BN, lim, S, hi);
+  }
+
+  // steps j >= 1
+  auto step = [&](int j, f32x16& cur, f32x16& nxt, bf16x8 (&pcur)[2],
+                  const bf16x8 (&pprev)[2], const char* knxt, const char* vprev, char* kfree,
+                  char* vfree) {
     wait_vmem();
-    __syncthreads();  // tile j is in stage0 for everyone; stage1 is free
-    if (j + 1 < nblocks) issue_tile(c, j + 1, stage1);
-    {
-      const int64_t kb = (int64_t)j * BN;
-      if (wave_live && kb < wave_kend) compute_tile(c, qf, st, stage0, kb, q0w, wave_kfull, cl2);
+    __syncthreads();  // K_{j+1} and V_{j-1} have landed; kfree and vfree are no longer read
+    if (j + 2 < nblocks) copy_k(geo, j + 2, kfree);
+    copy_v(geo, j, vfree);
+    if (j <= wave_last + 1) {
+      st.mx = -INFINITY;
+      st.psum = 0.0f;
+      // QK of tile j+1 and PV of tile j-1, with the softmax of tile j in between
+      mfma_stream<0, true, true>(nxt, knxt, acc, vprev, ln, qf, pprev, st, cur, pcur, cl2);
+      rescale_o(acc, st.alpha);
+      if (needs_mask(j + 1)) mask_tile(nxt, (int64_t)(j + 1) * BN, lim, S, hi);
     }
-    if (j + 1 >= nblocks) break;
-    wait_vmem();
-    __syncthreads();  // tile j+1 is in stage1; stage0 is free
-    if (j + 2 < nblocks) issue_tile(c, j + 2, stage0);
-    {
-      const int64_t kb = (int64_t)(j + 1) * BN;
-      if (wave_live && kb < wave_kend) compute_tile(c, qf, st, stage1, kb, q0w, wave_kfull, cl2);
-    }
+  };
+
+  // Register roles alternate: odd steps read scores from sb and P^T from pa
+  // and write sa / pb; even steps the reverse. The loop is unrolled by two so
+  // that every LDS buffer and register role is fixed in each copy of the step.
+  int j = 1;
+  for (; j + 1 < nblocks; j += 2) {
+    step(j, sb, sa, pb, pa, kbuf0, vbuf0, kbuf1, vbuf1);
+    step(j + 1, sa, sb, pa, pb, kbuf1, vbuf1, kbuf0, vbuf0);
+  }
+  if (j < nblocks) step(j, sb, sa, pb, pa, kbuf0, vbuf0, kbuf1, vbuf1);
+
+  // ---- drain: PV of the last tile
+  wait_vmem();
+  __syncthreads();
+  if (nblocks - 1 <= wave_last) {
+    // the last step (j = nblocks-1) left tile j's P^T in pb if j is odd, pa if even
+    if ((nblocks - 1) & 1)
+      mfma_stream<-1, false, true>(sb, kbuf0, acc, vbuf1, ln, qf, pb, st, sa, pa, cl2);
+    else
+      mfma_stream<-1, false, true>(sb, kbuf0, acc, vbuf0, ln, qf, pa, st, sa, pb, cl2);
   }
 
   // ---- epilogue: divide by the full row sum and store bf16
   if (!wave_live) return;
-  const float l_tot = st.l_run + xor32(st.l_run);
-  const float inv = 1.0f / l_tot;
-  const int64_t myq = q0w + c.l32;
+  const float inv = 1.0f / sum_pair32(acc.l_run);
+  const int64_t myq = q0w + l32;
   if (myq >= T) return;
   uint16_t* out_row = a.out + ((int64_t)bh * T + myq) * DV;
 #pragma unroll
   for (int n = 0; n < 4; ++n)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int dv0 = 32 * n + 8 * g + 4 * c.hi;
+    for (int gg = 0; gg < 4; ++gg) {
+      const int dv0 = 32 * n + 8 * gg + 4 * hi;
       bf16x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[n][4 * g + e] * inv);
+      for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc.o[n][4 * gg + e] * inv);
       *reinterpret_cast<bf16x4*>(out_row + dv0) = w;
     }
 }
 
 }  // namespace
+
+int prefill_block_m() { return BM; }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int grid = a.B * a.H * a.ntiles;

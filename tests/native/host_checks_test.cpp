@@ -26,36 +26,36 @@ int main() {
   using namespace mla;
 
   // valid prefill
-  EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 16, 16, 0, sc).status == MLA_OK);
-  EXPECT(!check_prefill(p, p, p, p, p, p, 1, 4, 16, 16, 0, sc).empty);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 16, 16, 0, sc, 128).status == MLA_OK);
+  EXPECT(!check_prefill(p, p, p, p, p, p, 1, 4, 16, 16, 0, sc, 128).empty);
   // shapes
-  EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 16, 17, 0, sc).status == MLA_ERR_SHAPE);
-  EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 16, 20, 5, sc).status == MLA_ERR_SHAPE);
-  EXPECT(check_prefill(p, p, p, p, p, p, -1, 4, 16, 16, 0, sc).status == MLA_ERR_SHAPE);
-  EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 16, 15, -1, sc).status == MLA_ERR_SHAPE);
-  EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 1, 2147483647LL + 1, 2147483647LL, sc).status == MLA_OK);
-  EXPECT(check_prefill(p, p, p, p, p, p, 65536, 65536, 2048, 2048, 0, sc).status == MLA_ERR_SHAPE);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 16, 17, 0, sc, 128).status == MLA_ERR_SHAPE);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 16, 20, 5, sc, 128).status == MLA_ERR_SHAPE);
+  EXPECT(check_prefill(p, p, p, p, p, p, -1, 4, 16, 16, 0, sc, 128).status == MLA_ERR_SHAPE);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 16, 15, -1, sc, 128).status == MLA_ERR_SHAPE);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 1, 2147483647LL + 1, 2147483647LL, sc, 128).status == MLA_OK);
+  EXPECT(check_prefill(p, p, p, p, p, p, 65536, 65536, 2048, 2048, 0, sc, 128).status == MLA_ERR_SHAPE);
   // empty calls are valid no-ops, even with NULL pointers
   {
-    CheckResult r = check_prefill(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 4, 16, 16, 0, sc);
+    CheckResult r = check_prefill(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 4, 16, 16, 0, sc, 128);
     EXPECT(r.status == MLA_OK && r.empty);
-    r = check_prefill(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 1, 4, 0, 7, 7, sc);
+    r = check_prefill(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 1, 4, 0, 7, 7, sc, 128);
     EXPECT(r.status == MLA_OK && r.empty);
   }
   // NULL and alignment, each argument in turn
   for (int i = 0; i < 6; ++i) {
     const void* a[6] = {p, p, p, p, p, p};
     a[i] = nullptr;
-    EXPECT(check_prefill(a[0], a[1], a[2], a[3], a[4], a[5], 1, 2, 3, 3, 0, sc).status == MLA_ERR_NULL);
+    EXPECT(check_prefill(a[0], a[1], a[2], a[3], a[4], a[5], 1, 2, 3, 3, 0, sc, 128).status == MLA_ERR_NULL);
     a[i] = bad;
-    EXPECT(check_prefill(a[0], a[1], a[2], a[3], a[4], a[5], 1, 2, 3, 3, 0, sc).status == MLA_ERR_ALIGN);
+    EXPECT(check_prefill(a[0], a[1], a[2], a[3], a[4], a[5], 1, 2, 3, 3, 0, sc, 128).status == MLA_ERR_ALIGN);
   }
   // scale
-  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, NAN).status == MLA_ERR_SCALE);
-  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, INFINITY).status == MLA_ERR_SCALE);
-  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, 0.0f).status == MLA_ERR_SCALE);
-  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, -0.5f).status == MLA_ERR_SCALE);
-  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, 3.0e38f).status == MLA_ERR_SCALE);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, NAN, 128).status == MLA_ERR_SCALE);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, INFINITY, 128).status == MLA_ERR_SCALE);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, 0.0f, 128).status == MLA_ERR_SCALE);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, -0.5f, 128).status == MLA_ERR_SCALE);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, 3.0e38f, 128).status == MLA_ERR_SCALE);
 
   // decode planning
   {
