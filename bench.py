@@ -264,7 +264,22 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--extra-steps", type=int, default=10)
+    ap.add_argument("--eager", action="store_true",
+                    help="time decode with plain launches instead of a HIP graph (profiler runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes three times (counter calibration)")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        a = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": args.copy_calibration}))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -281,7 +296,7 @@ def main():
     wl = WORKLOADS[args.workload]
     torch.cuda.synchronize()
     if wl.T == 1:
-        head = run_decode(wl, args.steps, args.warmup)
+        head = run_decode(wl, args.steps, args.warmup, graph=not args.eager)
         cpu = None if args.no_cpu else cpu_baseline_decode(wl, args.cpu_seconds)
     else:
         head, x = run_prefill(wl, args.steps, args.warmup)
