@@ -6,25 +6,25 @@
 // values" page, with the mask of the "Causal mask" page: query i sits at
 // absolute position past_len + i and sees keys 0..past_len+i.
 //
-// gfx950 design: one workgroup = 4 wave64s, one per SIMD, each owning 64
-// queries of one head (256 queries per workgroup), with the whole 512-entry
-// register file per wave.
+// gfx950 design: one workgroup = 4 wave64s (one per SIMD) owning 128 queries of
+// one head, 32 per wave; two workgroups share a CU, so each SIMD interleaves
+// the MFMA streams of two waves from different workgroups.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    K rows come from LDS as the A operand, Q stays in registers as the B
-//    operand. In each 32x32 accumulator a lane owns one query (lane % 32) and
-//    16 of 32 keys; lane and lane^32 share the query, so the row max and row
-//    sum are register reductions plus one exchange with lane^32. A K fragment
-//    read from LDS feeds two MFMAs (two groups of 32 queries).
+//    operand. In the 32x32 accumulator a lane owns one query (lane % 32) and
+//    16 of 32 keys; lane and lane^32 share the query, so the row max is a
+//    register reduction plus one v_permlane32_swap exchange.
 //  * The 192-wide contraction is split 128 + 64: the last 4 K-steps read the
 //    rotary key k_pe, one [S,64] tensor shared by every head; the joined
 //    query/key of the pages are never built in memory.
 //  * O^T = V^T P^T: P^T is the score accumulator converted to bf16, so the
 //    probabilities never leave registers; V^T fragments are read from a
 //    row-major V tile with ds_read_b64_tr_b16, whose key order matches the
-//    accumulator's. Each V fragment feeds two MFMAs.
-//  * Software pipeline: the QK^T MFMAs of tile j+1 are issued in the same
-//    block as the softmax of tile j, so the matrix cores and the VALU work of
-//    one wave overlap; then the PV MFMAs of tile j run.
+//    accumulator's.
+//  * Software pipeline over 32-key tiles: step j issues the 12 QK MFMAs of tile
+//    j+1 and the 8 PV MFMAs of tile j-1 as one stream, with the softmax of tile
+//    j cut into slots of a few VALU ops placed between those MFMAs (and pinned
+//    there, so the compiler cannot sink them past the stream).
 //  * Online softmax in fp32 in the exp2 domain (scale * log2 e folded into
 //    one FMA); O is rescaled only when a running max moved. Causal tiles past
 //    a wave's last query are skipped; only tiles on the diagonal are masked.
@@ -34,9 +34,10 @@
 //    64-byte column blocks whose 16-byte chunks are XOR-swizzled by row, which
 //    keeps both the copies and the operand reads free of bank conflicts and
 //    makes every operand read an immediate offset from two base registers.
-//  * Workgroup order: all query tiles of one head are placed on one XCD and
-//    dispatched together, heaviest (latest) tile first, so K/V blocks stream
-//    through that XCD's L2 once for all of them.
+//  * Workgroup order: all query tiles of one head are placed on one XCD; with
+//    many cached keys they are dispatched head by head (K/V blocks stream
+//    through that XCD's L2 once for all of a head's tiles), and when the causal
+//    triangle dominates, heaviest tile first across the XCD's heads.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -90,8 +91,18 @@ __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-// max / sum of x over lanes l and l^32 (the two halves holding one query's keys)
-__device__ __forceinline__ float max_pair32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+// x of lane l^32 (the other half holding the same query's keys), through
+// v_permlane32_swap_b32 (a VALU op; no LDS round trip). The empty asm hides
+// from the optimiser that both swap operands hold the same value.
+__device__ __forceinline__ float other_half(float x) {
+  float y = x;
+  asm volatile("" : "+v"(y));
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, y), false, false);
+  // r[0]: lanes 32..63 now hold x of lanes 0..31; r[1]: lanes 0..31 hold x of lanes 32..63
+  return __builtin_bit_cast(float, (unsigned)((__lane_id() < 32) ? r[1] : r[0]));
+}
+__device__ __forceinline__ float max_pair32(float x) { return fmaxf(x, other_half(x)); }
 __device__ __forceinline__ float sum_pair32(float x) { return x + __shfl_xor(x, 32); }
 
 __device__ __forceinline__ bf16x4 lds_tr_read(const char* p) {
@@ -106,6 +117,12 @@ __device__ __forceinline__ bf16x8 lds_read16(const char* p) {
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+
+// Keep a value computed where it stands: without this, the optimiser sinks the
+// softmax arithmetic whose results are only needed after the MFMA block out of
+// it, where nothing overlaps it.
+template <typename T>
+__device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
 
 // hard scheduling fence: nothing moves across it
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
@@ -214,16 +231,21 @@ __device__ __forceinline__ void smx_slot(Smx& st, f32x16& c, bf16x8 (&pc)[2], Ac
     acc.m_run = m_new;
   } else if constexpr (SLOT < 13) {  // p = 2^(scale*log2e*s - m), 2 per slot
 #pragma unroll
-    for (int r = 2 * (SLOT - 5); r < 2 * (SLOT - 5) + 2; ++r)
-      c[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(c[r], cl2, -st.m_ref));
+    for (int r = 2 * (SLOT - 5); r < 2 * (SLOT - 5) + 2; ++r) {
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(c[r], cl2, -st.m_ref));
+      pin(p);
+      c[r] = p;
+    }
   } else if constexpr (SLOT < 17) {  // row-sum share, 4 per slot
 #pragma unroll
     for (int r = 4 * (SLOT - 13); r < 4 * (SLOT - 13) + 4; ++r) st.psum += c[r];
+    pin(st.psum);
     if constexpr (SLOT == 16) acc.l_run = acc.l_run * st.alpha + st.psum;
   } else if constexpr (SLOT < SMX_SLOTS) {  // bf16 P^T operand for K-step ks
     constexpr int ks = SLOT - 17;
 #pragma unroll
     for (int e = 0; e < 8; ++e) pc[ks][e] = (__bf16)c[8 * ks + e];
+    pin(pc[ks]);
   }
 }
 
@@ -325,9 +347,25 @@ __global__ __launch_bounds__(NT, 2) void mla_prefill_kernel(PrefillArgs a) {
   // ---- which (batch, head, query tile) this workgroup owns
   const int nwg = gridDim.x;
   const int wg = blockIdx.x;
-  const int logical = (nwg % 8 == 0) ? (wg % 8) * (nwg / 8) + wg / 8 : wg;
-  const int bh = logical / a.ntiles;
-  const int qt = a.ntiles - 1 - logical % a.ntiles;
+  // Each XCD (wg % 8) takes a contiguous range of heads. When query tiles
+  // differ a lot in work (few cached keys: the causal triangle dominates), the
+  // XCD dispatches its tiles heaviest first across all of its heads
+  // (longest-job-first); otherwise head by head, heaviest tile first, so a
+  // head's K/V streams through the XCD's L2 for all its tiles at once.
+  int bh, qt;
+  {
+    const int per = nwg / 8, i = wg / 8;
+    const bool uneven = 2 * (a.past_len + (int64_t)BM) < a.past_len + (int64_t)a.T;
+    if (nwg % 8 == 0 && per % a.ntiles == 0 && uneven) {
+      const int nh = per / a.ntiles;
+      bh = (wg % 8) * nh + i % nh;
+      qt = a.ntiles - 1 - i / nh;
+    } else {
+      const int logical = (nwg % 8 == 0) ? (wg % 8) * per + i : wg;
+      bh = logical / a.ntiles;
+      qt = a.ntiles - 1 - logical % a.ntiles;
+    }
+  }
   const int b = bh / a.H;
   const int q0 = qt * BM;
 

@@ -94,12 +94,26 @@ def to_dev(bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
+RAMP_SECONDS = 0.3  # untimed warm-up lasts at least this long: the GPU clock ramps up under load
+
+
+def warm_up(fn, warmup):
+    """Run at least `warmup` untimed steps, and keep going until RAMP_SECONDS have passed."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t0 < RAMP_SECONDS:
+        fn(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def time_graph(fn, steps, warmup):
     """Warm up, capture `steps` calls in one HIP graph, time one replay."""
     import torch
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
+    warm_up(fn, warmup)
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -126,9 +140,7 @@ def time_graph(fn, steps, warmup):
 
 def time_eager(fn, steps, warmup):
     import torch
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
+    warm_up(fn, warmup)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -263,7 +275,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--extra-steps", type=int, default=10)
+    ap.add_argument("--extra-steps", type=int, default=20)
     ap.add_argument("--eager", action="store_true",
                     help="time decode with plain launches instead of a HIP graph (profiler runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -325,6 +337,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_min_seconds": RAMP_SECONDS,
         "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
