@@ -464,6 +464,13 @@ __global__ __launch_bounds__(NT, 2) void mla_prefill_kernel(PrefillArgs a) {
   auto step = [&](int j, f32x16& cur, f32x16& nxt, bf16x8 (&pcur)[2],
                   const bf16x8 (&pprev)[2], const char* knxt, const char* vprev, char* kfree,
                   char* vfree) {
+    // The two workgroups sharing a CU take turns at the higher issue priority.
+    // Left to age-based arbitration, the older one runs ~25% faster per step,
+    // and the round of workgroups that follows ends unevenly.
+    if ((j + blockIdx.x) & 1)
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(0);
     wait_vmem();
     __syncthreads();  // K_{j+1} and V_{j-1} have landed; kfree and vfree are no longer read
     if (j + 2 < nblocks) copy_k(geo, j + 2, kfree);
