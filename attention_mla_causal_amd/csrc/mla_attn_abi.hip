@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
+#include <atomic>
 #include <cstring>
 
 #include "../../include/mla_attn.h"
@@ -88,6 +89,25 @@ mla_status mla_attn_decode(const void* q_nope, const void* q_pe, const void* k_n
   char* ws = static_cast<char*>(workspace);
   a.ws_o = plan.nsplit > 1 ? reinterpret_cast<float*>(ws) : nullptr;
   a.ws_ml = plan.nsplit > 1 ? reinterpret_cast<float*>(ws + plan.ws_o_bytes) : nullptr;
+  a.ws_flag = plan.nsplit > 1
+                  ? reinterpret_cast<unsigned long long*>(ws + plan.ws_o_bytes + plan.ws_ml_bytes)
+                  : nullptr;
+  {
+    // A fresh tag per call: completion flags left by earlier calls (or any
+    // garbage in the workspace) hold another value and count as not done.
+    static std::atomic<unsigned long long> next_tag{0x6d6c615f00000001ull};
+    a.tag = next_tag.fetch_add(1);
+  }
+  {
+    // The split kernel merges the partials itself when every split of a
+    // (b, h) runs on one XCD (workgroup w runs on XCD w % 8, and the kernel
+    // hands each XCD whole (b, h) groups); otherwise a second kernel merges.
+    const int64_t grid = (int64_t)B * H * plan.nsplit;
+    a.fused = (plan.nsplit > 1 && plan.nsplit <= 64 && grid % 8 == 0 &&
+               (grid / 8) % plan.nsplit == 0)
+                  ? 1
+                  : 0;
+  }
   a.B = B;
   a.H = H;
   a.S = S;

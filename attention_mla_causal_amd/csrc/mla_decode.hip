@@ -18,11 +18,15 @@
 //  * Quarter-waves, then waves, are merged by log-sum-exp. When the key range
 //    of a (b, h) is split over several workgroups (to fill the chip when B*H
 //    is small), each writes an fp32 partial (o[128], max, sum) to the
-//    workspace and a second, tiny kernel merges the partials of each (b, h)
-//    and writes bf16. The kernel boundary orders the two; no device-scope
-//    fences or counters are needed (on this chip a device-scope release or
-//    acquire writes back or invalidates the whole L2, which costs far more
-//    than a second launch).
+//    workspace. If all splits of a (b, h) run on one XCD, they share that
+//    XCD's L2, and the split kernel merges them itself: each workgroup stores
+//    its partial, then a flag holding the call's tag, waits for both stores,
+//    and reads all flags of its (b, h) past L1; whichever sees every flag set
+//    merges (the last to finish always does; two that finish together both
+//    write the same bytes). No atomics or device-scope fences are needed: on
+//    this chip a device-scope release or acquire writes back or invalidates
+//    the whole L2. For other shapes a second, tiny kernel merges the
+//    partials, ordered by the kernel boundary.
 //  * Workgroups of one sequence are placed on one XCD so the shared k_pe rows
 //    are served from that XCD's L2 for all heads.
 #include <hip/hip_runtime.h>
@@ -234,13 +238,82 @@ __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
     return;
   }
 
-  // ---- split-KV: publish this workgroup's partial for the combine kernel
-  if (wave == 0 && qq == 0) {
-    const int64_t slot = (int64_t)bh * a.nsplit + split;
+  // ---- split-KV: publish this workgroup's partial
+  if (wave != 0) return;
+  const int64_t slot = (int64_t)bh * a.nsplit + split;
+  if (qq == 0) {
     float* dst = a.ws_o + slot * DV + 8 * cl;
     *reinterpret_cast<f32x4*>(dst) = f32x4{O[0], O[1], O[2], O[3]};
     *reinterpret_cast<f32x4*>(dst + 4) = f32x4{O[4], O[5], O[6], O[7]};
-    if (cl == 0) *reinterpret_cast<f32x2*>(a.ws_ml + 2 * slot) = f32x2{M, L};
+    if (cl == 0) {
+      const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);
+      *reinterpret_cast<f32x4*>(a.ws_ml + 4 * slot) = f32x4{M, L, __builtin_bit_cast(float, xcc), 0.0f};
+    }
+  }
+  if (!a.fused) return;
+  // Completion without atomics: each workgroup publishes its partial, then a
+  // flag holding this call's tag, waiting for each store to reach the XCD's
+  // L2; then it reads every flag of its (b, h) past L1. Of the workgroups that
+  // finish last, at least one sees all flags (a store that has completed is
+  // seen by every later load); any that do merge the same partials the same
+  // way and write identical bytes.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the partial is in L2
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (lane == 0) a.ws_flag[slot] = a.tag;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the flag is in L2
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const __amdgpu_buffer_rsrc_t rf = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.ws_flag + (int64_t)bh * a.nsplit), (short)0, a.nsplit * 8, 0x00020000);
+  bool done = true;
+  for (int sp = lane; sp < a.nsplit; sp += 64) {
+    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(rf, sp * 8, 0, 1);      // sc0: past L1
+    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(rf, sp * 8 + 4, 0, 1);
+    done = done && (((unsigned long long)hi << 32 | lo) == a.tag);
+  }
+  if (__any(!done)) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const uint32_t my_xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.ws_o + (int64_t)bh * a.nsplit * DV), (short)0, a.nsplit * DV * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.ws_ml + (int64_t)bh * a.nsplit * 4), (short)0, a.nsplit * 16, 0x00020000);
+  float mm = -INFINITY, ll = 0.0f, oo[8];
+  bool same_xcd = true;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) oo[e] = 0.0f;
+  for (int sp = qq; sp < a.nsplit; sp += 4) {
+    const u32x4 mlw = __builtin_amdgcn_raw_buffer_load_b128(rm, sp * 16, 0, 1);
+    const u32x4 w0 = __builtin_amdgcn_raw_buffer_load_b128(ro, (sp * DV + 8 * cl) * 4, 0, 1);
+    const u32x4 w1 = __builtin_amdgcn_raw_buffer_load_b128(ro, (sp * DV + 8 * cl + 4) * 4, 0, 1);
+    const uint32_t m_bits = mlw[0], l_bits = mlw[1], x_bits = mlw[2];
+    same_xcd = same_xcd && (x_bits == my_xcc);
+    const float m_sp = __builtin_bit_cast(float, m_bits), l_sp = __builtin_bit_cast(float, l_bits);
+    const float Mn = fmaxf(mm, m_sp);
+    const float a1 = rescale(mm, Mn), a2 = rescale(m_sp, Mn);
+    ll = ll * a1 + l_sp * a2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t b0 = w0[e], b1 = w1[e];
+      oo[e] = oo[e] * a1 + __builtin_bit_cast(float, b0) * a2;
+      oo[4 + e] = oo[4 + e] * a1 + __builtin_bit_cast(float, b1) * a2;
+    }
+    mm = Mn;
+  }
+  merge_xor(mm, ll, oo, 16);
+  merge_xor(mm, ll, oo, 32);
+  same_xcd = !__any(!same_xcd);
+  if (qq == 0) {
+    // A partial written on another XCD may not be visible here: poison the
+    // output rather than return a silently wrong row.
+    const float inv = same_xcd ? 1.0f / ll : __builtin_nanf("");
+    uint16_t* dst = a.out + (int64_t)bh * DV + 8 * cl;
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)to_bf16_rne(oo[2 * e] * inv) | ((uint32_t)to_bf16_rne(oo[2 * e + 1] * inv) << 16);
+    *reinterpret_cast<u32x4*>(dst) = w;
   }
 }
 
@@ -255,7 +328,7 @@ __global__ __launch_bounds__(64) void mla_decode_combine_kernel(DecodeArgs a) {
   for (int e = 0; e < 8; ++e) oo[e] = 0.0f;
   for (int sp = qq; sp < a.nsplit; sp += 4) {
     const int64_t sl = (int64_t)bh * a.nsplit + sp;
-    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.ws_ml + 2 * sl);
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.ws_ml + 4 * sl);
     const float Mn = fmaxf(mm, ml[0]);
     const float a1 = rescale(mm, Mn), a2 = rescale(ml[0], Mn);
     const f32x4 p0 = *reinterpret_cast<const f32x4*>(a.ws_o + sl * DV + 8 * cl);
@@ -286,7 +359,7 @@ __global__ __launch_bounds__(64) void mla_decode_combine_kernel(DecodeArgs a) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const int grid = a.B * a.H * a.nsplit;
   hipLaunchKernelGGL(mla_decode_kernel, dim3(grid), dim3(NT), 0, stream, a);
-  if (a.nsplit > 1)
+  if (a.nsplit > 1 && !a.fused)
     hipLaunchKernelGGL(mla_decode_combine_kernel, dim3(a.B * a.H), dim3(64), 0, stream, a);
   return hipGetLastError();
 }

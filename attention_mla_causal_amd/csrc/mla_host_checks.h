@@ -29,7 +29,8 @@ struct DecodePlan {
   int64_t nsplit = 1;          // workgroups per (b, h)
   int64_t keys_per_split = 0;  // multiple of kDecodeKeysPerTrip
   size_t ws_o_bytes = 0;       // fp32 [B*H, nsplit, 128]
-  size_t ws_ml_bytes = 0;      // fp32 pairs (max, sum) [B*H, nsplit]
+  size_t ws_ml_bytes = 0;      // fp32 (max, sum, XCD id, unused) [B*H, nsplit]
+  size_t ws_flag_bytes = 0;     // u64 completion flags [B*H, nsplit]
   size_t workspace_bytes = 0;  // total, each region 256-byte aligned
 };
 
@@ -55,8 +56,9 @@ inline DecodePlan plan_decode(int64_t B, int64_t H, int64_t S) {
   p.keys_per_split = kps;
   if (nsplit > 1) {
     p.ws_o_bytes = align256(size_t(bh) * size_t(nsplit) * 128 * sizeof(float));
-    p.ws_ml_bytes = align256(size_t(bh) * size_t(nsplit) * 2 * sizeof(float));
-    p.workspace_bytes = p.ws_o_bytes + p.ws_ml_bytes;
+    p.ws_ml_bytes = align256(size_t(bh) * size_t(nsplit) * 4 * sizeof(float));
+    p.ws_flag_bytes = align256(size_t(bh) * size_t(nsplit) * sizeof(unsigned long long));
+    p.workspace_bytes = p.ws_o_bytes + p.ws_ml_bytes + p.ws_flag_bytes;
   }
   return p;
 }

@@ -27,9 +27,12 @@ struct DecodeArgs {
   const uint16_t* v;       // [B,H,S,128]
   uint16_t* out;           // [B,H,1,128]
   float* ws_o;             // [B*H, nsplit, 128] partial outputs (nsplit > 1)
-  float* ws_ml;            // [B*H, nsplit, 2] partial (max, sum)
+  float* ws_ml;            // [B*H, nsplit, 4] partial (max, sum, XCD id, unused)
+  unsigned long long* ws_flag;  // [B*H, nsplit] completion flags (this call's tag)
+  unsigned long long tag;  // this call's tag
   int32_t B, H, S;
   int32_t nsplit, keys_per_split;
+  int32_t fused;           // the last workgroup of each (b, h) merges the partials
   float scale_log2;
 };
 

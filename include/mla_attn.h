@@ -89,7 +89,9 @@ size_t mla_attn_decode_workspace_bytes(int32_t B, int32_t H, int32_t S);
  *
  * When B*H is too small to fill the GPU, the key range of each (b, h) is
  * split across workgroups whose fp32 partial results (o, max, sum) are merged
- * by a log-sum-exp combine kernel enqueued right after on the same stream.
+ * by log-sum-exp: inside the same kernel when all splits of a (b, h) land on
+ * one XCD (the last workgroup to finish merges), otherwise by a combine kernel
+ * enqueued right after on the same stream.
  * workspace: caller-owned device scratch of at least
  * mla_attn_decode_workspace_bytes(B, H, S) bytes (may be NULL when that is 0),
  * 16-byte aligned. Its contents on entry do not matter and are overwritten.

@@ -61,8 +61,10 @@ int main() {
   {
     DecodePlan pl = plan_decode(1, 64, 1001);
     EXPECT(pl.nsplit == 8 && pl.keys_per_split == 128);
-    EXPECT(pl.workspace_bytes == pl.ws_o_bytes + pl.ws_ml_bytes);
+    EXPECT(pl.workspace_bytes == pl.ws_o_bytes + pl.ws_ml_bytes + pl.ws_flag_bytes);
     EXPECT(pl.ws_o_bytes == size_t(64) * 8 * 128 * 4);
+    EXPECT(pl.ws_ml_bytes == size_t(64) * 8 * 4 * 4);    // (max, sum, XCD id, unused) per split
+    EXPECT(pl.ws_flag_bytes == size_t(64) * 8 * 8);      // one 64-bit completion flag per split
     EXPECT(pl.workspace_bytes % 256 == 0);
     pl = plan_decode(32, 64, 8192);
     EXPECT(pl.nsplit == 1 && pl.workspace_bytes == 0 && pl.keys_per_split >= 8192);

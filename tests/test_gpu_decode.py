@@ -99,6 +99,33 @@ def test_workspace_contents_do_not_matter():
         ws.fill_(0xFF)
 
 
+def test_back_to_back_calls_share_one_workspace():
+    """Calls queued back to back on one stream reuse one workspace without
+    clearing it. At this shape every split of a head runs on one XCD and the
+    split kernel merges the partials itself; each call's completion flags carry
+    a fresh tag, so no call may merge a partial or flag left by the previous one."""
+    import torch
+    B, H, P = 1, 64, 1000
+    need = _lib().mla_attn_decode_workspace_bytes(B, H, P + 1)
+    log(f"case back-to-back decode calls need={need}")
+    xa = random_inputs(B, H, 1, P, seed=101)
+    xb = random_inputs(B, H, 1, P, seed=202)
+    da, db = upload(xa), upload(xb)
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device="cuda")
+    outs = []
+    for d in (da, db, da, db, da):
+        out = torch.empty((B, H, 1, 128), dtype=torch.bfloat16, device="cuda")
+        _lib().mla_attn_decode(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], P, ALPHA,
+                               out=out, workspace=ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    bits = [to_host_bits(o) for o in outs]
+    assert_parity(to_host_f64(outs[0]), _oracle(xa, P), "first call")
+    assert_parity(to_host_f64(outs[1]), _oracle(xb, P), "second call")
+    assert np.array_equal(bits[0], bits[2]) and np.array_equal(bits[0], bits[4])
+    assert np.array_equal(bits[1], bits[3])
+
+
 def test_decode_future_independence_and_determinism():
     B, H, P = 1, 4, 1234
     log("case decode determinism")
