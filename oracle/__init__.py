@@ -16,3 +16,10 @@ from .mla_oracle import (  # noqa: F401
     mla_attention,
     mla_attention_rows,
 )
+from .mla_latent import (  # noqa: F401
+    KV_LORA_RANK,
+    KV_B_PER_HEAD,
+    decompress_kv,
+    mla_decode_latent,
+    mla_decode_latent_rows,
+)

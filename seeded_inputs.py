@@ -16,6 +16,14 @@ Host recipe (all small and medium workloads):
   with round-to-nearest-even on the fp32 bits; kept as uint16 bit patterns.
   Per-batch streams let a test regenerate a single batch of a large workload.
 
+Latent-cache decode workloads (the compressed cache that kv_b_proj expands)
+draw q_nope, q_pe, c_kv (the normalised 512-dim latent), k_pe and w_kv_b
+(kv_b_proj's weight [64*256, 512]) the same way, in that order, with
+std 1 for the activations and 1/sqrt(512) for the weight, so that the
+decompressed keys and values have unit variance like the other workloads.
+The weight has no batch index: its stream is the tensor child's first
+grandchild.
+
 Device recipe (workloads whose inputs exceed a few GiB of host work, i.e. the
 batched decode): torch.Generator on the device seeded with `seed`, then for
 each tensor in the same order torch.randn(float32) * std rounded to bf16 by
@@ -73,6 +81,46 @@ WORKLOADS = {
 }
 
 
+KV_RANK = 512
+LATENT_TENSORS = ("q_nope", "q_pe", "c_kv", "k_pe", "w_kv_b")
+
+
+@dataclass(frozen=True)
+class LatentWorkload:
+    """Decode over the compressed cache: one query per sequence, S = past_len + 1."""
+    name: str
+    B: int
+    H: int
+    past_len: int
+    softmax_scale: float = float(np.float32(192.0 ** -0.5))
+
+    @property
+    def S(self) -> int:
+        return self.past_len + 1
+
+    def shapes(self) -> dict:
+        B, H, S = self.B, self.H, self.S
+        return {
+            "q_nope": (B, H, 1, NOPE),
+            "q_pe": (B, H, 1, ROPE),
+            "c_kv": (B, S, KV_RANK),
+            "k_pe": (B, 1, S, ROPE),
+            "w_kv_b": (1, H * (NOPE + VDIM), KV_RANK),  # leading 1: no batch index
+        }
+
+    @staticmethod
+    def std(tensor: str) -> float:
+        return float(1.0 / np.sqrt(KV_RANK)) if tensor == "w_kv_b" else 1.0
+
+
+# The pages' decode (64 heads, p = 1000) and the batched decode, with the
+# cache kept compressed.
+LATENT_WORKLOADS = {
+    "latent_decode_p1000": LatentWorkload("latent_decode_p1000", B=1, H=64, past_len=1000),
+    "latent_batched_decode": LatentWorkload("latent_batched_decode", B=32, H=64, past_len=8191),
+}
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 values to bf16 (round to nearest, ties to even); uint16 bits."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
@@ -82,8 +130,8 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return r.astype(np.uint16)
 
 
-def _batch_rng(seed: int, tensor: str, B: int, b: int) -> np.random.Generator:
-    child = np.random.SeedSequence(seed).spawn(len(TENSORS))[TENSORS.index(tensor)]
+def _batch_rng(seed: int, tensor: str, B: int, b: int, names=TENSORS) -> np.random.Generator:
+    child = np.random.SeedSequence(seed).spawn(len(names))[names.index(tensor)]
     grand = child.spawn(B)[b]
     return np.random.Generator(np.random.PCG64(grand))
 
@@ -106,6 +154,43 @@ def host_inputs(wl: Workload, seed: int = 0, std: float | None = None) -> dict:
         for b in range(shape[0]):
             arr[b] = tensor_batch(shape, name, b, seed, std)
         out[name] = arr
+    return out
+
+
+def latent_host_inputs(wl: LatentWorkload, seed: int = 0) -> dict:
+    """The five latent-decode inputs as uint16 bf16 bit arrays (host recipe)."""
+    out = {}
+    for name, shape in wl.shapes().items():
+        arr = np.empty(shape, dtype=np.uint16)
+        for b in range(shape[0]):
+            g = _batch_rng(seed, name, shape[0], b, LATENT_TENSORS)
+            x = g.standard_normal(shape[1:], dtype=np.float32)
+            x *= np.float32(wl.std(name))
+            arr[b] = f32_to_bf16_bits(x)
+        out[name] = arr[0] if name == "w_kv_b" else arr
+    return out
+
+
+def latent_random_inputs(B, H, past_len, seed=0) -> dict:
+    """Host-recipe latent-decode inputs for an arbitrary shape."""
+    return latent_host_inputs(LatentWorkload("custom", B, H, past_len), seed)
+
+
+def latent_device_inputs(wl: LatentWorkload, device, seed: int = 0) -> dict:
+    """The five latent-decode inputs drawn on a torch device (device recipe)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = {}
+    for name, shape in wl.shapes().items():
+        t = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        for b in range(shape[0]):
+            x = torch.randn(shape[1:], generator=g, dtype=torch.float32, device=device)
+            x.mul_(wl.std(name))
+            t[b].copy_(x)
+            del x
+        out[name] = t[0] if name == "w_kv_b" else t
     return out
 
 
