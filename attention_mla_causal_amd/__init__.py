@@ -4,7 +4,7 @@ A thin ctypes binding over libmla_attn.so (the C ABI in include/mla_attn.h).
 The functions below only check and marshal arguments: torch supplies device
 memory and the current HIP stream; every step of the attention runs in the
 library's HIP kernels. There is no fallback path: if the library has not been
-built (``python -m attention_mla_causal_amd.build``) importing this package
+built (``python attention_mla_causal_amd/build.py``) importing this package
 raises.
 """
 
@@ -37,6 +37,8 @@ SIGNATURES = {
     "mla_attn_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "mla_attn_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _F32, _VP]),
+    "mla_attn_decode_latent_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "mla_attn_decode_latent": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_last_error": (ctypes.c_char_p, []),
 }
@@ -54,7 +56,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(
             f"{path} is missing: build the HIP library first "
-            "(python -m attention_mla_causal_amd.build); there is no non-GPU fallback")
+            "(python attention_mla_causal_amd/build.py); there is no non-GPU fallback")
     try:
         import torch  # noqa: F401  (load torch's HIP runtime first so the library binds to it)
     except ImportError:
@@ -184,7 +186,64 @@ def mla_attn_decode(q_nope, q_pe, k_nope, k_pe, v, past_len: int, softmax_scale:
     return out
 
 
+KV_LORA_RANK = 512
+
+
+def mla_attn_decode_latent_workspace_bytes(B: int, H: int, S: int) -> int:
+    """Bytes of device scratch mla_attn_decode_latent needs for (B, H, S)."""
+    return int(_lib.mla_attn_decode_latent_workspace_bytes(int(B), int(H), int(S)))
+
+
+def mla_attn_decode_latent(q_nope, q_pe, c_kv, k_pe, w_kv_b, past_len: int, softmax_scale: float,
+                           out=None, workspace=None):
+    """Decode over the compressed cache: one query per sequence against S = past_len + 1 keys.
+
+    q_nope [B,H,1,128], q_pe [B,H,1,64], c_kv [B,S,512] (normalised latent),
+    k_pe [B,1,S,64] (shared rotary key), w_kv_b [H*256,512] (kv_b_proj.weight);
+    bf16, contiguous, one GPU. Returns out [B,H,1,128] bf16 on the current stream.
+    """
+    import torch
+
+    for t, n in ((q_nope, "q_nope"), (q_pe, "q_pe"), (k_pe, "k_pe")):
+        _check_tensor(t, n)
+    for t, n, nd in ((c_kv, "c_kv", 3), (w_kv_b, "w_kv_b", 2)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda \
+                or not t.is_contiguous() or t.dim() != nd:
+            raise ValueError(f"{n} must be a contiguous {nd}D bfloat16 GPU tensor")
+    B, H, T, _ = q_nope.shape
+    S = c_kv.shape[1]
+    want = {"q_nope": (B, H, 1, QK_NOPE_HEAD_DIM), "q_pe": (B, H, 1, QK_ROPE_HEAD_DIM),
+            "c_kv": (B, S, KV_LORA_RANK), "k_pe": (B, 1, S, QK_ROPE_HEAD_DIM),
+            "w_kv_b": (H * (QK_NOPE_HEAD_DIM + V_HEAD_DIM), KV_LORA_RANK)}
+    for t, n in ((q_nope, "q_nope"), (q_pe, "q_pe"), (c_kv, "c_kv"), (k_pe, "k_pe"), (w_kv_b, "w_kv_b")):
+        if tuple(t.shape) != want[n]:
+            raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {want[n]}")
+    devs = {t.device for t in (q_nope, q_pe, c_kv, k_pe, w_kv_b)}
+    if len(devs) != 1:
+        raise ValueError(f"inputs are on different devices: {devs}")
+    if out is None:
+        out = torch.empty((B, H, 1, V_HEAD_DIM), dtype=torch.bfloat16, device=q_nope.device)
+    else:
+        _check_tensor(out, "out")
+        if tuple(out.shape) != (B, H, 1, V_HEAD_DIM) or out.device != q_nope.device:
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, 1, V_HEAD_DIM)}")
+    need = mla_attn_decode_latent_workspace_bytes(B, H, S)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_nope.device)
+    if not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.mla_attn_decode_latent(
+        q_nope.data_ptr(), q_pe.data_ptr(), c_kv.data_ptr(), k_pe.data_ptr(), w_kv_b.data_ptr(),
+        out.data_ptr(), workspace.data_ptr(), ws_bytes, B, H, S, int(past_len),
+        float(softmax_scale), _stream_handle(q_nope.device))
+    _raise_for(st, "mla_attn_decode_latent")
+    return out
+
+
 __all__ = [
+    "mla_attn_decode_latent",
+    "mla_attn_decode_latent_workspace_bytes",
     "mla_attn_prefill",
     "mla_attn_decode",
     "mla_attn_decode_workspace_bytes",

@@ -1,6 +1,6 @@
 """Build libmla_attn.so in-tree with hipcc for gfx950.
 
-    python -m attention_mla_causal_amd.build
+    python attention_mla_causal_amd/build.py
 
 Compiles every HIP source under csrc/ into one shared library next to this
 file. Always recompiles (it is the "does it build" step); loading the
@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libmla_attn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["mla_attn_abi.hip", "mla_prefill.hip", "mla_decode.hip"]
+SOURCES = ["mla_attn_abi.hip", "mla_prefill.hip", "mla_decode.hip", "mla_latent.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",

@@ -119,6 +119,43 @@ mla_status mla_attn_decode(const void* q_nope, const void* q_pe, const void* k_n
   return MLA_OK;
 }
 
+size_t mla_attn_decode_latent_workspace_bytes(int32_t B, int32_t H, int32_t S) {
+  return mla::plan_latent(B, H, S).workspace_bytes;
+}
+
+mla_status mla_attn_decode_latent(const void* q_nope, const void* q_pe, const void* c_kv,
+                                  const void* k_pe, const void* w_kv_b, void* out,
+                                  void* workspace, size_t workspace_bytes, int32_t B, int32_t H,
+                                  int32_t S, int32_t past_len, float softmax_scale, void* stream) {
+  mla::LatentPlan plan;
+  const mla::CheckResult r =
+      mla::check_latent_decode(q_nope, q_pe, c_kv, k_pe, w_kv_b, out, workspace, workspace_bytes,
+                               B, H, S, past_len, softmax_scale, &plan);
+  if (r.status != MLA_OK) return report("mla_attn_decode_latent", r);
+  if (r.empty) return MLA_OK;
+  mla::LatentArgs a;
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.c_kv = static_cast<const uint16_t*>(c_kv);
+  a.k_pe = static_cast<const uint16_t*>(k_pe);
+  a.w_kv_b = static_cast<const uint16_t*>(w_kv_b);
+  a.out = static_cast<uint16_t*>(out);
+  char* ws = static_cast<char*>(workspace);
+  a.qt = reinterpret_cast<uint16_t*>(ws);
+  a.po = reinterpret_cast<float*>(ws + plan.qt_bytes);
+  a.pml = reinterpret_cast<float*>(ws + plan.qt_bytes + plan.po_bytes);
+  a.olat = reinterpret_cast<float*>(ws + plan.qt_bytes + plan.po_bytes + plan.pml_bytes);
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.nsplit = (int32_t)plan.nsplit;
+  a.keys_per_split = (int32_t)plan.keys_per_split;
+  a.scale_log2 = softmax_scale * kLog2e;
+  const hipError_t e = mla::launch_latent_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error("mla_attn_decode_latent", e);
+  return MLA_OK;
+}
+
 const char* mla_status_string(mla_status s) {
   switch (s) {
     case MLA_OK: return "MLA_OK";

@@ -81,7 +81,8 @@ inline bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) &
 // Common part of both entry points. T is the number of new queries.
 inline CheckResult check_common(const void* q_nope, const void* q_pe, const void* k_nope,
                                 const void* k_pe, const void* v, const void* out, int64_t B,
-                                int64_t H, int64_t T, int64_t S, int64_t past_len, float scale) {
+                                int64_t H, int64_t T, int64_t S, int64_t past_len, float scale,
+                                const char* const* tensor_names = nullptr) {
   CheckResult r;
   if (B < 0 || H < 0 || T < 0 || S < 0 || past_len < 0) {
     std::snprintf(r.msg, sizeof(r.msg),
@@ -103,7 +104,8 @@ inline CheckResult check_common(const void* q_nope, const void* q_pe, const void
   }
   // every tensor is non-empty from here on (S >= T >= 1)
   const void* ptrs[6] = {q_nope, q_pe, k_nope, k_pe, v, out};
-  const char* names[6] = {"q_nope", "q_pe", "k_nope", "k_pe", "v", "out"};
+  static const char* const default_names[6] = {"q_nope", "q_pe", "k_nope", "k_pe", "v", "out"};
+  const char* const* names = tensor_names ? tensor_names : default_names;
   for (int i = 0; i < 6; ++i) {
     if (ptrs[i] == nullptr) {
       std::snprintf(r.msg, sizeof(r.msg), "%s is NULL", names[i]);
@@ -170,6 +172,82 @@ inline CheckResult check_decode(const void* q_nope, const void* q_pe, const void
       r.status = MLA_ERR_ALIGN;
       return r;
     }
+  }
+  if (plan_out) *plan_out = plan;
+  return r;
+}
+
+// ---- decode over the compressed latent cache
+constexpr int64_t kLatentRank = 512;             // kv_lora_rank
+constexpr int64_t kLatentKeyWidth = 512 + 64;    // latent + shared rotary key, per key
+constexpr int64_t kLatentKeysPerTile = 32;
+constexpr int64_t kLatentTargetWorkgroups = 256; // one per CU
+
+struct LatentPlan {
+  int64_t nsplit = 1;          // workgroups per sequence
+  int64_t keys_per_split = 0;  // multiple of kLatentKeysPerTile
+  size_t qt_bytes = 0;         // bf16 [B, H, 576]: absorbed queries joined with q_pe
+  size_t po_bytes = 0;         // fp32 [B, nsplit, H, 512]: partial latent outputs
+  size_t pml_bytes = 0;        // fp32 [B, nsplit, H, 2]: partial (max, sum)
+  size_t olat_bytes = 0;       // fp32 [B, H, 512]: merged latent outputs
+  size_t workspace_bytes = 0;  // total, each region 256-byte aligned
+};
+
+// Split each sequence's keys so about one workgroup per CU runs.
+inline LatentPlan plan_latent(int64_t B, int64_t H, int64_t S) {
+  LatentPlan p;
+  if (B <= 0 || H <= 0 || S <= 0) return p;
+  const int64_t tiles = (S + kLatentKeysPerTile - 1) / kLatentKeysPerTile;
+  int64_t nsplit = (kLatentTargetWorkgroups + B - 1) / B;
+  if (nsplit > tiles) nsplit = tiles;
+  if (nsplit < 1) nsplit = 1;
+  int64_t kps = (S + nsplit - 1) / nsplit;
+  kps = (kps + kLatentKeysPerTile - 1) / kLatentKeysPerTile * kLatentKeysPerTile;
+  nsplit = (S + kps - 1) / kps;
+  p.nsplit = nsplit;
+  p.keys_per_split = kps;
+  p.qt_bytes = align256(size_t(B) * size_t(H) * size_t(kLatentKeyWidth) * 2);
+  p.po_bytes = align256(size_t(B) * size_t(nsplit) * size_t(H) * size_t(kLatentRank) * 4);
+  p.pml_bytes = align256(size_t(B) * size_t(nsplit) * size_t(H) * 2 * 4);
+  p.olat_bytes = align256(size_t(B) * size_t(H) * size_t(kLatentRank) * 4);
+  p.workspace_bytes = p.qt_bytes + p.po_bytes + p.pml_bytes + p.olat_bytes;
+  return p;
+}
+
+inline CheckResult check_latent_decode(const void* q_nope, const void* q_pe, const void* c_kv,
+                                       const void* k_pe, const void* w_kv_b, const void* out,
+                                       const void* workspace, size_t workspace_bytes, int64_t B,
+                                       int64_t H, int64_t S, int64_t past_len, float scale,
+                                       LatentPlan* plan_out) {
+  static const char* const names[6] = {"q_nope", "q_pe", "c_kv", "k_pe", "w_kv_b", "out"};
+  CheckResult r =
+      check_common(q_nope, q_pe, c_kv, k_pe, w_kv_b, out, B, H, 1, S, past_len, scale, names);
+  if (r.status != MLA_OK || r.empty) return r;
+  if (H % 16 != 0 || H > 64) {
+    std::snprintf(r.msg, sizeof(r.msg),
+                  "latent decode takes H a multiple of 16 and at most 64 (one wave per 16 heads), "
+                  "got H=%lld",
+                  (long long)H);
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  const LatentPlan plan = plan_latent(B, H, S);
+  if (B > kMaxGrid / plan.nsplit || B * H > kMaxGrid) {
+    std::snprintf(r.msg, sizeof(r.msg), "B*nsplit exceeds the grid limit");
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) {
+    std::snprintf(r.msg, sizeof(r.msg), "workspace %s: %zu bytes given, %zu needed",
+                  workspace == nullptr ? "is NULL" : "too small", workspace_bytes,
+                  plan.workspace_bytes);
+    r.status = MLA_ERR_WORKSPACE;
+    return r;
+  }
+  if (misaligned(workspace)) {
+    std::snprintf(r.msg, sizeof(r.msg), "workspace is not 16-byte aligned");
+    r.status = MLA_ERR_ALIGN;
+    return r;
   }
   if (plan_out) *plan_out = plan;
   return r;

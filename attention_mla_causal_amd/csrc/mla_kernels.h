@@ -36,10 +36,27 @@ struct DecodeArgs {
   float scale_log2;
 };
 
+struct LatentArgs {
+  const uint16_t* q_nope;  // [B,H,1,128]
+  const uint16_t* q_pe;    // [B,H,1,64]
+  const uint16_t* c_kv;    // [B,S,512] normalised latent
+  const uint16_t* k_pe;    // [B,1,S,64] shared rotary key
+  const uint16_t* w_kv_b;  // [H*256, 512] kv_b_proj weight (key rows, then value rows, per head)
+  uint16_t* out;           // [B,H,1,128]
+  uint16_t* qt;            // workspace: [B,H,576] absorbed queries joined with q_pe (bf16)
+  float* po;               // workspace: [B,nsplit,H,512] partial latent outputs
+  float* pml;              // workspace: [B,nsplit,H,2] partial (max, sum)
+  float* olat;             // workspace: [B,H,512] merged latent outputs
+  int32_t B, H, S;
+  int32_t nsplit, keys_per_split;
+  float scale_log2;
+};
+
 // Queries per prefill workgroup.
 int prefill_block_m();
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_latent_decode(const LatentArgs& a, hipStream_t stream);
 
 }  // namespace mla
 

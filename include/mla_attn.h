@@ -105,6 +105,44 @@ mla_status mla_attn_decode(const void* q_nope, const void* q_pe,
                            float softmax_scale, void* stream);
 
 /* Static name of a status code ("MLA_OK", ...); "unknown status" otherwise. */
+/*
+ * Bytes of device workspace mla_attn_decode_latent needs for (B, H, S); a pure
+ * function of its arguments (never 0 for a non-empty call).
+ */
+size_t mla_attn_decode_latent_workspace_bytes(int32_t B, int32_t H, int32_t S);
+
+/*
+ * Decode over the compressed key-value cache. The "Similarities" page's
+ * module ("Scale scores") keeps, per token, a latent of kv_lora_rank = 512
+ * dims (after its RMSNorm) plus the one shared rotary key, and kv_b_proj
+ * (no bias) expands the latent into each head's 128 non-rotary key dims and
+ * 128 value dims. This call returns what mla_attn_decode would return on
+ * those expanded keys and values, without expanding them: kv_b_proj's key
+ * half is folded into the query and its value half is applied to the
+ * attention-weighted latent.
+ *
+ *   q_nope  [B, H, 1, 128]  bf16      q_pe [B, H, 1, 64] bf16 (post-RoPE)
+ *   c_kv    [B, S, 512]     bf16      normalised latent of every key
+ *   k_pe    [B, 1, S, 64]   bf16      shared rotary key (post-RoPE)
+ *   w_kv_b  [H*256, 512]    bf16      kv_b_proj.weight as stored ([out, in]);
+ *                                     rows 256h..256h+127 give head h's key,
+ *                                     rows 256h+128..256h+255 its value
+ *   out     [B, H, 1, 128]  bf16
+ *   S = past_len + 1; H a multiple of 16, at most 64 (else MLA_ERR_SHAPE).
+ *
+ * workspace: caller-owned device scratch of at least
+ * mla_attn_decode_latent_workspace_bytes(B, H, S) bytes, 16-byte aligned;
+ * contents on entry do not matter. Calls that may run at the same time must
+ * not share a workspace. Errors as for mla_attn_decode. Four kernels are
+ * enqueued on `stream` (absorb, attention, merge, up-projection).
+ */
+mla_status mla_attn_decode_latent(const void* q_nope, const void* q_pe,
+                                  const void* c_kv, const void* k_pe,
+                                  const void* w_kv_b, void* out,
+                                  void* workspace, size_t workspace_bytes,
+                                  int32_t B, int32_t H, int32_t S, int32_t past_len,
+                                  float softmax_scale, void* stream);
+
 const char* mla_status_string(mla_status s);
 
 /* Thread-local message for the last failing call on this thread ("" if none). */

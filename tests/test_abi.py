@@ -32,6 +32,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert _declared_functions() == sorted([
         "mla_attn_decode", "mla_attn_decode_workspace_bytes", "mla_attn_prefill",
+        "mla_attn_decode_latent", "mla_attn_decode_latent_workspace_bytes",
         "mla_last_error", "mla_status_string"])
 
 
@@ -99,3 +100,33 @@ def test_binding_has_no_fallback(tmp_path):
     import attention_mla_causal_amd as m
     with pytest.raises(ImportError):
         m.load_library(str(tmp_path / "missing.so"))
+
+
+def _latent(lib, ptrs, ws, ws_bytes, B, H, S, P, scale=SC):
+    return lib.mla_attn_decode_latent(*ptrs, ws, ws_bytes, B, H, S, P, scale, None)
+
+
+def test_latent_decode_errors(lib):
+    need = lib.mla_attn_decode_latent_workspace_bytes(1, 64, 1001)
+    assert need > 0 and need % 256 == 0
+    ok = [ALIGNED] * 6
+    # shapes: S != past_len + 1, negative sizes, H not a multiple of 16 or above 64
+    assert _latent(lib, ok, ALIGNED, need, 1, 64, 1001, 999) == 2
+    assert _latent(lib, ok, ALIGNED, need, -1, 64, 1001, 1000) == 2
+    for H in (8, 24, 80):
+        ws = lib.mla_attn_decode_latent_workspace_bytes(1, H, 11)
+        assert _latent(lib, ok, ALIGNED, ws, 1, H, 11, 10) == 2
+    assert "multiple of 16" in lib.mla_last_error().decode()
+    for i in range(6):
+        ptrs = list(ok)
+        ptrs[i] = None
+        assert _latent(lib, ptrs, ALIGNED, need, 1, 64, 1001, 1000) == 1
+        ptrs[i] = MISALIGNED
+        assert _latent(lib, ptrs, ALIGNED, need, 1, 64, 1001, 1000) == 3
+    assert _latent(lib, ok, None, need, 1, 64, 1001, 1000) == 5
+    assert _latent(lib, ok, ALIGNED, need - 1, 1, 64, 1001, 1000) == 5
+    assert _latent(lib, ok, MISALIGNED, need, 1, 64, 1001, 1000) == 3
+    assert _latent(lib, ok, ALIGNED, need, 1, 64, 1001, 1000, float("nan")) == 4
+    assert "mla_attn_decode_latent" in lib.mla_last_error().decode()
+    assert _latent(lib, [None] * 6, None, 0, 0, 64, 1001, 1000) == 0   # empty batch
+

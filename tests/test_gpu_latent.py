@@ -1,0 +1,102 @@
+"""GPU parity of mla_attn_decode_latent (decode over the compressed cache)
+against the fp64 oracle that decompresses keys and values, through the C ABI."""
+
+import numpy as np
+import pytest
+
+from oracle import mla_decode_latent, mla_decode_latent_rows
+from seeded_inputs import LATENT_WORKLOADS, latent_device_inputs, latent_host_inputs, latent_random_inputs
+
+from _gpu_util import assert_parity, log, to_host_bits, to_host_f64, upload
+
+pytestmark = pytest.mark.gpu
+
+ALPHA = LATENT_WORKLOADS["latent_decode_p1000"].softmax_scale
+
+
+def _lib():
+    import attention_mla_causal_amd as m
+    return m
+
+
+def _gpu(d, P, out=None, workspace=None):
+    import torch
+    o = _lib().mla_attn_decode_latent(d["q_nope"], d["q_pe"], d["c_kv"], d["k_pe"], d["w_kv_b"], P,
+                                      ALPHA, out=out, workspace=workspace)
+    torch.cuda.synchronize()
+    return o
+
+
+def _oracle(x, P):
+    return mla_decode_latent(x["q_nope"], x["q_pe"], x["c_kv"], x["k_pe"], x["w_kv_b"], P, ALPHA)
+
+
+def test_latent_decode_as_on_the_pages():
+    wl = LATENT_WORKLOADS["latent_decode_p1000"]
+    log(f"case latent_decode_p1000 B={wl.B} H={wl.H} S={wl.S}")
+    x = latent_host_inputs(wl, seed=0)
+    out = _gpu(upload(x), wl.past_len)
+    assert_parity(to_host_f64(out), _oracle(x, wl.past_len), "latent decode p1000")
+
+
+# (B, H, past_len): one key; one key short of a tile, a full tile, one past it;
+# each wave count (16..64 heads); several key splits with a ragged last tile.
+EDGE = [(1, 16, 0), (1, 64, 30), (2, 32, 31), (1, 48, 32), (3, 64, 777), (2, 16, 4095), (4, 64, 2000)]
+
+
+@pytest.mark.parametrize("B,H,P", EDGE)
+def test_latent_decode_edge_shapes(B, H, P):
+    need = _lib().mla_attn_decode_latent_workspace_bytes(B, H, P + 1)
+    log(f"case latent edge B={B} H={H} P={P} ws={need}")
+    x = latent_random_inputs(B, H, P, seed=B * 11 + H + P)
+    out = _gpu(upload(x), P)
+    assert_parity(to_host_f64(out), _oracle(x, P), f"latent {B},{H},{P}")
+
+
+def test_latent_workspace_garbage_and_determinism():
+    import torch
+    B, H, P = 2, 64, 1500
+    x = latent_random_inputs(B, H, P, seed=9)
+    d = upload(x)
+    need = _lib().mla_attn_decode_latent_workspace_bytes(B, H, P + 1)
+    log(f"case latent workspace garbage need={need}")
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    first = None
+    for it in range(3):
+        out = torch.full((B, H, 1, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+        _gpu(d, P, out=out, workspace=ws)
+        bits = to_host_bits(out)
+        if first is None:
+            first = bits
+            assert_parity(to_host_f64(out), _oracle(x, P), "latent workspace first call")
+        assert np.array_equal(bits, first), f"call {it} differs"
+        ws.fill_(0xA5)
+
+
+def test_latent_batched_decode_full_size_sampled():
+    """B=32, H=64, S=8192 with inputs drawn on the device; sampled (b, h) rows
+    against the oracle (which decompresses one head at a time)."""
+    import torch
+    wl = LATENT_WORKLOADS["latent_batched_decode"]
+    log(f"case latent_batched_decode B={wl.B} H={wl.H} S={wl.S}")
+    d = latent_device_inputs(wl, "cuda", seed=0)
+    out = _gpu(d, wl.past_len)
+    assert torch.isfinite(out).all().item()
+    rng = np.random.default_rng(1)
+    picks = {(0, 0), (wl.B - 1, wl.H - 1)}
+    while len(picks) < 10:
+        picks.add((int(rng.integers(wl.B)), int(rng.integers(wl.H))))
+    picks = sorted(picks)
+    w = to_host_bits(d["w_kv_b"])
+    got, ref = [], []
+    for b, h in picks:
+        xs = {"q_nope": to_host_bits(d["q_nope"][b:b + 1, h:h + 1]),
+              "q_pe": to_host_bits(d["q_pe"][b:b + 1, h:h + 1]),
+              "c_kv": to_host_bits(d["c_kv"][b:b + 1]),
+              "k_pe": to_host_bits(d["k_pe"][b:b + 1])}
+        wh = np.zeros((256, 512), dtype=np.uint16)
+        wh[:] = w[256 * h:256 * h + 256]
+        ref.append(mla_decode_latent_rows(xs["q_nope"], xs["q_pe"], xs["c_kv"], xs["k_pe"], wh,
+                                          wl.past_len, ALPHA, [(0, 0)])[0])
+        got.append(to_host_f64(out[b, h, 0]))
+    assert_parity(np.stack(got), np.stack(ref), "latent batched decode sampled")
