@@ -15,19 +15,20 @@
 // A key costs 1152 bytes (latent + rotary key) instead of 64 heads x 512.
 //
 // Four kernels on the caller's stream:
-//  1. absorb: q~ for every (batch, head), rounded to bf16, joined with q_pe
-//     into a 576-dim row (workspace).
+//  1. absorb: q~ for every (batch, head) on MFMA (W_k read transposed out of
+//     LDS), rounded to bf16, joined with q_pe into a 576-dim row (workspace).
 //  2. attention: one workgroup per (batch, key split) with one wave per 16
 //     heads. 32-key tiles of [latent | k_pe] (36 KiB) are copied straight from
-//     HBM into LDS (buffer_load ... lds, double-buffered), in 64-byte column
-//     blocks with row-swizzled 16-byte chunks. Scores use
+//     HBM into LDS (buffer_load ... lds; four buffers, three tiles ahead), in
+//     64-byte column blocks with row-swizzled 16-byte chunks. Scores use
 //     v_mfma_f32_16x16x32_bf16 with keys as rows and the wave's 16 heads as
 //     columns (S^T = K Q~^T, 18 K-steps); online softmax in fp32 per head; the
 //     latent output uses O~^T = C^T P^T, 32 tiles of 16 latent dims, whose
 //     C^T fragments come from ds_read_b64_tr_b16 in the key order the score
 //     accumulator leaves P in. Each split writes an fp32 partial (o~, max, sum).
 //  3. merge: log-sum-exp over the splits of each (batch, head) -> o~ (fp32).
-//  4. up-projection: out = W_v o~, rounded to bf16.
+//  4. up-projection: out = W_v o~ on MFMA (o~ split into two bf16 halves),
+//     rounded to bf16.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -72,43 +73,91 @@ __device__ __forceinline__ bf16x4 lds_tr_read(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
-
-// Sum over the 16 lanes of a row; every lane gets the total.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                                               0xf, 0xf, false));
-}
-__device__ __forceinline__ float row_sum16(float x) {
-  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
-  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
-  x += dpp<0x141>(x);  // row_half_mirror
-  x += dpp<0x140>(x);  // row_mirror
-  return x;
+// Wait until at most N of this wave's vector-memory operations are in flight
+// (vmcnt is 6 bits: low 4 in [3:0], high 2 in [15:14]; lgkm and exp counts left open).
+template <int N>
+__device__ __forceinline__ void wait_vmem_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // ---- 1. absorb: q~[b,h,e] = sum_d q_nope[b,h,d] * W[256h + d, e]; q~[b,h,512+i] = q_pe[b,h,i]
+// As a product per head, Q~_h^T [512 x B] = W_k[h]^T [512 x 128] . Q_h^T [128 x B],
+// on v_mfma_f32_16x16x32_bf16. Workgroup: one head, 64 latent dims; wave w
+// owns the 16 dims e0 + 16w and runs over the batch 16 rows at a time. W_k is
+// stored with e contiguous, so the workgroup stages its [128 d x 64 e] block
+// in LDS and reads it back transposed (ds_read_b64_tr_b16): lane (g, j) then
+// holds dim e0 + 16w + j at d = 32ks + 4g + 0..3 and 32ks + 16 + 4g + 0..3,
+// the K order its query fragment is loaded in.
+constexpr int ABS_ROW = 144;  // bytes per staged W row: 128 + 16 keeps the 4 rows a read touches apart
 __global__ __launch_bounds__(256) void latent_absorb_kernel(LatentArgs a) {
+  __shared__ __attribute__((aligned(16))) char wt[DN * ABS_ROW];
   const int h = blockIdx.x >> 3, chunk = blockIdx.x & 7;
-  const int e = chunk * 64 + (threadIdx.x & 63);
-  const uint16_t* wk = a.w_kv_b + (int64_t)h * KVB * R + e;  // W[256h + d, e] = wk[d * R]
-  for (int b = threadIdx.x >> 6; b < a.B; b += 4) {
-    const uint16_t* q = a.q_nope + ((int64_t)b * a.H + h) * DN;
-    float acc = 0.0f;
-#pragma unroll 8
-    for (int d = 0; d < DN; ++d) acc = __builtin_fmaf(bf16_to_f32(q[d]), bf16_to_f32(wk[(int64_t)d * R]), acc);
-    uint16_t* dst = a.qt + ((int64_t)b * a.H + h) * KW;
-    dst[e] = f32_to_bf16(acc);
-    if (chunk == 0) dst[R + (threadIdx.x & 63)] = a.q_pe[((int64_t)b * a.H + h) * DR + (threadIdx.x & 63)];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, j = lane & 15;
+  const int e0 = chunk * 64;
+  const uint16_t* wk = a.w_kv_b + (int64_t)h * KVB * R + e0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {  // 128 rows x 8 chunks of 16 bytes
+    const int c = tid + 256 * k, row = c >> 3, col = c & 7;
+    *reinterpret_cast<u32x4*>(wt + row * ABS_ROW + col * 16) =
+        *reinterpret_cast<const u32x4*>(wk + (int64_t)row * R + col * 8);
+  }
+  if (chunk == 0) {  // the rotary query goes through unchanged
+    for (int c = tid; c < a.B * 8; c += 256) {
+      const int64_t bh = (int64_t)(c >> 3) * a.H + h;
+      *reinterpret_cast<u32x4*>(a.qt + bh * KW + R + (c & 7) * 8) =
+          *reinterpret_cast<const u32x4*>(a.q_pe + bh * DR + (c & 7) * 8);
+    }
+  }
+  // query fragments of the first 16 batches load while W lands in LDS
+  auto load_q = [&](int b0, u32x4* qv) {
+    const int b = b0 + j;
+    const uint16_t* q = a.q_nope + ((int64_t)(b < a.B ? b : 0) * a.H + h) * DN + 4 * g;
+#pragma unroll
+    for (int ks = 0; ks < DN / 32; ++ks) {
+      qv[ks] = u32x4{0u, 0u, 0u, 0u};
+      if (b < a.B) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(q + 32 * ks);
+        const uint2 hi = *reinterpret_cast<const uint2*>(q + 32 * ks + 16);
+        qv[ks] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+    }
+  };
+  u32x4 qv[DN / 32];
+  load_q(0, qv);
+  __syncthreads();
+  bf16x8 wf[DN / 32];
+#pragma unroll
+  for (int ks = 0; ks < DN / 32; ++ks) {
+    const char* p = wt + (32 * ks + 4 * g + (j >> 2)) * ABS_ROW + (16 * wave + 4 * (j & 3)) * 2;
+    const bf16x4 lo = lds_tr_read(p);
+    const bf16x4 hi = lds_tr_read(p + 16 * ABS_ROW);
+    wf[ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  for (int b0 = 0; b0 < a.B; b0 += 16) {
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < DN / 32; ++ks) acc = mfma16(wf[ks], __builtin_bit_cast(bf16x8, qv[ks]), acc);
+    if (b0 + 16 < a.B) load_q(b0 + 16, qv);
+    // acc[r] = q~[b][e0 + 16w + 4g + r]
+    const int b = b0 + j;
+    if (b < a.B) {
+      const uint32_t p0 = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+      const uint32_t p1 = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+      *reinterpret_cast<uint2*>(a.qt + ((int64_t)b * a.H + h) * KW + e0 + 16 * wave + 4 * g) =
+          uint2{p0, p1};
+    }
   }
 }
 
-// Buffer resource over rows [kb, S) of one sequence's row-major [S, rowbytes/2]
-// bf16 tensor; rows past the end read as zeros.
+// Buffer resource over rows [kb, end) of one sequence's row-major
+// [S, rowbytes/2] bf16 tensor; rows at or past `end` read as zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* seq, int64_t kb,
-                                                           int64_t S, int rowbytes) {
-  const int64_t left = S - kb;
+                                                           int64_t end, int rowbytes) {
+  // A resource only ever addresses one tile's rows: capping the range at 2^20
+  // rows keeps the byte count inside 32 bits for any sequence length.
+  const int64_t left = end - kb < (int64_t(1) << 20) ? end - kb : (int64_t(1) << 20);
   const int records = left > 0 ? (int)(left * rowbytes) : 0;
   return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)seq + kb * rowbytes), (short)0,
                                            records, 0x00020000);
@@ -117,8 +166,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* seq,
 // ---- 2. attention over the latent keys of one key split
 template <int NWV>  // waves per workgroup: one per 16 heads
 __device__ __forceinline__ void latent_attn(const LatentArgs& a) {
+  // four tile buffers: tile t lives in buf[t % 4] and is copied three steps ahead
   __shared__ __attribute__((aligned(1024))) char tile0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char tile1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char tile2[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char tile3[TILE_BYTES];
   constexpr int NCOPY = COPIES / NWV;
   static_assert(COPIES % NWV == 0, "copies must divide over the waves");
 
@@ -149,8 +201,8 @@ __device__ __forceinline__ void latent_attn(const LatentArgs& a) {
   }
   auto copy_tile = [&](int t, char* dst) {
     const int64_t kb = k0 + (int64_t)t * BN;
-    const __amdgpu_buffer_rsrc_t rc = rows_rsrc(c_seq, kb, S, R * 2);
-    const __amdgpu_buffer_rsrc_t rp = rows_rsrc(kp_seq, kb, S, DR * 2);
+    const __amdgpu_buffer_rsrc_t rc = rows_rsrc(c_seq, kb, k1, R * 2);
+    const __amdgpu_buffer_rsrc_t rp = rows_rsrc(kp_seq, kb, k1, DR * 2);
 #pragma unroll
     for (int u = 0; u < NCOPY; ++u) {
       const int ct = u * NWV + wave;  // uniform
@@ -161,8 +213,6 @@ __device__ __forceinline__ void latent_attn(const LatentArgs& a) {
     }
   };
 
-  copy_tile(0, tile0);
-
   // absorbed queries of the wave's 16 heads (B operand): lane (g, j) holds
   // head h0 + j, dims 32 ks + 8 g .. + 8
   bf16x8 qf[KSTEPS];
@@ -171,6 +221,13 @@ __device__ __forceinline__ void latent_attn(const LatentArgs& a) {
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(q + 32 * ks);
   }
+
+  // Past the split's end a copy still runs but reads nothing (rows past k1 read
+  // as zeros), so every tile costs each wave exactly NCOPY copies and one
+  // vmcnt bound serves every step.
+  copy_tile(0, tile0);
+  copy_tile(1, tile1);
+  copy_tile(2, tile2);
 
   // LDS operand offsets. Score A operand (16 keys x 32 dims): lane (g, j)
   // reads key row kt*16 + j, chunk g of column block ks. Output A operand
@@ -189,10 +246,11 @@ __device__ __forceinline__ void latent_attn(const LatentArgs& a) {
   for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  auto step = [&](int t, const char* cur, char* nxt) {
-    wait_vmem();
-    __syncthreads();  // tile t has landed; every wave is done with the other buffer
-    if (t + 1 < ntiles) copy_tile(t + 1, nxt);
+  constexpr int IN_FLIGHT = (2 * NCOPY < 63) ? 2 * NCOPY : 63;
+  auto step = [&](int t, const char* cur, char* fill) {
+    wait_vmem_keep<IN_FLIGHT>();   // this wave's copies of tile t have landed
+    __builtin_amdgcn_s_barrier();  // ... and every wave's; nobody reads tile t-1 any more
+    copy_tile(t + 3, fill);
     const int64_t kb = k0 + (int64_t)t * BN;
     // scores S^T: keys kb + kt*16 + 4g + r, head h0 + j
     f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -244,12 +302,18 @@ __device__ __forceinline__ void latent_attn(const LatentArgs& a) {
     }
   };
 
+  // unrolled by four so that every buffer role is fixed in each copy of the step
   int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
-    step(t, tile0, tile1);
+  for (; t + 3 < ntiles; t += 4) {
+    step(t, tile0, tile3);
     step(t + 1, tile1, tile0);
+    step(t + 2, tile2, tile1);
+    step(t + 3, tile3, tile2);
   }
-  if (t < ntiles) step(t, tile0, tile1);
+  if (t < ntiles) step(t, tile0, tile3);
+  if (t + 1 < ntiles) step(t + 1, tile1, tile0);
+  if (t + 2 < ntiles) step(t + 2, tile2, tile1);
+  wait_vmem_keep<0>();  // (copies past the end are never read; let them land before exit)
 
   // ---- partial of this split: o~ (unnormalised), max and sum per head
   float l_tot = l_run + __shfl_xor(l_run, 16);
@@ -270,20 +334,26 @@ __global__ __launch_bounds__(192, 1) void latent_attn_kernel_w3(LatentArgs a) { 
 __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) { latent_attn<4>(a); }
 
 // ---- 3. merge the splits of each (batch, head): o~ = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
-__global__ __launch_bounds__(64) void latent_merge_kernel(LatentArgs a) {
+// Workgroup: one (batch, head); wave w sums splits w, w + 4, ..., lane l holds
+// dims 8l .. 8l + 7; the four wave sums meet in LDS.
+__global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
+  __shared__ __attribute__((aligned(16))) float part[4][R + 4];
   const int bh = blockIdx.x;
   const int b = bh / a.H, h = bh % a.H;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row0 = (int64_t)b * a.nsplit * a.H + h;  // split s: row0 + s * H
   float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s)
-    M = fmaxf(M, a.pml[2 * (((int64_t)b * a.nsplit + s) * a.H + h)]);
+  for (int s = lane; s < a.nsplit; s += 64) M = fmaxf(M, a.pml[2 * (row0 + (int64_t)s * a.H)]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float L = 0.0f, O[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) O[e] = 0.0f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const int64_t row = ((int64_t)b * a.nsplit + s) * a.H + h;
+#pragma unroll 4
+  for (int s = wave; s < a.nsplit; s += 4) {
+    const int64_t row = row0 + (int64_t)s * a.H;
     const float w = __builtin_amdgcn_exp2f(a.pml[2 * row] - M);
-    L += w * a.pml[2 * row + 1];
+    L = __builtin_fmaf(w, a.pml[2 * row + 1], L);
     const f32x4 p0 = *reinterpret_cast<const f32x4*>(a.po + row * R + 8 * lane);
     const f32x4 p1 = *reinterpret_cast<const f32x4*>(a.po + row * R + 8 * lane + 4);
 #pragma unroll
@@ -292,41 +362,70 @@ __global__ __launch_bounds__(64) void latent_merge_kernel(LatentArgs a) {
       O[4 + e] = __builtin_fmaf(w, p1[e], O[4 + e]);
     }
   }
-  const float inv = 1.0f / L;
-  float* dst = a.olat + (int64_t)bh * R + 8 * lane;
-  *reinterpret_cast<f32x4*>(dst) = f32x4{O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv};
-  *reinterpret_cast<f32x4*>(dst + 4) = f32x4{O[4] * inv, O[5] * inv, O[6] * inv, O[7] * inv};
+  *reinterpret_cast<f32x4*>(&part[wave][8 * lane]) = f32x4{O[0], O[1], O[2], O[3]};
+  *reinterpret_cast<f32x4*>(&part[wave][8 * lane + 4]) = f32x4{O[4], O[5], O[6], O[7]};
+  if (lane == 0) part[wave][R] = L;
+  __syncthreads();
+  const int e = 2 * threadIdx.x;
+  const float inv = 1.0f / (part[0][R] + part[1][R] + part[2][R] + part[3][R]);
+  const float o0 = part[0][e] + part[1][e] + part[2][e] + part[3][e];
+  const float o1 = part[0][e + 1] + part[1][e + 1] + part[2][e + 1] + part[3][e + 1];
+  *reinterpret_cast<float2*>(a.olat + (int64_t)bh * R + e) = float2{o0 * inv, o1 * inv};
 }
 
 // ---- 4. up-projection: out[b,h,d] = sum_e W[256h + 128 + d, e] * o~[b,h,e]
-// Workgroup: one head, 16 output dims; 16 lanes per dim, 32 latent dims each.
-__global__ __launch_bounds__(256) void latent_up_kernel(LatentArgs a) {
-  const int h = blockIdx.x >> 3, chunk = blockIdx.x & 7;
-  const int d = chunk * 16 + (threadIdx.x >> 4);
-  const int part = threadIdx.x & 15;
-  const uint16_t* wrow = a.w_kv_b + ((int64_t)h * KVB + DN + d) * R + part * 32;
-  u32x4 w[4];
+// Per head, Out_h^T [128 x B] = W_v[h] [128 x 512] . O~_h^T [512 x B] on
+// v_mfma_f32_16x16x32_bf16. W_v is stored with e (the contraction) contiguous,
+// so its fragments load straight from HBM. o~ is fp32: it enters as two bf16
+// operands, hi = bf16(x) and lo = bf16(x - hi), whose sum carries x to about
+// 2^-17 relative. Workgroup: one head, 32 output dims; wave w owns 16 of them
+// and runs over the batch 16 rows at a time.
+__global__ __launch_bounds__(128) void latent_up_kernel(LatentArgs a) {
+  const int h = blockIdx.x >> 2, chunk = blockIdx.x & 3;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, j = lane & 15;
+  const int d0 = chunk * 32 + wave * 16;
+  const uint16_t* wrow = a.w_kv_b + ((int64_t)h * KVB + DN + d0 + j) * R + 8 * g;
+  u32x4 wf[R / 32];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = *reinterpret_cast<const u32x4*>(wrow + 8 * i);
-  for (int b = 0; b < a.B; ++b) {
-    const float* ol = a.olat + ((int64_t)b * a.H + h) * R + part * 32;
-    float acc = 0.0f;
+  for (int ks = 0; ks < R / 32; ++ks) wf[ks] = *reinterpret_cast<const u32x4*>(wrow + 32 * ks);
+  for (int b0 = 0; b0 < a.B; b0 += 16) {
+    const int b = b0 + j;
+    const bool live = b < a.B;
+    const float* ol = a.olat + ((int64_t)(live ? b : 0) * a.H + h) * R + 8 * g;
+    f32x4 x[R / 32][2];  // every load of the group in flight at once
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(ol + 8 * i);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(ol + 8 * i + 4);
-      const u32x4 wi = w[i];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const uint32_t w0 = wi[e], w1 = wi[2 + e];
-        acc = __builtin_fmaf(__builtin_bit_cast(float, w0 << 16), x0[2 * e], acc);
-        acc = __builtin_fmaf(__builtin_bit_cast(float, w0 & 0xffff0000u), x0[2 * e + 1], acc);
-        acc = __builtin_fmaf(__builtin_bit_cast(float, w1 << 16), x1[2 * e], acc);
-        acc = __builtin_fmaf(__builtin_bit_cast(float, w1 & 0xffff0000u), x1[2 * e + 1], acc);
+    for (int ks = 0; ks < R / 32; ++ks) {
+      x[ks][0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      x[ks][1] = x[ks][0];
+      if (live) {
+        x[ks][0] = *reinterpret_cast<const f32x4*>(ol + 32 * ks);
+        x[ks][1] = *reinterpret_cast<const f32x4*>(ol + 32 * ks + 4);
       }
     }
-    acc = row_sum16(acc);
-    if (part == 0) a.out[((int64_t)b * a.H + h) * DV + d] = f32_to_bf16(acc);
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < R / 32; ++ks) {
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v0 = x[ks][0][e], v1 = x[ks][1][e];
+        const __bf16 h0 = (__bf16)v0, h1 = (__bf16)v1;
+        hi[e] = h0;
+        hi[4 + e] = h1;
+        lo[e] = (__bf16)(v0 - (float)h0);
+        lo[4 + e] = (__bf16)(v1 - (float)h1);
+      }
+      const bf16x8 w = __builtin_bit_cast(bf16x8, wf[ks]);
+      acc = mfma16(w, hi, acc);
+      acc = mfma16(w, lo, acc);
+    }
+    // acc[r] = out[b][d0 + 4g + r]
+    if (live) {
+      const uint32_t p0 = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+      const uint32_t p1 = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+      *reinterpret_cast<uint2*>(a.out + ((int64_t)b * a.H + h) * DV + d0 + 4 * g) = uint2{p0, p1};
+    }
   }
 }
 
@@ -341,8 +440,8 @@ hipError_t launch_latent_decode(const LatentArgs& a, hipStream_t stream) {
     case 3: hipLaunchKernelGGL(latent_attn_kernel_w3, dim3(grid), dim3(192), 0, stream, a); break;
     default: hipLaunchKernelGGL(latent_attn_kernel, dim3(grid), dim3(256), 0, stream, a); break;
   }
-  hipLaunchKernelGGL(latent_merge_kernel, dim3(a.B * a.H), dim3(64), 0, stream, a);
-  hipLaunchKernelGGL(latent_up_kernel, dim3(a.H * 8), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(latent_merge_kernel, dim3(a.B * a.H), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(latent_up_kernel, dim3(a.H * 4), dim3(128), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -33,7 +33,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from seeded_inputs import WORKLOADS, device_inputs, host_inputs  # noqa: E402
+from seeded_inputs import (LATENT_WORKLOADS, WORKLOADS, device_inputs, host_inputs,  # noqa: E402
+                           latent_device_inputs, latent_host_inputs)
 
 METRIC = "prefill attn TFLOP/s & decode HBM GB/s, 1 MI355X, as fraction of peak"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
@@ -43,6 +44,7 @@ CACHE_BYTES = 256 << 20      # Infinity Cache
 KERNEL_SOURCES = {
     "mla_decode_kernel": "attention_mla_causal_amd/csrc/mla_decode.hip",
     "mla_prefill_kernel": "attention_mla_causal_amd/csrc/mla_prefill.hip",
+    "latent_attn_kernel": "attention_mla_causal_amd/csrc/mla_latent.hip",
 }
 
 
@@ -53,6 +55,20 @@ def log(msg):
 def decode_bytes(wl) -> int:
     B, H, S = wl.B, wl.H, wl.S
     return B * (H * S * (128 + 128) * 2 + S * 64 * 2 + H * 192 * 2 + H * 128 * 2)
+
+
+def latent_bytes(wl) -> int:
+    """Decode over the compressed cache: the latent and rotary key of every key
+    (once per sequence), kv_b_proj's weight (once per call), queries, output."""
+    B, H, S = wl.B, wl.H, wl.S
+    return B * S * (512 + 64) * 2 + H * 256 * 512 * 2 + B * H * (192 + 128) * 2
+
+
+def latent_flops(wl) -> int:
+    """Two contractions per (batch, head, key) over 576 and 512 dims, plus the
+    absorb and up-projection matrix-vector products."""
+    B, H, S = wl.B, wl.H, wl.S
+    return 2 * B * H * S * (576 + 512) + 2 * B * H * 128 * 512 * 2
 
 
 def prefill_flops(wl) -> int:
@@ -198,6 +214,49 @@ def run_decode(wl, steps, warmup, seed=0, graph=True, copies=None):
     return res
 
 
+def run_latent(wl, steps, warmup, seed=0, copies=None):
+    """mla_attn_decode_latent, graph-timed over rotating input copies (weights too)."""
+    import torch
+    import attention_mla_causal_amd as mla
+    dev = torch.device("cuda:0")
+    nbytes = latent_bytes(wl)
+    if copies is None:
+        copies = 1 if nbytes >= 2 * CACHE_BYTES else min(64, -(-2 * CACHE_BYTES // nbytes) + 1)
+    log(f"[bench] {wl.name}: B={wl.B} H={wl.H} S={wl.S} copies={copies} steps={steps}")
+    if wl.B * wl.S * 512 * 2 > (1 << 28):
+        sets = [latent_device_inputs(wl, dev, seed=seed + c) for c in range(copies)]
+        recipe = "device"
+    else:
+        sets = [{k: to_dev(v, dev) for k, v in latent_host_inputs(wl, seed=seed + c).items()}
+                for c in range(copies)]
+        recipe = "host"
+    out = torch.empty((wl.B, wl.H, 1, 128), dtype=torch.bfloat16, device=dev)
+    need = mla.mla_attn_decode_latent_workspace_bytes(wl.B, wl.H, wl.S)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        d = sets[i % copies]
+        mla.mla_attn_decode_latent(d["q_nope"], d["q_pe"], d["c_kv"], d["k_pe"], d["w_kv_b"],
+                                   wl.past_len, wl.softmax_scale, out=out, workspace=ws)
+
+    ms, wall_ms = time_graph(step, steps, warmup)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tfs = latent_flops(wl) / (ms * 1e-3) / 1e12
+    kernel = "latent_attn_kernel"
+    res = {
+        "workload": wl.name, "B": wl.B, "H": wl.H, "T": 1, "past_len": wl.past_len, "S": wl.S,
+        "inputs": recipe, "input_copies": copies, "steps": steps, "timing": "hip_graph",
+        "ms_per_step": ms, "wall_ms_per_step": wall_ms, "value": gbs, "unit": "GB/s",
+        "algorithmic_bytes": nbytes, "algorithmic_flops": latent_flops(wl), "tflops": tfs,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(kernel, wl.name)},
+    }
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_prefill(wl, steps, warmup, seed=0):
     import torch
     import attention_mla_causal_amd as mla
@@ -329,6 +388,8 @@ def main():
                     r["cpu_baseline"] = cpu_baseline_prefill(w, x, min(args.cpu_seconds, 5.0))
                 del x
             workloads[name] = r
+        for name, w in LATENT_WORKLOADS.items():
+            workloads[name] = run_latent(w, 200 if w.B == 1 else args.extra_steps, 3)
 
     line = {
         "metric": METRIC,
