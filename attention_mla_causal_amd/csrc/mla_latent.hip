@@ -17,15 +17,17 @@
 // Four kernels on the caller's stream:
 //  1. absorb: q~ for every (batch, head) on MFMA (W_k read transposed out of
 //     LDS), rounded to bf16, joined with q_pe into a 576-dim row (workspace).
-//  2. attention: one workgroup per (batch, key split) with one wave per 16
-//     heads. 32-key tiles of [latent | k_pe] (36 KiB) are copied straight from
-//     HBM into LDS (buffer_load ... lds; four buffers, three tiles ahead), in
-//     64-byte column blocks with row-swizzled 16-byte chunks. Scores use
-//     v_mfma_f32_16x16x32_bf16 with keys as rows and the wave's 16 heads as
-//     columns (S^T = K Q~^T, 18 K-steps); online softmax in fp32 per head; the
-//     latent output uses O~^T = C^T P^T, 32 tiles of 16 latent dims, whose
-//     C^T fragments come from ds_read_b64_tr_b16 in the key order the score
-//     accumulator leaves P in. Each split writes an fp32 partial (o~, max, sum).
+//  2. attention: one workgroup per (batch, key split), four waves. 32-key
+//     tiles of [latent | k_pe] (36 KiB) are copied straight from HBM into LDS
+//     (buffer_load ... lds; four buffers, two tiles ahead), in 64-byte column
+//     blocks with swizzled 16-byte chunks. Scores use v_mfma_f32_16x16x32_bf16
+//     with keys as rows and a wave's 16 heads as columns (S^T = K Q~^T, 18
+//     K-steps); online softmax in fp32 per head. The latent output
+//     O~^T = C^T P^T is split by latent dims instead: each wave accumulates
+//     128 dims of all heads from the probabilities every wave leaves in LDS,
+//     one tile behind the scores, its C^T fragments read with
+//     ds_read_b64_tr_b16 in the key order the score accumulator leaves P in.
+//     Each split writes an fp32 partial (o~, max, sum).
 //  3. merge: log-sum-exp over the splits of each (batch, head) -> o~ (fp32).
 //  4. up-projection: out = W_v o~ on MFMA (o~ split into two bf16 halves),
 //     rounded to bf16.
@@ -151,6 +153,15 @@ __global__ __launch_bounds__(256) void latent_absorb_kernel(LatentArgs a) {
   }
 }
 
+// Chunk swizzle of the tile layout: chunk c & 3 of row r sits at position
+// (c & 3) ^ tile_swz(r), the two bits of (r >> 2) & 3 swapped. Sixteen lanes
+// reading one chunk of sixteen rows, and thirty-two lanes reading half a
+// row of eight rows (the transposed reads), then touch every bank once.
+__device__ __forceinline__ int tile_swz(int r) {
+  const int x = (r >> 2) & 3;
+  return ((x & 1) << 1) | (x >> 1);
+}
+
 // Buffer resource over rows [kb, end) of one sequence's row-major
 // [S, rowbytes/2] bf16 tensor; rows at or past `end` read as zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* seq, int64_t kb,
@@ -164,15 +175,37 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* seq,
 }
 
 // ---- 2. attention over the latent keys of one key split
-template <int NWV>  // waves per workgroup: one per 16 heads
-__device__ __forceinline__ void latent_attn(const LatentArgs& a) {
-  // four tile buffers: tile t lives in buf[t % 4] and is copied three steps ahead
+// Workgroup: one (batch, key split), four waves, always 64 head columns (heads
+// at or past H get zero queries and are never stored). Phase p of the loop
+// does two independent jobs in one straight run of code:
+//   * scores of tile p for heads 16w .. 16w+15 (wave w), the online-softmax
+//     update of their max and sum, and their probabilities, which go to LDS
+//     in the MFMA B-operand layout together with the rescale factor;
+//   * the latent output of tile p-1 for latent dims 128w .. 128w+127 of all
+//     64 heads, from the probabilities the four waves left in LDS.
+// Each wave thus reads the whole tile once for its scores but only a quarter
+// of it for the output. Tile t sits in buffer t % 4; at phase p tiles p and
+// p-1 are read and tile p+2 is copied into the buffer tile p-2 left.
+constexpr int NWAVE = 4;
+constexpr int NCOPY = COPIES / NWAVE;  // 9 one-KiB copies per wave per tile
+constexpr int NDTW = NDT / NWAVE;      // 8 latent-dim tiles of 16 per wave
+static_assert(COPIES % NWAVE == 0, "copies must divide over the waves");
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// and every LDS operation it issued has completed.
+template <int N>
+__device__ __forceinline__ void wait_vmem_keep_lds_done() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | ((N >> 4) << 14));
+}
+
+__global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
   __shared__ __attribute__((aligned(1024))) char tile0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char tile1[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char tile2[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char tile3[TILE_BYTES];
-  constexpr int NCOPY = COPIES / NWV;
-  static_assert(COPIES % NWV == 0, "copies must divide over the waves");
+  __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2][NWAVE][64];  // [phase parity][head group][lane]
+  __shared__ float abuf[2][NWAVE * 16];                               // rescale factor per head
 
   const int b = blockIdx.x / a.nsplit, split = blockIdx.x % a.nsplit;
   const int lane = threadIdx.x & 63;
@@ -182,156 +215,187 @@ __device__ __forceinline__ void latent_attn(const LatentArgs& a) {
   const int64_t k0 = (int64_t)split * a.keys_per_split;
   const int64_t k1 = (k0 + a.keys_per_split < S) ? k0 + a.keys_per_split : S;
   const int ntiles = (int)((k1 - k0 + BN - 1) / BN);
-  const int h0 = wave * 16;
   const uint16_t* c_seq = a.c_kv + (int64_t)b * S * R;
   const uint16_t* kp_seq = a.k_pe + (int64_t)b * S * DR;
+
+  // absorbed queries of heads 16w + j (B operand): lane (g, j) holds dims
+  // 32 ks + 8 g .. + 8; zero for heads at or past H
+  bf16x8 qf[KSTEPS];
+  if (16 * wave < H) {
+    const uint16_t* q = a.qt + ((int64_t)b * H + 16 * wave + j) * KW + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(q + 32 * ks);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = bf16x8{};
+  }
 
   // Copy t of a tile moves 1 KiB: t < 32 latent, t >= 32 rotary key. Lane l
   // moves physical chunk pc = (t mod region) * 64 + l of its region; block
   // cb = pc / 128 holds row r = (pc / 4) % 32 at r * 64, its chunk c & 3 at
-  // position (c & 3) ^ ((r >> 2) & 3).
+  // position (c & 3) ^ tile_swz(r).
   int voff[NCOPY];
 #pragma unroll
   for (int u = 0; u < NCOPY; ++u) {
-    const int t = u * NWV + wave;
+    const int t = u * NWAVE + wave;
     const bool lat = t < LAT_COPIES;
     const int pc = (lat ? t : t - LAT_COPIES) * 64 + lane;
-    const int cb = pc >> 7, r = (pc >> 2) & 31, c4 = (pc & 3) ^ ((r >> 2) & 3);
+    const int cb = pc >> 7, r = (pc >> 2) & 31, c4 = (pc & 3) ^ tile_swz(r);
     voff[u] = r * (lat ? R * 2 : DR * 2) + (cb * 4 + c4) * 16;
   }
+  // Past the split's end a copy still runs but reads nothing (rows at or past
+  // k1 read as zeros), so every phase costs each wave exactly NCOPY copies and
+  // one vmcnt bound serves every phase.
   auto copy_tile = [&](int t, char* dst) {
     const int64_t kb = k0 + (int64_t)t * BN;
     const __amdgpu_buffer_rsrc_t rc = rows_rsrc(c_seq, kb, k1, R * 2);
     const __amdgpu_buffer_rsrc_t rp = rows_rsrc(kp_seq, kb, k1, DR * 2);
 #pragma unroll
     for (int u = 0; u < NCOPY; ++u) {
-      const int ct = u * NWV + wave;  // uniform
+      const int ct = u * NWAVE + wave;  // uniform
       if (ct < LAT_COPIES)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void*)(dst + ct * 1024), 16, voff[u], 0, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (lds_void*)(dst + ct * 1024), 16, voff[u], 0, 0, 0);
     }
   };
-
-  // absorbed queries of the wave's 16 heads (B operand): lane (g, j) holds
-  // head h0 + j, dims 32 ks + 8 g .. + 8
-  bf16x8 qf[KSTEPS];
-  {
-    const uint16_t* q = a.qt + ((int64_t)b * H + h0 + j) * KW + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(q + 32 * ks);
-  }
-
-  // Past the split's end a copy still runs but reads nothing (rows past k1 read
-  // as zeros), so every tile costs each wave exactly NCOPY copies and one
-  // vmcnt bound serves every step.
   copy_tile(0, tile0);
   copy_tile(1, tile1);
-  copy_tile(2, tile2);
 
   // LDS operand offsets. Score A operand (16 keys x 32 dims): lane (g, j)
   // reads key row kt*16 + j, chunk g of column block ks. Output A operand
   // (16 latent dims x 32 keys, transposed read): lane (g, j) addresses 8 bytes
   // of key row 4g + j/4 (and +16), dims 16 dt + 4 (j % 4); the read hands lane
-  // i dims 16 dt + i of keys 4g .. 4g+3 (and 16+4g ..), the key order of the
-  // score accumulator.
-  const int kA = j * 64 + ((g ^ (j >> 2)) & 3) * 16;
-  const int vrow = 4 * g + (j >> 2);
-  const int vA0 = vrow * 64 + ((((j & 3) >> 1)) ^ g) * 16 + 8 * (j & 1);        // even dt
-  const int vA1 = vrow * 64 + (((2 + ((j & 3) >> 1))) ^ g) * 16 + 8 * (j & 1);  // odd dt
+  // i dims 16 dt + i of keys 4g .. 4g+3 (and 16+4g ..), the key order in which
+  // the score accumulator leaves the probabilities.
+  const int kA = j * 64 + (g ^ tile_swz(j)) * 16;
+  const int vrow = 4 * g + (j >> 2);  // tile_swz(vrow) = tile_swz(vrow + 16) = tile_swz(4 g)
+  const int vA0 = vrow * 64 + (((j & 3) >> 1) ^ tile_swz(vrow)) * 16 + 8 * (j & 1);        // even dt
+  const int vA1 = vrow * 64 + ((2 + ((j & 3) >> 1)) ^ tile_swz(vrow)) * 16 + 8 * (j & 1);  // odd dt
 
   const float cl2 = a.scale_log2;
-  f32x4 o[NDT];
+  // o[hg * NDTW + d]: dims 128w + 16d + 4g + r, head 16 hg + j
+  f32x4 o[NWAVE * NDTW];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int i = 0; i < NWAVE * NDTW; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  constexpr int IN_FLIGHT = (2 * NCOPY < 63) ? 2 * NCOPY : 63;
-  auto step = [&](int t, const char* cur, char* fill) {
-    wait_vmem_keep<IN_FLIGHT>();   // this wave's copies of tile t have landed
-    __builtin_amdgcn_s_barrier();  // ... and every wave's; nobody reads tile t-1 any more
-    copy_tile(t + 3, fill);
-    const int64_t kb = k0 + (int64_t)t * BN;
-    // scores S^T: keys kb + kt*16 + 4g + r, head h0 + j
-    f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto phase = [&](int p, const char* cur, const char* prv, char* fill, bool do_scores,
+                   bool do_out) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    wait_vmem_keep_lds_done<NCOPY>();  // tile p landed (this wave); its LDS writes are done
+    __builtin_amdgcn_s_barrier();      // ... every wave's; tile p-2's buffer is free
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    copy_tile(p + 2, fill);
+    bf16x8 pin[NWAVE];
+    if (do_out) {
+      // rescale by the factors of tile p-1 before its contribution lands
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(cur + ks * CB_BYTES + kA);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(cur + ks * CB_BYTES + 16 * 64 + kA);
-      s0 = mfma16(a0, qf[ks], s0);
-      s1 = mfma16(a1, qf[ks], s1);
+      for (int hg = 0; hg < NWAVE; ++hg) {
+        const float al = abuf[(p - 1) & 1][16 * hg + j];
+        pin[hg] = pbuf[(p - 1) & 1][hg][lane];
+        if (__any(al != 1.0f)) {
+#pragma unroll
+          for (int d = 0; d < NDTW; ++d) o[hg * NDTW + d] *= al;
+        }
+      }
     }
-    // keys past this split's end (or the sequence's) take no weight
-    const int64_t lim = k1 - kb;  // keys kb .. kb + lim - 1 are visible (lim >= 1)
-    float x[8];
+    if (do_scores) {
+      const int64_t kb = k0 + (int64_t)p * BN;
+      // scores S^T: keys kb + kt*16 + 4g + r, head 16w + j
+      f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      x[r] = (4 * g + r < lim) ? s0[r] : -INFINITY;
-      x[4 + r] = (16 + 4 * g + r < lim) ? s1[r] : -INFINITY;
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(cur + ks * CB_BYTES + kA);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(cur + ks * CB_BYTES + 16 * 64 + kA);
+        s0 = mfma16(a0, qf[ks], s0);
+        s1 = mfma16(a1, qf[ks], s1);
+      }
+      // keys past this split's end (or the sequence's) take no weight
+      const int64_t lim = k1 - kb;  // keys kb .. kb + lim - 1 are visible (lim >= 1)
+      float x[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[r] = (4 * g + r < lim) ? s0[r] : -INFINITY;
+        x[4 + r] = (16 + 4 * g + r < lim) ? s1[r] : -INFINITY;
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int r = 1; r < 8; ++r) mx = fmaxf(mx, x[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * cl2);
+      const float ref = (m_new == -INFINITY) ? 0.0f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - ref);
+      m_run = m_new;
+      float psum = 0.0f;
+      bf16x8 pb;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], cl2, -ref));
+        psum += pr;
+        pb[r] = (__bf16)pr;
+      }
+      l_run = l_run * alpha + psum;
+      pbuf[p & 1][wave][lane] = pb;
+      if (g == 0) abuf[p & 1][16 * wave + j] = alpha;
     }
-    float mx = x[0];
+    if (do_out) {
+      // latent output O~^T += C^T P^T for this wave's 128 dims, all head groups
 #pragma unroll
-    for (int r = 1; r < 8; ++r) mx = fmaxf(mx, x[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * cl2);
-    const float ref = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - ref);
-    m_run = m_new;
-    float psum = 0.0f;
-    bf16x8 pb;
+      for (int d = 0; d < NDTW; ++d) {
+        const int dt = wave * NDTW + d;
+        const char* pp = prv + (dt >> 1) * CB_BYTES + ((dt & 1) ? vA1 : vA0);
+        const bf16x4 lo = lds_tr_read(pp);
+        const bf16x4 hi = lds_tr_read(pp + 16 * 64);
+        const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], cl2, -ref));
-      psum += p;
-      pb[r] = (__bf16)p;
-    }
-    l_run = l_run * alpha + psum;
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-    }
-    // latent output O~^T += C^T P^T, 16 latent dims per MFMA
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const char* p = cur + (dt >> 1) * CB_BYTES + ((dt & 1) ? vA1 : vA0);
-      const bf16x4 lo = lds_tr_read(p);
-      const bf16x4 hi = lds_tr_read(p + 16 * 64);
-      const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      o[dt] = mfma16(va, pb, o[dt]);
+        for (int hg = 0; hg < NWAVE; ++hg) o[hg * NDTW + d] = mfma16(va, pin[hg], o[hg * NDTW + d]);
+      }
     }
   };
 
-  // unrolled by four so that every buffer role is fixed in each copy of the step
-  int t = 0;
-  for (; t + 3 < ntiles; t += 4) {
-    step(t, tile0, tile3);
-    step(t + 1, tile1, tile0);
-    step(t + 2, tile2, tile1);
-    step(t + 3, tile3, tile2);
+  // phase 0: scores only; phases 1 .. ntiles-1: both; phase ntiles: output only.
+  // Unrolled by four so that every buffer role is fixed in each copy.
+  phase(0, tile0, tile3, tile2, true, false);
+  int p = 1;
+  for (; p + 3 < ntiles; p += 4) {
+    phase(p, tile1, tile0, tile3, true, true);
+    phase(p + 1, tile2, tile1, tile0, true, true);
+    phase(p + 2, tile3, tile2, tile1, true, true);
+    phase(p + 3, tile0, tile3, tile2, true, true);
   }
-  if (t < ntiles) step(t, tile0, tile3);
-  if (t + 1 < ntiles) step(t + 1, tile1, tile0);
-  if (t + 2 < ntiles) step(t + 2, tile2, tile1);
+  if (p < ntiles) phase(p, tile1, tile0, tile3, true, true);
+  if (p + 1 < ntiles) phase(p + 1, tile2, tile1, tile0, true, true);
+  if (p + 2 < ntiles) phase(p + 2, tile3, tile2, tile1, true, true);
+  // the last phase reads tile ntiles - 1, in buffer (ntiles - 1) % 4
+  switch ((ntiles - 1) & 3) {
+    case 0: phase(ntiles, tile1, tile0, tile3, false, true); break;
+    case 1: phase(ntiles, tile2, tile1, tile0, false, true); break;
+    case 2: phase(ntiles, tile3, tile2, tile1, false, true); break;
+    default: phase(ntiles, tile0, tile3, tile2, false, true); break;
+  }
   wait_vmem_keep<0>();  // (copies past the end are never read; let them land before exit)
 
-  // ---- partial of this split: o~ (unnormalised), max and sum per head
+  // ---- partial of this split: o~ (unnormalised) for this wave's dims; max and
+  // sum of the wave's own heads
+  const int64_t row0 = ((int64_t)b * a.nsplit + split) * H;
+#pragma unroll
+  for (int hg = 0; hg < NWAVE; ++hg) {
+    if (16 * hg < H) {
+      float* po = a.po + (row0 + 16 * hg + j) * R + 128 * wave + 4 * g;
+#pragma unroll
+      for (int d = 0; d < NDTW; ++d) *reinterpret_cast<f32x4*>(po + 16 * d) = o[hg * NDTW + d];
+    }
+  }
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  const int64_t row = ((int64_t)b * a.nsplit + split) * H + h0 + j;
-  float* po = a.po + row * R + 4 * g;
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[dt];
-  if (g == 0) {
+  if (16 * wave < H && g == 0) {
+    const int64_t row = row0 + 16 * wave + j;
     a.pml[2 * row] = m_run;
     a.pml[2 * row + 1] = l_tot;
   }
 }
-
-__global__ __launch_bounds__(64, 1) void latent_attn_kernel_w1(LatentArgs a) { latent_attn<1>(a); }
-__global__ __launch_bounds__(128, 1) void latent_attn_kernel_w2(LatentArgs a) { latent_attn<2>(a); }
-__global__ __launch_bounds__(192, 1) void latent_attn_kernel_w3(LatentArgs a) { latent_attn<3>(a); }
-__global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) { latent_attn<4>(a); }
 
 // ---- 3. merge the splits of each (batch, head): o~ = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
 // Workgroup: one (batch, head); wave w sums splits w, w + 4, ..., lane l holds
@@ -433,13 +497,7 @@ __global__ __launch_bounds__(128) void latent_up_kernel(LatentArgs a) {
 
 hipError_t launch_latent_decode(const LatentArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(latent_absorb_kernel, dim3(a.H * 8), dim3(256), 0, stream, a);
-  const int grid = a.B * a.nsplit;
-  switch (a.H / 16) {
-    case 1: hipLaunchKernelGGL(latent_attn_kernel_w1, dim3(grid), dim3(64), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(latent_attn_kernel_w2, dim3(grid), dim3(128), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(latent_attn_kernel_w3, dim3(grid), dim3(192), 0, stream, a); break;
-    default: hipLaunchKernelGGL(latent_attn_kernel, dim3(grid), dim3(256), 0, stream, a); break;
-  }
+  hipLaunchKernelGGL(latent_attn_kernel, dim3(a.B * a.nsplit), dim3(256), 0, stream, a);
   hipLaunchKernelGGL(latent_merge_kernel, dim3(a.B * a.H), dim3(256), 0, stream, a);
   hipLaunchKernelGGL(latent_up_kernel, dim3(a.H * 4), dim3(128), 0, stream, a);
   return hipGetLastError();
