@@ -44,7 +44,7 @@ CACHE_BYTES = 256 << 20      # Infinity Cache
 KERNEL_SOURCES = {
     "mla_decode_kernel": "attention_mla_causal_amd/csrc/mla_decode.hip",
     "mla_prefill_kernel": "attention_mla_causal_amd/csrc/mla_prefill.hip",
-    "latent_attn_kernel": "attention_mla_causal_amd/csrc/mla_latent.hip",
+    "mla_attn_decode_latent": "attention_mla_causal_amd/csrc/mla_latent.hip",  # its four launches
 }
 
 
@@ -214,8 +214,8 @@ def run_decode(wl, steps, warmup, seed=0, graph=True, copies=None):
     return res
 
 
-def run_latent(wl, steps, warmup, seed=0, copies=None):
-    """mla_attn_decode_latent, graph-timed over rotating input copies (weights too)."""
+def run_latent(wl, steps, warmup, seed=0, copies=None, graph=True):
+    """mla_attn_decode_latent, graph-timed (or eager) over rotating input copies (weights too)."""
     import torch
     import attention_mla_causal_amd as mla
     dev = torch.device("cuda:0")
@@ -239,13 +239,17 @@ def run_latent(wl, steps, warmup, seed=0, copies=None):
         mla.mla_attn_decode_latent(d["q_nope"], d["q_pe"], d["c_kv"], d["k_pe"], d["w_kv_b"],
                                    wl.past_len, wl.softmax_scale, out=out, workspace=ws)
 
-    ms, wall_ms = time_graph(step, steps, warmup)
+    if graph:
+        ms, wall_ms = time_graph(step, steps, warmup)
+    else:
+        ms, wall_ms = time_eager(step, steps, warmup)
     gbs = nbytes / (ms * 1e-3) / 1e9
     tfs = latent_flops(wl) / (ms * 1e-3) / 1e12
-    kernel = "latent_attn_kernel"
+    kernel = "mla_attn_decode_latent"  # whole call: absorb, attention, merge, up-projection
     res = {
         "workload": wl.name, "B": wl.B, "H": wl.H, "T": 1, "past_len": wl.past_len, "S": wl.S,
-        "inputs": recipe, "input_copies": copies, "steps": steps, "timing": "hip_graph",
+        "inputs": recipe, "input_copies": copies, "steps": steps,
+        "timing": "hip_graph" if graph else "eager",
         "ms_per_step": ms, "wall_ms_per_step": wall_ms, "value": gbs, "unit": "GB/s",
         "algorithmic_bytes": nbytes, "algorithmic_flops": latent_flops(wl), "tflops": tfs,
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": gbs, "peak": HBM_PEAK_GBS,
@@ -306,6 +310,28 @@ def cpu_baseline_decode(wl, seconds):
             "s_per_step": per}
 
 
+def cpu_baseline_latent(wl, seconds):
+    """The fp64 latent-cache oracle on sampled (batch, head) rows until ~`seconds`
+    pass; effective rate = the workload's algorithmic bytes scaled by the share
+    of rows done / time."""
+    from oracle import mla_decode_latent_rows
+    if wl.B * wl.S * 512 * 2 > (1 << 28):
+        return None  # the host copy of the batched cache alone would take minutes to draw
+    x = latent_host_inputs(wl, seed=0)
+    rows, t0 = 0, time.perf_counter()
+    while rows < wl.B * wl.H:
+        b, h = divmod(rows, wl.H)
+        mla_decode_latent_rows(x["q_nope"], x["q_pe"], x["c_kv"], x["k_pe"], x["w_kv_b"], wl.past_len,
+                               wl.softmax_scale, [(b, h)])
+        rows += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": latent_bytes(wl) * rows / (wl.B * wl.H) / el / 1e9, "unit": "GB/s",
+            "cores": blas_threads(), "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{rows} of {wl.B * wl.H} (batch, head) rows, {el:.1f} s"}
+
+
 def cpu_baseline_prefill(wl, x, seconds):
     """The fp64 oracle on the first heads of the workload until ~`seconds` pass;
     effective rate = algorithmic flops of the heads done / time."""
@@ -330,7 +356,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_p1000", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="decode_p1000",
+                    choices=sorted(WORKLOADS) + sorted(LATENT_WORKLOADS))
     ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -364,12 +391,17 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
-    wl = WORKLOADS[args.workload]
     torch.cuda.synchronize()
-    if wl.T == 1:
+    if args.workload in LATENT_WORKLOADS:
+        wl = LATENT_WORKLOADS[args.workload]
+        head = run_latent(wl, args.steps, args.warmup, graph=not args.eager)
+        cpu = None if args.no_cpu else cpu_baseline_latent(wl, args.cpu_seconds)
+    elif WORKLOADS[args.workload].T == 1:
+        wl = WORKLOADS[args.workload]
         head = run_decode(wl, args.steps, args.warmup, graph=not args.eager)
         cpu = None if args.no_cpu else cpu_baseline_decode(wl, args.cpu_seconds)
     else:
+        wl = WORKLOADS[args.workload]
         head, x = run_prefill(wl, args.steps, args.warmup)
         cpu = None if args.no_cpu else cpu_baseline_prefill(wl, x, args.cpu_seconds)
         del x
@@ -389,7 +421,11 @@ def main():
                 del x
             workloads[name] = r
         for name, w in LATENT_WORKLOADS.items():
+            if name == wl.name:
+                continue
             workloads[name] = run_latent(w, 200 if w.B == 1 else args.extra_steps, 3)
+            if not args.no_cpu:
+                workloads[name]["cpu_baseline"] = cpu_baseline_latent(w, min(args.cpu_seconds, 5.0))
 
     line = {
         "metric": METRIC,
