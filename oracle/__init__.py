@@ -23,3 +23,7 @@ from .mla_latent import (  # noqa: F401
     mla_decode_latent,
     mla_decode_latent_rows,
 )
+from .mla_varlen import (  # noqa: F401
+    mla_decode_varlen,
+    mla_decode_varlen_rows,
+)
