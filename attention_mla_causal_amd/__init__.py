@@ -37,6 +37,8 @@ SIGNATURES = {
     "mla_attn_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "mla_attn_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _F32, _VP]),
+    "mla_attn_decode_varlen_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "mla_attn_decode_varlen": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_attn_decode_latent_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "mla_attn_decode_latent": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -186,6 +188,50 @@ def mla_attn_decode(q_nope, q_pe, k_nope, k_pe, v, past_len: int, softmax_scale:
     return out
 
 
+def mla_attn_decode_varlen_workspace_bytes(B: int, H: int, max_seq_len: int) -> int:
+    """Bytes of device scratch mla_attn_decode_varlen needs (0: none)."""
+    return int(_lib.mla_attn_decode_varlen_workspace_bytes(int(B), int(H), int(max_seq_len)))
+
+
+def mla_attn_decode_varlen(q_nope, q_pe, k_nope_cache, k_pe_cache, v_cache, seq_lens,
+                           max_seq_len: int, softmax_scale: float, out=None, workspace=None):
+    """Decode over a preallocated, right-padded cache with a length per sequence.
+
+    q_nope [B,H,1,128], q_pe [B,H,1,64]; k_nope_cache [B,H,L,128], k_pe_cache
+    [B,1,L,64], v_cache [B,H,L,128] with L the cache length; seq_lens an int32
+    GPU tensor [B]: sequence b attends over cache rows [0, seq_lens[b]),
+    each length clamped on the device to [0, max_seq_len] (max_seq_len <= L).
+    A sequence of length 0 gives a zero row. Returns out [B,H,1,128] bf16.
+    """
+    import torch
+
+    B, H, T, L = _shapes(q_nope, q_pe, k_nope_cache, k_pe_cache, v_cache)
+    if T != 1:
+        raise ValueError(f"decode takes one query per sequence, got T={T}")
+    if not (isinstance(seq_lens, torch.Tensor) and seq_lens.dtype == torch.int32 and seq_lens.is_cuda
+            and seq_lens.is_contiguous() and tuple(seq_lens.shape) == (B,)
+            and seq_lens.device == q_nope.device):
+        raise ValueError(f"seq_lens must be a contiguous int32 tensor of shape ({B},) on {q_nope.device}")
+    if out is None:
+        out = torch.empty((B, H, 1, V_HEAD_DIM), dtype=torch.bfloat16, device=q_nope.device)
+    else:
+        _check_tensor(out, "out")
+        if tuple(out.shape) != (B, H, 1, V_HEAD_DIM) or out.device != q_nope.device:
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, 1, V_HEAD_DIM)}")
+    need = mla_attn_decode_varlen_workspace_bytes(B, H, max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_nope.device)
+    if not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.mla_attn_decode_varlen(
+        q_nope.data_ptr(), q_pe.data_ptr(), k_nope_cache.data_ptr(), k_pe_cache.data_ptr(),
+        v_cache.data_ptr(), seq_lens.data_ptr(), out.data_ptr(), workspace.data_ptr(), ws_bytes,
+        B, H, L, int(max_seq_len), float(softmax_scale), _stream_handle(q_nope.device))
+    _raise_for(st, "mla_attn_decode_varlen")
+    return out
+
+
 KV_LORA_RANK = 512
 
 
@@ -242,6 +288,8 @@ def mla_attn_decode_latent(q_nope, q_pe, c_kv, k_pe, w_kv_b, past_len: int, soft
 
 
 __all__ = [
+    "mla_attn_decode_varlen",
+    "mla_attn_decode_varlen_workspace_bytes",
     "mla_attn_decode_latent",
     "mla_attn_decode_latent_workspace_bytes",
     "mla_attn_prefill",

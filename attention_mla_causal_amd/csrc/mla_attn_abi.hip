@@ -35,6 +35,61 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 }  // namespace
 
+namespace {
+
+// Both decode entry points: fill the arguments from a checked plan and launch.
+mla_status launch_decode_call(const char* where, const void* q_nope, const void* q_pe,
+                              const void* k_nope, const void* k_pe, const void* v,
+                              const int32_t* seq_lens, void* out, void* workspace,
+                              const mla::DecodePlan& plan, int32_t B, int32_t H, int32_t S,
+                              int32_t cap, float softmax_scale, void* stream) {
+  mla::DecodeArgs a;
+  a.seq_lens = seq_lens;
+  a.cap = cap;
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.k_nope = static_cast<const uint16_t*>(k_nope);
+  a.k_pe = static_cast<const uint16_t*>(k_pe);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<uint16_t*>(out);
+  char* ws = static_cast<char*>(workspace);
+  a.ws_o = plan.nsplit > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ws_ml = plan.nsplit > 1 ? reinterpret_cast<float*>(ws + plan.ws_o_bytes) : nullptr;
+  a.ws_flag = plan.nsplit > 1
+                  ? reinterpret_cast<unsigned long long*>(ws + plan.ws_o_bytes + plan.ws_ml_bytes)
+                  : nullptr;
+  {
+    // A fresh tag per call: completion flags left by earlier calls (or any
+    // garbage in the workspace) hold another value and count as not done.
+    static std::atomic<unsigned long long> next_tag{0x6d6c615f00000001ull};
+    a.tag = next_tag.fetch_add(1);
+  }
+  {
+    // The split kernel merges the partials itself when every split of a
+    // (b, h) runs on one XCD (workgroup w runs on XCD w % 8, and the kernel
+    // hands each XCD whole (b, h) groups); otherwise a second kernel merges.
+    // With a length per sequence, (b, h) pairs are dealt round-robin over
+    // the XCDs when B*H is a multiple of 8, which keeps each one's splits
+    // together by construction.
+    const int64_t bh = (int64_t)B * H;
+    const int64_t grid = bh * plan.nsplit;
+    a.interleave = (seq_lens != nullptr && bh % 8 == 0) ? 1 : 0;
+    const bool together = a.interleave || (grid % 8 == 0 && (grid / 8) % plan.nsplit == 0);
+    a.fused = (plan.nsplit > 1 && plan.nsplit <= 64 && together) ? 1 : 0;
+  }
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.nsplit = (int32_t)plan.nsplit;
+  a.keys_per_split = (int32_t)plan.keys_per_split;
+  a.scale_log2 = softmax_scale * kLog2e;
+  const hipError_t e = mla::launch_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(where, e);
+  return MLA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 mla_status mla_attn_prefill(const void* q_nope, const void* q_pe, const void* k_nope,
@@ -79,44 +134,29 @@ mla_status mla_attn_decode(const void* q_nope, const void* q_pe, const void* k_n
                                                softmax_scale, &plan);
   if (r.status != MLA_OK) return report("mla_attn_decode", r);
   if (r.empty) return MLA_OK;
-  mla::DecodeArgs a;
-  a.q_nope = static_cast<const uint16_t*>(q_nope);
-  a.q_pe = static_cast<const uint16_t*>(q_pe);
-  a.k_nope = static_cast<const uint16_t*>(k_nope);
-  a.k_pe = static_cast<const uint16_t*>(k_pe);
-  a.v = static_cast<const uint16_t*>(v);
-  a.out = static_cast<uint16_t*>(out);
-  char* ws = static_cast<char*>(workspace);
-  a.ws_o = plan.nsplit > 1 ? reinterpret_cast<float*>(ws) : nullptr;
-  a.ws_ml = plan.nsplit > 1 ? reinterpret_cast<float*>(ws + plan.ws_o_bytes) : nullptr;
-  a.ws_flag = plan.nsplit > 1
-                  ? reinterpret_cast<unsigned long long*>(ws + plan.ws_o_bytes + plan.ws_ml_bytes)
-                  : nullptr;
-  {
-    // A fresh tag per call: completion flags left by earlier calls (or any
-    // garbage in the workspace) hold another value and count as not done.
-    static std::atomic<unsigned long long> next_tag{0x6d6c615f00000001ull};
-    a.tag = next_tag.fetch_add(1);
-  }
-  {
-    // The split kernel merges the partials itself when every split of a
-    // (b, h) runs on one XCD (workgroup w runs on XCD w % 8, and the kernel
-    // hands each XCD whole (b, h) groups); otherwise a second kernel merges.
-    const int64_t grid = (int64_t)B * H * plan.nsplit;
-    a.fused = (plan.nsplit > 1 && plan.nsplit <= 64 && grid % 8 == 0 &&
-               (grid / 8) % plan.nsplit == 0)
-                  ? 1
-                  : 0;
-  }
-  a.B = B;
-  a.H = H;
-  a.S = S;
-  a.nsplit = (int32_t)plan.nsplit;
-  a.keys_per_split = (int32_t)plan.keys_per_split;
-  a.scale_log2 = softmax_scale * kLog2e;
-  const hipError_t e = mla::launch_decode(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return device_error("mla_attn_decode", e);
-  return MLA_OK;
+  return launch_decode_call("mla_attn_decode", q_nope, q_pe, k_nope, k_pe, v, nullptr, out,
+                            workspace, plan, B, H, S, S, softmax_scale, stream);
+}
+
+size_t mla_attn_decode_varlen_workspace_bytes(int32_t B, int32_t H, int32_t max_seq_len) {
+  return mla::plan_decode_varlen(B, H, max_seq_len).workspace_bytes;
+}
+
+mla_status mla_attn_decode_varlen(const void* q_nope, const void* q_pe, const void* k_nope_cache,
+                                  const void* k_pe_cache, const void* v_cache,
+                                  const int32_t* seq_lens, void* out, void* workspace,
+                                  size_t workspace_bytes, int32_t B, int32_t H,
+                                  int32_t cache_len, int32_t max_seq_len, float softmax_scale,
+                                  void* stream) {
+  mla::DecodePlan plan;
+  const mla::CheckResult r = mla::check_decode_varlen(
+      q_nope, q_pe, k_nope_cache, k_pe_cache, v_cache, seq_lens, out, workspace, workspace_bytes,
+      B, H, cache_len, max_seq_len, softmax_scale, &plan);
+  if (r.status != MLA_OK) return report("mla_attn_decode_varlen", r);
+  if (r.empty) return MLA_OK;
+  return launch_decode_call("mla_attn_decode_varlen", q_nope, q_pe, k_nope_cache, k_pe_cache,
+                            v_cache, seq_lens, out, workspace, plan, B, H, max_seq_len,
+                            cache_len, softmax_scale, stream);
 }
 
 size_t mla_attn_decode_latent_workspace_bytes(int32_t B, int32_t H, int32_t S) {

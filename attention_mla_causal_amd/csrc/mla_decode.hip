@@ -1,4 +1,8 @@
 // Causal MLA attention, decode (one new query per sequence, S = past_len + 1 keys).
+// Also serves decode over a preallocated, right-padded cache: sequence b then
+// attends over rows [0, seq_lens[b]) of cache slices of `cap` rows (the 2D
+// padding mask that the "Causal mask" page's "Construct causal mask" hands
+// to the 4D mask builder, for right padding); a sequence with no key gives 0.
 //
 // The same computation as prefill with T = 1 (the Kimi K2 "Similarities"
 // page shows it in decode mode with p = 1000: scores [B, 64, 1, 1001]); the
@@ -23,12 +27,16 @@
 //    its partial, then a flag holding the call's tag, waits for both stores,
 //    and reads all flags of its (b, h) past L1; whichever sees every flag set
 //    merges (the last to finish always does; two that finish together both
-//    write the same bytes). No atomics or device-scope fences are needed: on
+//    write the same bytes), then clears the flags of its (b, h), so a replayed
+//    graph, which repeats the captured tag, starts from cleared flags. No
+//    atomics or device-scope fences are needed: on
 //    this chip a device-scope release or acquire writes back or invalidates
 //    the whole L2. For other shapes a second, tiny kernel merges the
 //    partials, ordered by the kernel boundary.
 //  * Workgroups of one sequence are placed on one XCD so the shared k_pe rows
-//    are served from that XCD's L2 for all heads.
+//    are served from that XCD's L2 for all heads. With a length per sequence
+//    that would leave the XCDs unequally loaded, so there the (b, h) pairs go
+//    round-robin over the XCDs instead (k_pe is then read once per XCD).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -99,9 +107,19 @@ __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
 
   const int nwg = gridDim.x;
   const int wg = blockIdx.x;
-  const int logical = (nwg % 8 == 0) ? (wg % 8) * (nwg / 8) + wg / 8 : wg;
-  const int bh = logical / a.nsplit;
-  const int split = logical % a.nsplit;
+  int bh, split;
+  if (a.interleave) {
+    // Variable lengths: (b, h) pairs go round-robin over the XCDs, so every
+    // XCD gets H/8 heads of every sequence and the same share of keys; the
+    // splits of one (b, h) still share an XCD.
+    const int k = wg >> 3;
+    bh = (wg & 7) + 8 * (k / a.nsplit);
+    split = k % a.nsplit;
+  } else {
+    const int logical = (nwg % 8 == 0) ? (wg % 8) * (nwg / 8) + wg / 8 : wg;
+    bh = logical / a.nsplit;
+    split = logical % a.nsplit;
+  }
   const int b = bh / a.H;
 
   const int tid = threadIdx.x;
@@ -110,10 +128,18 @@ __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
   const int cl = lane & 15;   // column slot: dims 8cl..8cl+7 (rotary 4cl..4cl+3)
   const int qq = lane >> 4;   // quarter-wave
 
-  const int64_t S = a.S;
-  const uint16_t* kn_g = a.k_nope + (int64_t)bh * S * DN + 8 * cl;
-  const uint16_t* v_g = a.v + (int64_t)bh * S * DV + 8 * cl;
-  const uint16_t* kp_g = a.k_pe + (int64_t)b * S * DR + 4 * cl;
+  // Keys of this sequence: rows [0, S) of its cache slices (cap rows each).
+  // A length array from the caller is clamped to [0, a.S], so no row past the
+  // bound the host checked against the capacity is ever read.
+  const int64_t cap = a.cap;
+  int64_t S = a.S;
+  if (a.seq_lens != nullptr) {
+    const int32_t len = a.seq_lens[b];
+    S = len < 0 ? 0 : (len > a.S ? a.S : len);
+  }
+  const uint16_t* kn_g = a.k_nope + (int64_t)bh * cap * DN + 8 * cl;
+  const uint16_t* v_g = a.v + (int64_t)bh * cap * DV + 8 * cl;
+  const uint16_t* kp_g = a.k_pe + (int64_t)b * cap * DR + 4 * cl;
 
   float qn[8], qp[4];
   {
@@ -227,7 +253,7 @@ __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
 
   if (a.nsplit == 1) {
     if (wave == 0 && qq == 0) {
-      const float inv = 1.0f / L;
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;  // a sequence with no key gives 0
       uint16_t* dst = a.out + (int64_t)bh * DV + 8 * cl;
       u32x4 w;
 #pragma unroll
@@ -307,7 +333,7 @@ __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
   if (qq == 0) {
     // A partial written on another XCD may not be visible here: poison the
     // output rather than return a silently wrong row.
-    const float inv = same_xcd ? 1.0f / ll : __builtin_nanf("");
+    const float inv = !same_xcd ? __builtin_nanf("") : (ll > 0.0f ? 1.0f / ll : 0.0f);
     uint16_t* dst = a.out + (int64_t)bh * DV + 8 * cl;
     u32x4 w;
 #pragma unroll
@@ -315,6 +341,13 @@ __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
       w[e] = (uint32_t)to_bf16_rne(oo[2 * e] * inv) | ((uint32_t)to_bf16_rne(oo[2 * e + 1] * inv) << 16);
     *reinterpret_cast<u32x4*>(dst) = w;
   }
+  // Clear this (b, h)'s flags for the next call. A replayed graph repeats the
+  // captured tag, so flags left set would make a replay merge partials of the
+  // run before. Every split of this call has already set its flag (that is
+  // why this workgroup merged), so none is written again in this call; a
+  // workgroup still reading them sees a cleared flag and leaves the merge to
+  // this one.
+  for (int sp = lane; sp < a.nsplit; sp += 64) a.ws_flag[(int64_t)bh * a.nsplit + sp] = 0ull;
 }
 
 // Log-sum-exp merge of the nsplit partials of each (b, h): one wave per (b, h);
@@ -344,7 +377,7 @@ __global__ __launch_bounds__(64) void mla_decode_combine_kernel(DecodeArgs a) {
   merge_xor(mm, ll, oo, 16);
   merge_xor(mm, ll, oo, 32);
   if (qq == 0) {
-    const float inv = 1.0f / ll;
+    const float inv = ll > 0.0f ? 1.0f / ll : 0.0f;
     uint16_t* dst = a.out + (int64_t)bh * DV + 8 * cl;
     u32x4 w;
 #pragma unroll

@@ -63,6 +63,32 @@ inline DecodePlan plan_decode(int64_t B, int64_t H, int64_t S) {
   return p;
 }
 
+// Variable-length decode: lengths differ, so a (b, h) with many keys would
+// keep its workgroup running long after the short ones finished. Splitting
+// every (b, h) into pieces of at most this many keys bounds that tail (the
+// pieces past a short sequence's end find no key and finish at once).
+constexpr int64_t kDecodeVarlenKeysPerSplit = 1024;
+constexpr int64_t kDecodeMaxFusedSplits = 64;
+
+inline DecodePlan plan_decode_varlen(int64_t B, int64_t H, int64_t max_len) {
+  DecodePlan p = plan_decode(B, H, max_len);
+  if (B <= 0 || H <= 0 || max_len <= 0) return p;
+  int64_t want = (max_len + kDecodeVarlenKeysPerSplit - 1) / kDecodeVarlenKeysPerSplit;
+  if (want > kDecodeMaxFusedSplits) want = kDecodeMaxFusedSplits;
+  if (want <= p.nsplit) return p;
+  int64_t kps = (max_len + want - 1) / want;
+  kps = (kps + kDecodeKeysPerTrip - 1) / kDecodeKeysPerTrip * kDecodeKeysPerTrip;
+  const int64_t nsplit = (max_len + kps - 1) / kps;
+  const int64_t bh = B * H;
+  p.nsplit = nsplit;
+  p.keys_per_split = kps;
+  p.ws_o_bytes = align256(size_t(bh) * size_t(nsplit) * 128 * sizeof(float));
+  p.ws_ml_bytes = align256(size_t(bh) * size_t(nsplit) * 4 * sizeof(float));
+  p.ws_flag_bytes = align256(size_t(bh) * size_t(nsplit) * sizeof(unsigned long long));
+  p.workspace_bytes = p.ws_o_bytes + p.ws_ml_bytes + p.ws_flag_bytes;
+  return p;
+}
+
 struct CheckResult {
   mla_status status = MLA_OK;
   bool empty = false;  // valid call with nothing to compute
@@ -154,6 +180,78 @@ inline CheckResult check_decode(const void* q_nope, const void* q_pe, const void
   CheckResult r = check_common(q_nope, q_pe, k_nope, k_pe, v, out, B, H, 1, S, past_len, scale);
   if (r.status != MLA_OK || r.empty) return r;
   const DecodePlan plan = plan_decode(B, H, S);
+  if (B * H > kMaxGrid / plan.nsplit) {
+    std::snprintf(r.msg, sizeof(r.msg), "B*H*nsplit exceeds the grid limit");
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  if (plan.workspace_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) {
+      std::snprintf(r.msg, sizeof(r.msg), "workspace %s: %zu bytes given, %zu needed",
+                    workspace == nullptr ? "is NULL" : "too small", workspace_bytes,
+                    plan.workspace_bytes);
+      r.status = MLA_ERR_WORKSPACE;
+      return r;
+    }
+    if (misaligned(workspace)) {
+      std::snprintf(r.msg, sizeof(r.msg), "workspace is not 16-byte aligned");
+      r.status = MLA_ERR_ALIGN;
+      return r;
+    }
+  }
+  if (plan_out) *plan_out = plan;
+  return r;
+}
+
+// ---- decode over a preallocated, right-padded cache with a length per sequence
+inline CheckResult check_decode_varlen(const void* q_nope, const void* q_pe, const void* k_nope,
+                                       const void* k_pe, const void* v, const void* seq_lens,
+                                       const void* out, const void* workspace,
+                                       size_t workspace_bytes, int64_t B, int64_t H, int64_t cap,
+                                       int64_t max_len, float scale, DecodePlan* plan_out) {
+  CheckResult r;
+  if (B < 0 || H < 0 || cap < 0 || max_len < 0) {
+    std::snprintf(r.msg, sizeof(r.msg),
+                  "negative size: B=%lld H=%lld cache_len=%lld max_seq_len=%lld", (long long)B,
+                  (long long)H, (long long)cap, (long long)max_len);
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  if (max_len > cap) {
+    std::snprintf(r.msg, sizeof(r.msg), "max_seq_len %lld exceeds the cache length %lld",
+                  (long long)max_len, (long long)cap);
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  if (B == 0 || H == 0) {
+    r.empty = true;
+    return r;
+  }
+  const void* ptrs[7] = {q_nope, q_pe, k_nope, k_pe, v, seq_lens, out};
+  static const char* const names[7] = {"q_nope", "q_pe", "k_nope_cache", "k_pe_cache",
+                                       "v_cache", "seq_lens", "out"};
+  for (int i = 0; i < 7; ++i) {
+    const bool cache = i >= 2 && i <= 4;
+    if (ptrs[i] == nullptr && !(cache && cap == 0)) {
+      std::snprintf(r.msg, sizeof(r.msg), "%s is NULL", names[i]);
+      r.status = MLA_ERR_NULL;
+      return r;
+    }
+    const uintptr_t align = i == 5 ? 4u : 16u;
+    if ((reinterpret_cast<uintptr_t>(ptrs[i]) & (align - 1)) != 0) {
+      std::snprintf(r.msg, sizeof(r.msg), "%s is not %u-byte aligned", names[i], (unsigned)align);
+      r.status = MLA_ERR_ALIGN;
+      return r;
+    }
+  }
+  const float c = scale * 1.4426950408889634f;
+  if (!std::isfinite(scale) || !(scale > 0.0f) || !std::isfinite(c)) {
+    std::snprintf(r.msg, sizeof(r.msg), "softmax_scale %g must be finite and positive",
+                  (double)scale);
+    r.status = MLA_ERR_SCALE;
+    return r;
+  }
+  const DecodePlan plan = plan_decode_varlen(B, H, max_len);
   if (B * H > kMaxGrid / plan.nsplit) {
     std::snprintf(r.msg, sizeof(r.msg), "B*H*nsplit exceeds the grid limit");
     r.status = MLA_ERR_SHAPE;

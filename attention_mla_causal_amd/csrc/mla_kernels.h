@@ -22,17 +22,20 @@ struct PrefillArgs {
 struct DecodeArgs {
   const uint16_t* q_nope;  // [B,H,1,128]
   const uint16_t* q_pe;    // [B,H,1,64]
-  const uint16_t* k_nope;  // [B,H,S,128]
-  const uint16_t* k_pe;    // [B,1,S,64]
-  const uint16_t* v;       // [B,H,S,128]
+  const uint16_t* k_nope;  // [B,H,cap,128]
+  const uint16_t* k_pe;    // [B,1,cap,64]
+  const uint16_t* v;       // [B,H,cap,128]
+  const int32_t* seq_lens; // [B] keys per sequence (rows [0, len) of the cache), or null: S each
   uint16_t* out;           // [B,H,1,128]
   float* ws_o;             // [B*H, nsplit, 128] partial outputs (nsplit > 1)
   float* ws_ml;            // [B*H, nsplit, 4] partial (max, sum, XCD id, unused)
   unsigned long long* ws_flag;  // [B*H, nsplit] completion flags (this call's tag)
   unsigned long long tag;  // this call's tag
-  int32_t B, H, S;
+  int32_t B, H, S;         // S: keys per sequence, or the bound lengths are clamped to
+  int32_t cap;             // cache rows per (b, h) slice (= S without seq_lens)
   int32_t nsplit, keys_per_split;
   int32_t fused;           // the last workgroup of each (b, h) merges the partials
+  int32_t interleave;      // (b, h) -> XCD (b*H + h) % 8 (needs B*H % 8 == 0); else by sequence
   float scale_log2;
 };
 

@@ -33,8 +33,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from seeded_inputs import (LATENT_WORKLOADS, WORKLOADS, device_inputs, host_inputs,  # noqa: E402
-                           latent_device_inputs, latent_host_inputs)
+from seeded_inputs import (LATENT_WORKLOADS, VARLEN_WORKLOADS, WORKLOADS, device_inputs,  # noqa: E402
+                           host_inputs, latent_device_inputs, latent_host_inputs, varlen_seq_lens)
 
 METRIC = "prefill attn TFLOP/s & decode HBM GB/s, 1 MI355X, as fraction of peak"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
@@ -55,6 +55,14 @@ def log(msg):
 def decode_bytes(wl) -> int:
     B, H, S = wl.B, wl.H, wl.S
     return B * (H * S * (128 + 128) * 2 + S * 64 * 2 + H * 192 * 2 + H * 128 * 2)
+
+
+def varlen_bytes(wl, lens) -> int:
+    """Right-padded cache: each sequence's valid rows only (k_nope + v per head,
+    the shared rotary key once), plus queries and output."""
+    H = wl.H
+    L = int(np.asarray(lens, dtype=np.int64).sum())
+    return H * L * (128 + 128) * 2 + L * 64 * 2 + wl.B * H * (192 + 128) * 2
 
 
 def latent_bytes(wl) -> int:
@@ -214,6 +222,46 @@ def run_decode(wl, steps, warmup, seed=0, graph=True, copies=None):
     return res
 
 
+def run_varlen(wl, steps, warmup, seed=0, graph=True):
+    """mla_attn_decode_varlen on a right-padded cache (inputs drawn on the
+    device; the cache is far larger than the Infinity Cache)."""
+    import torch
+    import attention_mla_causal_amd as mla
+    dev = torch.device("cuda:0")
+    lens = varlen_seq_lens(wl.B, wl.cap, seed=seed)
+    nbytes = varlen_bytes(wl, lens)
+    log(f"[bench] {wl.name}: B={wl.B} H={wl.H} cap={wl.cap} sum(lens)={int(lens.sum())} steps={steps}")
+    d = device_inputs(wl.cache(), dev, seed=seed)
+    sl = torch.as_tensor(lens, device=dev)
+    out = torch.empty((wl.B, wl.H, 1, 128), dtype=torch.bfloat16, device=dev)
+    need = mla.mla_attn_decode_varlen_workspace_bytes(wl.B, wl.H, wl.cap)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        mla.mla_attn_decode_varlen(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], sl, wl.cap,
+                                   wl.softmax_scale, out=out, workspace=ws)
+
+    if graph:
+        ms, wall_ms = time_graph(step, steps, warmup)
+    else:
+        ms, wall_ms = time_eager(step, steps, warmup)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    kernel = "mla_decode_kernel"
+    res = {
+        "workload": wl.name, "B": wl.B, "H": wl.H, "T": 1, "cache_len": wl.cap,
+        "sum_seq_lens": int(lens.sum()), "min_seq_len": int(lens.min()), "inputs": "device",
+        "steps": steps, "timing": "hip_graph" if graph else "eager",
+        "ms_per_step": ms, "wall_ms_per_step": wall_ms, "value": gbs, "unit": "GB/s",
+        "algorithmic_bytes": nbytes,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(kernel, wl.name)},
+    }
+    del d
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_latent(wl, steps, warmup, seed=0, copies=None, graph=True):
     """mla_attn_decode_latent, graph-timed (or eager) over rotating input copies (weights too)."""
     import torch
@@ -357,7 +405,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_p1000",
-                    choices=sorted(WORKLOADS) + sorted(LATENT_WORKLOADS))
+                    choices=sorted(WORKLOADS) + sorted(LATENT_WORKLOADS) + sorted(VARLEN_WORKLOADS))
     ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -392,7 +440,11 @@ def main():
         sys.exit(2)
 
     torch.cuda.synchronize()
-    if args.workload in LATENT_WORKLOADS:
+    if args.workload in VARLEN_WORKLOADS:
+        wl = VARLEN_WORKLOADS[args.workload]
+        head = run_varlen(wl, args.steps, args.warmup, graph=not args.eager)
+        cpu = None
+    elif args.workload in LATENT_WORKLOADS:
         wl = LATENT_WORKLOADS[args.workload]
         head = run_latent(wl, args.steps, args.warmup, graph=not args.eager)
         cpu = None if args.no_cpu else cpu_baseline_latent(wl, args.cpu_seconds)
@@ -420,6 +472,9 @@ def main():
                     r["cpu_baseline"] = cpu_baseline_prefill(w, x, min(args.cpu_seconds, 5.0))
                 del x
             workloads[name] = r
+        for name, w in VARLEN_WORKLOADS.items():
+            if name != wl.name:
+                workloads[name] = run_varlen(w, args.extra_steps, 3)
         for name, w in LATENT_WORKLOADS.items():
             if name == wl.name:
                 continue

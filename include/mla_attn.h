@@ -104,7 +104,55 @@ mla_status mla_attn_decode(const void* q_nope, const void* q_pe,
                            int32_t B, int32_t H, int32_t S, int32_t past_len,
                            float softmax_scale, void* stream);
 
-/* Static name of a status code ("MLA_OK", ...); "unknown status" otherwise. */
+/*
+ * Bytes of device workspace mla_attn_decode_varlen needs for (B, H,
+ * max_seq_len); 0 when no split is needed. A pure function of its arguments.
+ */
+size_t mla_attn_decode_varlen_workspace_bytes(int32_t B, int32_t H, int32_t max_seq_len);
+
+/*
+ * Decode over a preallocated, right-padded key-value cache with a length per
+ * sequence. The "Causal mask" page ("Construct causal mask") hands a 2D
+ * padding mask (1 keeps a position, 0 pads it) with the cached length to the
+ * 4D mask builder, and the "Similarities" page ("Query-key similarity")
+ * appends each new key and value to the cache before the new query attends.
+ * Here sequence b's keys are rows [0, seq_lens[b]) of its cache slices, which
+ * is the 2D mask [1]*len + [0]*(cache_len - len): right padding. The new
+ * query of sequence b sees all of its keys (the new token's own key is its
+ * last one); rows past seq_lens[b] are never read.
+ *
+ *   q_nope        [B, H, 1, 128]        bf16
+ *   q_pe          [B, H, 1, 64]         bf16 (post-RoPE)
+ *   k_nope_cache  [B, H, cache_len, 128] bf16
+ *   k_pe_cache    [B, 1, cache_len, 64]  bf16 (shared rotary key, post-RoPE)
+ *   v_cache       [B, H, cache_len, 128] bf16
+ *   seq_lens      [B] int32 in device memory, 4-byte aligned; read by the
+ *                 kernel (the host never looks at it), so a graph can capture
+ *                 the call and the lengths change between replays
+ *   out           [B, H, 1, 128]        bf16
+ *
+ * max_seq_len (0 <= max_seq_len <= cache_len, else MLA_ERR_SHAPE) bounds the
+ * lengths: each seq_lens[b] is clamped to [0, max_seq_len] on the device, so
+ * no row at or past max_seq_len is read whatever the array holds; the split
+ * plan and the workspace size follow max_seq_len. A sequence whose length is
+ * 0 has no visible key; its output is 0 (the convention for a fully masked
+ * row, where the softmax is undefined). The cache pointers may be NULL only
+ * when cache_len is 0.
+ *
+ * workspace: caller-owned device scratch of at least
+ * mla_attn_decode_varlen_workspace_bytes(B, H, max_seq_len) bytes, 16-byte
+ * aligned (may be NULL when that is 0); contents on entry do not matter.
+ * Calls that may run at the same time must not share a workspace. Other
+ * errors as for mla_attn_decode. One kernel (two for some shapes), as
+ * mla_attn_decode, enqueued on `stream`.
+ */
+mla_status mla_attn_decode_varlen(const void* q_nope, const void* q_pe,
+                                  const void* k_nope_cache, const void* k_pe_cache,
+                                  const void* v_cache, const int32_t* seq_lens,
+                                  void* out, void* workspace, size_t workspace_bytes,
+                                  int32_t B, int32_t H, int32_t cache_len,
+                                  int32_t max_seq_len, float softmax_scale, void* stream);
+
 /*
  * Bytes of device workspace mla_attn_decode_latent needs for (B, H, S); a pure
  * function of its arguments (never 0 for a non-empty call).
@@ -143,6 +191,7 @@ mla_status mla_attn_decode_latent(const void* q_nope, const void* q_pe,
                                   int32_t B, int32_t H, int32_t S, int32_t past_len,
                                   float softmax_scale, void* stream);
 
+/* Static name of a status code ("MLA_OK", ...); "unknown status" otherwise. */
 const char* mla_status_string(mla_status s);
 
 /* Thread-local message for the last failing call on this thread ("" if none). */

@@ -24,6 +24,13 @@ decompressed keys and values have unit variance like the other workloads.
 The weight has no batch index: its stream is the tensor child's first
 grandchild.
 
+Variable-length decode workloads (a preallocated cache of `cap` rows per
+sequence, right-padded) draw the five tensors exactly as a decode workload
+with S = cap, plus one length per sequence from PCG64(SeedSequence([seed,
+1])): integers uniform in [1, cap], the first sequence set to cap so the
+longest sequence fills the cache. The pages give no length mix; a uniform mix
+over the cache stands in for a serving batch.
+
 Device recipe (workloads whose inputs exceed a few GiB of host work, i.e. the
 batched decode): torch.Generator on the device seeded with `seed`, then for
 each tensor in the same order torch.randn(float32) * std rounded to bf16 by
@@ -218,3 +225,32 @@ def device_inputs(wl: Workload, device, seed: int = 0, std: float | None = None)
             del x
         out[name] = t
     return out
+
+
+@dataclass(frozen=True)
+class VarlenWorkload:
+    """Decode over a preallocated cache of `cap` rows per sequence; sequence b
+    uses rows [0, L_b) (right padding)."""
+    name: str
+    B: int
+    H: int
+    cap: int
+    softmax_scale: float = float(np.float32(192.0 ** -0.5))
+
+    def cache(self) -> Workload:
+        """The tensors: a decode workload with S = cap."""
+        return Workload(self.name, self.B, self.H, 1, self.cap - 1)
+
+
+VARLEN_WORKLOADS = {
+    "varlen_batched_decode": VarlenWorkload("varlen_batched_decode", B=32, H=64, cap=8192),
+}
+
+
+def varlen_seq_lens(B: int, cap: int, seed: int = 0) -> np.ndarray:
+    """Lengths [B] int32, uniform in [1, cap], the first one cap."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 1])))
+    lens = g.integers(1, cap + 1, size=B).astype(np.int32)
+    if B:
+        lens[0] = cap
+    return lens

@@ -33,6 +33,7 @@ def test_header_declares_the_boundary():
     assert _declared_functions() == sorted([
         "mla_attn_decode", "mla_attn_decode_workspace_bytes", "mla_attn_prefill",
         "mla_attn_decode_latent", "mla_attn_decode_latent_workspace_bytes",
+        "mla_attn_decode_varlen", "mla_attn_decode_varlen_workspace_bytes",
         "mla_last_error", "mla_status_string"])
 
 
@@ -130,3 +131,40 @@ def test_latent_decode_errors(lib):
     assert "mla_attn_decode_latent" in lib.mla_last_error().decode()
     assert _latent(lib, [None] * 6, None, 0, 0, 64, 1001, 1000) == 0   # empty batch
 
+
+
+def _varlen(lib, ptrs, ws, ws_bytes, B, H, L, M, scale=SC):
+    # ptrs: q_nope, q_pe, k_nope_cache, k_pe_cache, v_cache, seq_lens, out
+    return lib.mla_attn_decode_varlen(*ptrs, ws, ws_bytes, B, H, L, M, scale, None)
+
+
+def test_varlen_decode_errors(lib):
+    need = lib.mla_attn_decode_varlen_workspace_bytes(1, 64, 1001)
+    assert need > 0 and need == lib.mla_attn_decode_workspace_bytes(1, 64, 1001)
+    # B*H fills the chip, but long sequences still split into pieces of <= 1024 keys
+    assert lib.mla_attn_decode_workspace_bytes(32, 64, 8192) == 0
+    assert lib.mla_attn_decode_varlen_workspace_bytes(32, 64, 8192) >= 32 * 64 * 8 * (128 + 4) * 4
+    assert lib.mla_attn_decode_varlen_workspace_bytes(32, 64, 1024) == 0
+    ok = [ALIGNED] * 7
+    assert _varlen(lib, ok, ALIGNED, need, 1, 64, 1000, 1001) == 2        # max_seq_len > cache
+    assert "exceeds the cache length" in lib.mla_last_error().decode()
+    assert _varlen(lib, ok, ALIGNED, need, -1, 64, 1001, 1001) == 2
+    assert _varlen(lib, ok, ALIGNED, need, 1, 64, 1001, -1) == 2
+    for i in range(7):
+        ptrs = list(ok)
+        ptrs[i] = None
+        assert _varlen(lib, ptrs, ALIGNED, need, 1, 64, 2048, 1001) == 1
+        ptrs[i] = MISALIGNED
+        assert _varlen(lib, ptrs, ALIGNED, need, 1, 64, 2048, 1001) == 3
+    # the length array needs only 4-byte alignment: such a call gets past the
+    # alignment checks and stops at the missing workspace
+    ptrs = list(ok)
+    ptrs[5] = ctypes.c_void_p(0x10004)
+    assert _varlen(lib, ptrs, None, need, 1, 64, 2048, 1001) == 5
+    ptrs[5] = ctypes.c_void_p(0x10002)
+    assert _varlen(lib, ptrs, None, need, 1, 64, 2048, 1001) == 3
+    assert _varlen(lib, [None] * 7, None, 0, 0, 64, 2048, 1001) == 0      # empty batch: no-op
+    assert _varlen(lib, ok, None, need, 1, 64, 2048, 1001) == 5
+    assert _varlen(lib, ok, ALIGNED, need - 1, 1, 64, 2048, 1001) == 5
+    assert _varlen(lib, ok, ALIGNED, need, 1, 64, 2048, 1001, 0.0) == 4
+    assert "mla_attn_decode_varlen" in lib.mla_last_error().decode()

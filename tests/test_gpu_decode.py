@@ -126,6 +126,49 @@ def test_back_to_back_calls_share_one_workspace():
     assert np.array_equal(bits[1], bits[3])
 
 
+@pytest.mark.parametrize("B,H,P", [(1, 64, 1000), (1, 5, 1999)])
+def test_graph_replays_with_new_inputs(B, H, P):
+    """A captured decode replayed after its inputs change (copied in between
+    replays, outside the graph) matches an eager call every time: the graph
+    repeats the captured completion tag, so the in-kernel merge must not see
+    flags left by the replay before (first shape: merged in the split kernel;
+    second: by the merge kernel)."""
+    import torch
+    log(f"case decode graph replays B={B} H={H} P={P}")
+    m = _lib()
+    xs = [random_inputs(B, H, 1, P, seed=300 + i) for i in range(3)]
+    ds = [upload(x) for x in xs]
+    d = {k: v.clone() for k, v in ds[0].items()}
+    out = torch.empty((B, H, 1, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(m.mla_attn_decode_workspace_bytes(B, H, P + 1), 16), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        m.mla_attn_decode(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], P, ALPHA,
+                          out=out, workspace=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for i in (1, 2, 0, 1, 2):
+        for k in d:
+            d[k].copy_(ds[i][k])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        replayed = to_host_bits(out).copy()
+        eager = to_host_bits(_gpu_decode(ds[i], P))
+        assert np.array_equal(replayed, eager), f"replay with input set {i}"
+    assert_parity(to_host_f64(out), _oracle(xs[2], P), "decode graph replay")
+
+
 def test_decode_future_independence_and_determinism():
     B, H, P = 1, 4, 1234
     log("case decode determinism")
