@@ -299,6 +299,13 @@ __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
     done = done && (((unsigned long long)hi << 32 | lo) == a.tag);
   }
   if (__any(!done)) return;
+  // Clear this (b, h)'s flags for the next call, before merging so the stores
+  // overlap the merge. A replayed graph repeats the captured tag, so flags
+  // left set would make a replay merge partials of the run before. Every
+  // split of this call has already set its flag (that is why this workgroup
+  // merges), so none is written again in this call; a workgroup still
+  // reading them sees a cleared flag and leaves the merge to this one.
+  for (int sp = lane; sp < a.nsplit; sp += 64) a.ws_flag[(int64_t)bh * a.nsplit + sp] = 0ull;
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   const uint32_t my_xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);
   const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
@@ -341,13 +348,6 @@ __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
       w[e] = (uint32_t)to_bf16_rne(oo[2 * e] * inv) | ((uint32_t)to_bf16_rne(oo[2 * e + 1] * inv) << 16);
     *reinterpret_cast<u32x4*>(dst) = w;
   }
-  // Clear this (b, h)'s flags for the next call. A replayed graph repeats the
-  // captured tag, so flags left set would make a replay merge partials of the
-  // run before. Every split of this call has already set its flag (that is
-  // why this workgroup merged), so none is written again in this call; a
-  // workgroup still reading them sees a cleared flag and leaves the merge to
-  // this one.
-  for (int sp = lane; sp < a.nsplit; sp += 64) a.ws_flag[(int64_t)bh * a.nsplit + sp] = 0ull;
 }
 
 // Log-sum-exp merge of the nsplit partials of each (b, h): one wave per (b, h);

@@ -24,6 +24,11 @@ constexpr int64_t kDecodeKeysPerTrip = 128;
 // Decode split heuristic: aim for this many workgroups (2 per CU on 256 CUs).
 constexpr int64_t kDecodeTargetWorkgroups = 512;
 constexpr int64_t kMaxGrid = 2147483647;  // grid.x limit
+// The prefill and latent kernels address a sequence's keys through buffer
+// resources whose 32-bit byte range must hold S rows of 256 bytes (k_nope, v)
+// or 1024 bytes (latent); longer sequences are refused.
+constexpr int64_t kMaxPrefillKeys = 2147483647 / 256;  // 8,388,607
+constexpr int64_t kMaxLatentKeys = 2147483647 / 1024;  // 2,097,151
 
 struct DecodePlan {
   int64_t nsplit = 1;          // workgroups per (b, h)
@@ -163,6 +168,12 @@ inline CheckResult check_prefill(const void* q_nope, const void* q_pe, const voi
                                  int64_t block_m) {
   CheckResult r = check_common(q_nope, q_pe, k_nope, k_pe, v, out, B, H, T, S, past_len, scale);
   if (r.status != MLA_OK || r.empty) return r;
+  if (S > kMaxPrefillKeys) {
+    std::snprintf(r.msg, sizeof(r.msg), "S=%lld keys exceeds the prefill limit of %lld",
+                  (long long)S, (long long)kMaxPrefillKeys);
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
   const int64_t tiles = (T + block_m - 1) / block_m;
   if (B * H > kMaxGrid / tiles) {
     std::snprintf(r.msg, sizeof(r.msg), "B*H*ceil(T/%lld) = %lld*%lld exceeds the grid limit",
@@ -321,6 +332,12 @@ inline CheckResult check_latent_decode(const void* q_nope, const void* q_pe, con
   CheckResult r =
       check_common(q_nope, q_pe, c_kv, k_pe, w_kv_b, out, B, H, 1, S, past_len, scale, names);
   if (r.status != MLA_OK || r.empty) return r;
+  if (S > kMaxLatentKeys) {
+    std::snprintf(r.msg, sizeof(r.msg), "S=%lld keys exceeds the latent decode limit of %lld",
+                  (long long)S, (long long)kMaxLatentKeys);
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
   if (H % 16 != 0 || H > 64) {
     std::snprintf(r.msg, sizeof(r.msg),
                   "latent decode takes H a multiple of 16 and at most 64 (one wave per 16 heads), "

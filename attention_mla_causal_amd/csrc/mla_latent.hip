@@ -166,9 +166,8 @@ __device__ __forceinline__ int tile_swz(int r) {
 // [S, rowbytes/2] bf16 tensor; rows at or past `end` read as zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* seq, int64_t kb,
                                                            int64_t end, int rowbytes) {
-  // A resource only ever addresses one tile's rows: capping the range at 2^20
-  // rows keeps the byte count inside 32 bits for any sequence length.
-  const int64_t left = end - kb < (int64_t(1) << 20) ? end - kb : (int64_t(1) << 20);
+  // (end * rowbytes < 2^31: the host caps S, so the byte count fits 32 bits)
+  const int64_t left = end - kb;
   const int records = left > 0 ? (int)(left * rowbytes) : 0;
   return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)seq + kb * rowbytes), (short)0,
                                            records, 0x00020000);

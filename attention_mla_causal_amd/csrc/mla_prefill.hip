@@ -79,9 +79,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 // only: scalar instructions.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* slice, int64_t kb,
                                                            int64_t S, int rowbytes) {
-  // A resource only ever addresses one tile's rows: capping the range at 2^20
-  // rows keeps the byte count inside 32 bits for any sequence length.
-  const int64_t left = S - kb < (int64_t(1) << 20) ? S - kb : (int64_t(1) << 20);
+  // (S * rowbytes < 2^31: the host caps S, so the byte count fits 32 bits)
+  const int64_t left = S - kb;
   const int records = left > 0 ? (int)(left * rowbytes) : 0;
   return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)slice + kb * rowbytes), (short)0,
                                            records, 0x00020000);

@@ -66,6 +66,8 @@ typedef enum mla_status {
  * the scores must be (B,H,T,kv_seq_len) and the mask (B,1,T,kv_seq_len) with
  * kv_seq_len = past_len + T; a mismatch is MLA_ERR_SHAPE (ValueError there).
  * The causal mask is generated from indices and never read from memory.
+ * S is at most 8,388,607 (the key rows of a (b, h) slice are addressed
+ * through a 32-bit byte range); longer sequences are MLA_ERR_SHAPE.
  */
 mla_status mla_attn_prefill(const void* q_nope, const void* q_pe,
                             const void* k_nope, const void* k_pe,
@@ -176,7 +178,8 @@ size_t mla_attn_decode_latent_workspace_bytes(int32_t B, int32_t H, int32_t S);
  *                                     rows 256h..256h+127 give head h's key,
  *                                     rows 256h+128..256h+255 its value
  *   out     [B, H, 1, 128]  bf16
- *   S = past_len + 1; H a multiple of 16, at most 64 (else MLA_ERR_SHAPE).
+ *   S = past_len + 1, at most 2,097,151; H a multiple of 16, at most 64
+ *   (else MLA_ERR_SHAPE).
  *
  * workspace: caller-owned device scratch of at least
  * mla_attn_decode_latent_workspace_bytes(B, H, S) bytes, 16-byte aligned;

@@ -33,7 +33,10 @@ int main() {
   EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 16, 20, 5, sc, 128).status == MLA_ERR_SHAPE);
   EXPECT(check_prefill(p, p, p, p, p, p, -1, 4, 16, 16, 0, sc, 128).status == MLA_ERR_SHAPE);
   EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 16, 15, -1, sc, 128).status == MLA_ERR_SHAPE);
-  EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 1, 2147483647LL + 1, 2147483647LL, sc, 128).status == MLA_OK);
+  // S = past_len + T is formed in 64 bits; S is capped so S * 256 bytes fits 32 bits
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 1, 2147483647LL + 1, 2147483647LL, sc, 128).status == MLA_ERR_SHAPE);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 1, 8388607, 8388606, sc, 128).status == MLA_OK);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 4, 1, 8388608, 8388607, sc, 128).status == MLA_ERR_SHAPE);
   EXPECT(check_prefill(p, p, p, p, p, p, 65536, 65536, 2048, 2048, 0, sc, 128).status == MLA_ERR_SHAPE);
   // empty calls are valid no-ops, even with NULL pointers
   {
@@ -95,6 +98,39 @@ int main() {
     EXPECT(check_decode(p, p, p, p, p, p, nullptr, 0, 1, 64, 0, -1, sc, &pl).status == MLA_ERR_SHAPE);
     CheckResult r = check_decode(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 64, 5, 4, sc, &pl);
     EXPECT(r.status == MLA_OK && r.empty);
+  }
+  // variable-length decode: pieces of at most 1024 keys, at most 64 per (b, h)
+  {
+    for (long long M : {0LL, 1LL, 1000LL, 1024LL, 1025LL, 4096LL, 8192LL, 65536LL, 100000LL}) {
+      for (long long bh : {1LL, 48LL, 2048LL}) {
+        const DecodePlan pl = plan_decode_varlen(1, bh, M);
+        const DecodePlan base = plan_decode(1, bh, M);
+        EXPECT(pl.nsplit >= base.nsplit && pl.nsplit <= 64 + base.nsplit);
+        if (M > 0) {
+          EXPECT(pl.keys_per_split % kDecodeKeysPerTrip == 0);
+          EXPECT(pl.keys_per_split * pl.nsplit >= M);
+          EXPECT(pl.keys_per_split * (pl.nsplit - 1) < M);
+          EXPECT(pl.keys_per_split <= 1024 || M > 64 * 1024 || pl.nsplit == base.nsplit);
+        }
+        EXPECT(pl.workspace_bytes == (pl.nsplit > 1 ? pl.ws_o_bytes + pl.ws_ml_bytes + pl.ws_flag_bytes : 0));
+      }
+    }
+    EXPECT(plan_decode_varlen(32, 64, 8192).nsplit == 8);
+    EXPECT(plan_decode_varlen(32, 64, 1024).nsplit == 1);
+    DecodePlan pl;
+    const size_t need = plan_decode_varlen(32, 64, 8192).workspace_bytes;
+    EXPECT(check_decode_varlen(p, p, p, p, p, p, p, p, need, 32, 64, 8192, 8192, sc, &pl).status == MLA_OK);
+    EXPECT(pl.nsplit == 8);
+    EXPECT(check_decode_varlen(p, p, p, p, p, p, p, p, need, 32, 64, 8192, 8193, sc, &pl).status == MLA_ERR_SHAPE);
+    EXPECT(check_decode_varlen(p, p, p, p, p, p, p, p, need - 1, 32, 64, 8192, 8192, sc, &pl).status == MLA_ERR_WORKSPACE);
+    EXPECT(check_decode_varlen(p, p, nullptr, nullptr, nullptr, p, p, nullptr, 0, 2, 8, 0, 0, sc, &pl).status == MLA_OK);
+    EXPECT(check_decode_varlen(p, p, nullptr, p, p, p, p, nullptr, 0, 2, 8, 16, 0, sc, &pl).status == MLA_ERR_NULL);
+  }
+  // latent decode: S limit (1024-byte rows in a 32-bit byte range)
+  {
+    LatentPlan lp;
+    EXPECT(check_latent_decode(p, p, p, p, p, p, p, size_t(1) << 40, 1, 64, 2097151, 2097150, sc, &lp).status == MLA_OK);
+    EXPECT(check_latent_decode(p, p, p, p, p, p, p, size_t(1) << 40, 1, 64, 2097152, 2097151, sc, &lp).status == MLA_ERR_SHAPE);
   }
   if (failures) {
     std::printf("%d failures\n", failures);

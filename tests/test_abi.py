@@ -60,7 +60,8 @@ def _prefill(lib, ptrs, B, H, T, S, P, scale=SC):
 
 
 @pytest.mark.parametrize("B,H,T,S,P", [(1, 4, 16, 17, 0), (1, 4, 16, 20, 5), (-1, 4, 16, 16, 0),
-                                       (1, 4, 16, 15, -1), (1, -2, 3, 3, 0)])
+                                       (1, 4, 16, 15, -1), (1, -2, 3, 3, 0),
+                                       (1, 1, 1, 8388608, 8388607)])   # S beyond the prefill limit
 def test_prefill_shape_errors(lib, B, H, T, S, P):
     assert _prefill(lib, [ALIGNED] * 6, B, H, T, S, P) == 2
     assert "mla_attn_prefill" in lib.mla_last_error().decode()
@@ -114,6 +115,8 @@ def test_latent_decode_errors(lib):
     # shapes: S != past_len + 1, negative sizes, H not a multiple of 16 or above 64
     assert _latent(lib, ok, ALIGNED, need, 1, 64, 1001, 999) == 2
     assert _latent(lib, ok, ALIGNED, need, -1, 64, 1001, 1000) == 2
+    assert _latent(lib, ok, ALIGNED, 1 << 40, 1, 64, 2097152, 2097151) == 2   # S beyond the limit
+    assert "exceeds the latent decode limit" in lib.mla_last_error().decode()
     for H in (8, 24, 80):
         ws = lib.mla_attn_decode_latent_workspace_bytes(1, H, 11)
         assert _latent(lib, ok, ALIGNED, ws, 1, H, 11, 10) == 2
