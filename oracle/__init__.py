@@ -27,3 +27,8 @@ from .mla_varlen import (  # noqa: F401
     mla_decode_varlen,
     mla_decode_varlen_rows,
 )
+from .mla_paged import (  # noqa: F401
+    append_rows,
+    gather_sequence,
+    mla_decode_paged,
+)
