@@ -39,6 +39,9 @@ SIGNATURES = {
     "mla_attn_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_attn_decode_varlen_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "mla_attn_decode_varlen": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _F32, _VP]),
+    "mla_attn_decode_paged_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "mla_attn_decode_paged": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
+                                             _I32, _I32, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_attn_decode_latent_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "mla_attn_decode_latent": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -232,6 +235,81 @@ def mla_attn_decode_varlen(q_nope, q_pe, k_nope_cache, k_pe_cache, v_cache, seq_
     return out
 
 
+def mla_attn_decode_paged_workspace_bytes(B: int, H: int, max_seq_len: int) -> int:
+    """Bytes of device scratch mla_attn_decode_paged needs (0: none)."""
+    return int(_lib.mla_attn_decode_paged_workspace_bytes(int(B), int(H), int(max_seq_len)))
+
+
+def _check_int32(t, name, shape, device):
+    import torch
+    if not (isinstance(t, torch.Tensor) and t.dtype == torch.int32 and t.is_cuda and t.is_contiguous()
+            and tuple(t.shape) == tuple(shape) and t.device == device):
+        raise ValueError(f"{name} must be a contiguous int32 tensor of shape {tuple(shape)} on {device}")
+
+
+def mla_attn_decode_paged(q_nope, q_pe, k_nope_pages, k_pe_pages, v_pages, block_table, seq_lens,
+                          max_seq_len: int, softmax_scale: float, new=None, out=None, workspace=None):
+    """Decode over a paged cache, optionally appending the new token.
+
+    k_nope_pages / v_pages [N, H, bs, 128], k_pe_pages [N, bs, 64] (bs a
+    multiple of 32); block_table int32 [B, M]; seq_lens int32 [B] (keys after
+    the call, clamped on the device to [0, max_seq_len]). new: None or
+    (k_nope_new [B,H,1,128], k_pe_new [B,1,1,64], v_new [B,H,1,128]), attended
+    to as key seq_lens[b]-1 and written into that slot of the pages.
+    Returns out [B,H,1,128] bf16 on the current stream.
+    """
+    import torch
+
+    for t, n in ((q_nope, "q_nope"), (q_pe, "q_pe"), (k_nope_pages, "k_nope_pages"), (v_pages, "v_pages")):
+        _check_tensor(t, n)
+    if not (isinstance(k_pe_pages, torch.Tensor) and k_pe_pages.dtype == torch.bfloat16 and k_pe_pages.is_cuda
+            and k_pe_pages.is_contiguous() and k_pe_pages.dim() == 3):
+        raise ValueError("k_pe_pages must be a contiguous 3D bfloat16 GPU tensor")
+    B, H = q_nope.shape[0], q_nope.shape[1]
+    N, bs = k_pe_pages.shape[0], k_pe_pages.shape[1]
+    want = {"q_nope": (B, H, 1, QK_NOPE_HEAD_DIM), "q_pe": (B, H, 1, QK_ROPE_HEAD_DIM),
+            "k_nope_pages": (N, H, bs, QK_NOPE_HEAD_DIM), "k_pe_pages": (N, bs, QK_ROPE_HEAD_DIM),
+            "v_pages": (N, H, bs, V_HEAD_DIM)}
+    for t, n in ((q_nope, "q_nope"), (q_pe, "q_pe"), (k_nope_pages, "k_nope_pages"),
+                 (k_pe_pages, "k_pe_pages"), (v_pages, "v_pages")):
+        if tuple(t.shape) != want[n] or t.device != q_nope.device:
+            raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {want[n]} on {q_nope.device}")
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be 2D [B, max_blocks]")
+    M = block_table.shape[1]
+    _check_int32(block_table, "block_table", (B, M), q_nope.device)
+    _check_int32(seq_lens, "seq_lens", (B,), q_nope.device)
+    ptr_new = [None, None, None]
+    if new is not None:
+        kn_new, kp_new, v_new = new
+        for t, n, shp in ((kn_new, "k_nope_new", (B, H, 1, QK_NOPE_HEAD_DIM)),
+                          (kp_new, "k_pe_new", (B, 1, 1, QK_ROPE_HEAD_DIM)),
+                          (v_new, "v_new", (B, H, 1, V_HEAD_DIM))):
+            _check_tensor(t, n)
+            if tuple(t.shape) != shp or t.device != q_nope.device:
+                raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {shp}")
+        ptr_new = [kn_new.data_ptr(), kp_new.data_ptr(), v_new.data_ptr()]
+    if out is None:
+        out = torch.empty((B, H, 1, V_HEAD_DIM), dtype=torch.bfloat16, device=q_nope.device)
+    else:
+        _check_tensor(out, "out")
+        if tuple(out.shape) != (B, H, 1, V_HEAD_DIM) or out.device != q_nope.device:
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, 1, V_HEAD_DIM)}")
+    need = mla_attn_decode_paged_workspace_bytes(B, H, max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_nope.device)
+    if not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.mla_attn_decode_paged(
+        q_nope.data_ptr(), q_pe.data_ptr(), k_nope_pages.data_ptr(), k_pe_pages.data_ptr(),
+        v_pages.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), *ptr_new, out.data_ptr(),
+        workspace.data_ptr(), ws_bytes, B, H, N, bs, M, int(max_seq_len), float(softmax_scale),
+        _stream_handle(q_nope.device))
+    _raise_for(st, "mla_attn_decode_paged")
+    return out
+
+
 KV_LORA_RANK = 512
 
 
@@ -288,6 +366,8 @@ def mla_attn_decode_latent(q_nope, q_pe, c_kv, k_pe, w_kv_b, past_len: int, soft
 
 
 __all__ = [
+    "mla_attn_decode_paged",
+    "mla_attn_decode_paged_workspace_bytes",
     "mla_attn_decode_varlen",
     "mla_attn_decode_varlen_workspace_bytes",
     "mla_attn_decode_latent",

@@ -37,14 +37,33 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 namespace {
 
-// Both decode entry points: fill the arguments from a checked plan and launch.
+// Optional parts of a decode call: per-sequence lengths, a paged cache, an
+// appended token.
+struct DecodeExtras {
+  const int32_t* seq_lens = nullptr;
+  const int32_t* block_table = nullptr;
+  int32_t max_blocks = 0, block_size = 0, num_blocks = 0;
+  const void* kn_new = nullptr;
+  const void* kp_new = nullptr;
+  const void* v_new = nullptr;
+};
+
+// Every decode entry point: fill the arguments from a checked plan and launch.
 mla_status launch_decode_call(const char* where, const void* q_nope, const void* q_pe,
                               const void* k_nope, const void* k_pe, const void* v,
-                              const int32_t* seq_lens, void* out, void* workspace,
+                              const DecodeExtras& x, void* out, void* workspace,
                               const mla::DecodePlan& plan, int32_t B, int32_t H, int32_t S,
                               int32_t cap, float softmax_scale, void* stream) {
-  mla::DecodeArgs a;
+  mla::DecodeArgs a{};
+  const int32_t* seq_lens = x.seq_lens;
   a.seq_lens = seq_lens;
+  a.block_table = x.block_table;
+  a.max_blocks = x.max_blocks;
+  a.block_size = x.block_size;
+  a.num_blocks = x.num_blocks;
+  a.kn_new = static_cast<const uint16_t*>(x.kn_new);
+  a.kp_new = static_cast<const uint16_t*>(x.kp_new);
+  a.v_new = static_cast<const uint16_t*>(x.v_new);
   a.cap = cap;
   a.q_nope = static_cast<const uint16_t*>(q_nope);
   a.q_pe = static_cast<const uint16_t*>(q_pe);
@@ -134,8 +153,8 @@ mla_status mla_attn_decode(const void* q_nope, const void* q_pe, const void* k_n
                                                softmax_scale, &plan);
   if (r.status != MLA_OK) return report("mla_attn_decode", r);
   if (r.empty) return MLA_OK;
-  return launch_decode_call("mla_attn_decode", q_nope, q_pe, k_nope, k_pe, v, nullptr, out,
-                            workspace, plan, B, H, S, S, softmax_scale, stream);
+  return launch_decode_call("mla_attn_decode", q_nope, q_pe, k_nope, k_pe, v, DecodeExtras{},
+                            out, workspace, plan, B, H, S, S, softmax_scale, stream);
 }
 
 size_t mla_attn_decode_varlen_workspace_bytes(int32_t B, int32_t H, int32_t max_seq_len) {
@@ -154,9 +173,43 @@ mla_status mla_attn_decode_varlen(const void* q_nope, const void* q_pe, const vo
       B, H, cache_len, max_seq_len, softmax_scale, &plan);
   if (r.status != MLA_OK) return report("mla_attn_decode_varlen", r);
   if (r.empty) return MLA_OK;
+  DecodeExtras x;
+  x.seq_lens = seq_lens;
   return launch_decode_call("mla_attn_decode_varlen", q_nope, q_pe, k_nope_cache, k_pe_cache,
-                            v_cache, seq_lens, out, workspace, plan, B, H, max_seq_len,
-                            cache_len, softmax_scale, stream);
+                            v_cache, x, out, workspace, plan, B, H, max_seq_len, cache_len,
+                            softmax_scale, stream);
+}
+
+size_t mla_attn_decode_paged_workspace_bytes(int32_t B, int32_t H, int32_t max_seq_len) {
+  return mla::plan_decode_varlen(B, H, max_seq_len).workspace_bytes;
+}
+
+mla_status mla_attn_decode_paged(const void* q_nope, const void* q_pe, void* k_nope_pages,
+                                 void* k_pe_pages, void* v_pages, const int32_t* block_table,
+                                 const int32_t* seq_lens, const void* k_nope_new,
+                                 const void* k_pe_new, const void* v_new, void* out,
+                                 void* workspace, size_t workspace_bytes, int32_t B, int32_t H,
+                                 int32_t num_blocks, int32_t block_size, int32_t max_blocks,
+                                 int32_t max_seq_len, float softmax_scale, void* stream) {
+  mla::DecodePlan plan;
+  const mla::CheckResult r = mla::check_decode_paged(
+      q_nope, q_pe, k_nope_pages, k_pe_pages, v_pages, block_table, seq_lens, k_nope_new,
+      k_pe_new, v_new, out, workspace, workspace_bytes, B, H, num_blocks, block_size, max_blocks,
+      max_seq_len, softmax_scale, &plan);
+  if (r.status != MLA_OK) return report("mla_attn_decode_paged", r);
+  if (r.empty) return MLA_OK;
+  DecodeExtras x;
+  x.seq_lens = seq_lens;
+  x.block_table = block_table;
+  x.max_blocks = max_blocks;
+  x.block_size = block_size;
+  x.num_blocks = num_blocks;
+  x.kn_new = k_nope_new;
+  x.kp_new = k_pe_new;
+  x.v_new = v_new;
+  return launch_decode_call("mla_attn_decode_paged", q_nope, q_pe, k_nope_pages, k_pe_pages,
+                            v_pages, x, out, workspace, plan, B, H, max_seq_len, 0,
+                            softmax_scale, stream);
 }
 
 size_t mla_attn_decode_latent_workspace_bytes(int32_t B, int32_t H, int32_t S) {

@@ -3,6 +3,9 @@
 // attends over rows [0, seq_lens[b]) of cache slices of `cap` rows (the 2D
 // padding mask that the "Causal mask" page's "Construct causal mask" hands
 // to the 4D mask builder, for right padding); a sequence with no key gives 0.
+// The cache may be paged (blocks named by a table per sequence), and the new
+// token's key and value may be appended by the call itself (the cache update
+// the "Similarities" page runs before attending).
 //
 // The same computation as prefill with T = 1 (the Kimi K2 "Similarities"
 // page shows it in decode mode with p = 1000: scores [B, 64, 1, 1001]); the
@@ -121,6 +124,7 @@ __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
     split = logical % a.nsplit;
   }
   const int b = bh / a.H;
+  const int h = bh - b * a.H;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -140,6 +144,30 @@ __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
   const uint16_t* kn_g = a.k_nope + (int64_t)bh * cap * DN + 8 * cl;
   const uint16_t* v_g = a.v + (int64_t)bh * cap * DV + 8 * cl;
   const uint16_t* kp_g = a.k_pe + (int64_t)b * cap * DR + 4 * cl;
+  // Paged cache: key j of sequence b is row j % bs of block table[b][j / bs],
+  // blocks [num_blocks, H, bs, 128] (k_nope, v) and [num_blocks, bs, 64]
+  // (k_pe). bs is a multiple of 32, so a wave's 32 keys of one trip share a
+  // block and one scalar table read serves them. Block ids are clamped into
+  // [0, num_blocks) so no id, however bad, addresses outside the pages.
+  const int32_t* table = a.block_table != nullptr ? a.block_table + (int64_t)b * a.max_blocks : nullptr;
+  const int64_t bsz = a.block_size;
+  auto block_of = [&](int64_t key) -> int64_t {
+    int32_t blk = table[key / bsz];
+    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+    return blk;
+  };
+  // Row `key` of this (b, h) in the cache (16 lanes x 8 dims; rotary 16 x 4).
+  auto kn_row = [&](int64_t key) -> const uint16_t* {
+    return table ? a.k_nope + ((block_of(key) * a.H + h) * bsz + key % bsz) * DN + 8 * cl
+                 : kn_g + key * DN;
+  };
+  auto v_row = [&](int64_t key) -> const uint16_t* {
+    return table ? a.v + ((block_of(key) * a.H + h) * bsz + key % bsz) * DV + 8 * cl
+                 : v_g + key * DV;
+  };
+  auto kp_row = [&](int64_t key) -> const uint16_t* {
+    return table ? a.k_pe + (block_of(key) * bsz + key % bsz) * DR + 4 * cl : kp_g + key * DR;
+  };
 
   float qn[8], qp[4];
   {
@@ -159,24 +187,54 @@ __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
 
   const float c = a.scale_log2;
   const int64_t s0 = (int64_t)split * a.keys_per_split;
-  const int64_t s1 = (s0 + a.keys_per_split < S) ? s0 + a.keys_per_split : S;
+  // With an appended token, key S-1 comes from the new rows (never from the
+  // cache, which this call writes); the loop covers keys before it.
+  const bool append = a.kn_new != nullptr && S >= 1;
+  const int64_t S_loop = append ? S - 1 : S;
+  const int64_t s1 = (s0 + a.keys_per_split < S_loop) ? s0 + a.keys_per_split : S_loop;
+  const bool owns_new = append && S - 1 >= s0 && S - 1 < s0 + a.keys_per_split;
 
   float m = -INFINITY, l = 0.0f, o[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = 0.0f;
 
-  for (int64_t base = s0 + wave * KEYS_PER_WAVE; base < s1; base += KEYS_PER_TRIP) {
+  // Block ids of this wave's trips (paged cache): lane t reads the id for
+  // trip t once, and each trip broadcasts it with readlane, so no table read
+  // sits in the loop (trips past the 64th, only for splits longer than 8192
+  // keys, read the table directly).
+  const int64_t base0 = s0 + wave * KEYS_PER_WAVE;
+  int32_t blk_lane = 0;
+  if (table != nullptr) {
+    const int64_t kb = base0 + (int64_t)KEYS_PER_TRIP * lane;
+    if (kb < s1) blk_lane = (int32_t)block_of(kb);
+  }
+  int trip = 0;
+  for (int64_t base = base0; base < s1; base += KEYS_PER_TRIP, ++trip) {
     u32x4 kn[KEYS_PER_LANE], vv[KEYS_PER_LANE];
     u32x2 kp[KEYS_PER_LANE];
     bool ok[KEYS_PER_LANE];
+    const uint16_t* kn_t;  // rows base .. base+31 are consecutive
+    const uint16_t* v_t;
+    const uint16_t* kp_t;
+    if (table != nullptr) {
+      const int64_t blk = trip < 64 ? __builtin_amdgcn_readlane(blk_lane, trip) : block_of(base);
+      const int64_t r0 = base % bsz;
+      kn_t = a.k_nope + ((blk * a.H + h) * bsz + r0) * DN + 8 * cl;
+      v_t = a.v + ((blk * a.H + h) * bsz + r0) * DV + 8 * cl;
+      kp_t = a.k_pe + (blk * bsz + r0) * DR + 4 * cl;
+    } else {
+      kn_t = kn_g + base * DN;
+      v_t = v_g + base * DV;
+      kp_t = kp_g + base * DR;
+    }
 #pragma unroll
     for (int u = 0; u < KEYS_PER_LANE; ++u) {
       const int64_t key = base + 4 * u + qq;
       ok[u] = key < s1;
       if (ok[u]) {
-        kn[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kn_g + key * DN));
-        kp[u] = *reinterpret_cast<const u32x2*>(kp_g + key * DR);
-        vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_g + key * DV));
+        kn[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kn_t + (4 * u + qq) * DN));
+        kp[u] = *reinterpret_cast<const u32x2*>(kp_t + (4 * u + qq) * DR);
+        vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_t + (4 * u + qq) * DV));
       } else {
         kn[u] = u32x4{0, 0, 0, 0};
         kp[u] = u32x2{0, 0};
@@ -220,6 +278,42 @@ __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
         o[2 * e + 1] = __builtin_fmaf(p, hi_bf16(vv[u][e]), o[2 * e + 1]);
       }
     }
+  }
+
+  // ---- the appended token (key S-1): the split that owns it takes it from
+  // the new rows in quarter-wave 0 of wave 0, which also writes the rows into
+  // the cache (the rotary row by head 0 only: it is shared by the heads, and
+  // every head reads key S-1 from the new rows, so no one reads that slot).
+  if (owns_new && wave == 0 && qq == 0) {
+    const u32x4 kw = *reinterpret_cast<const u32x4*>(a.kn_new + (int64_t)bh * DN + 8 * cl);
+    const u32x2 pw = *reinterpret_cast<const u32x2*>(a.kp_new + (int64_t)b * DR + 4 * cl);
+    const u32x4 vw = *reinterpret_cast<const u32x4*>(a.v_new + (int64_t)bh * DV + 8 * cl);
+    float d = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      d = __builtin_fmaf(qn[2 * e], lo_bf16(kw[e]), d);
+      d = __builtin_fmaf(qn[2 * e + 1], hi_bf16(kw[e]), d);
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      d = __builtin_fmaf(qp[2 * e], lo_bf16(pw[e]), d);
+      d = __builtin_fmaf(qp[2 * e + 1], hi_bf16(pw[e]), d);
+    }
+    const float t = row_sum16(d) * c;
+    const float m_new = fmaxf(m, t);
+    const float alpha = rescale(m, m_new);
+    const float p = __builtin_amdgcn_exp2f(t - m_new);
+    l = l * alpha + p;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[2 * e] = __builtin_fmaf(p, lo_bf16(vw[e]), o[2 * e] * alpha);
+      o[2 * e + 1] = __builtin_fmaf(p, hi_bf16(vw[e]), o[2 * e + 1] * alpha);
+    }
+    m = m_new;
+    const int64_t key = S - 1;
+    *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(kn_row(key))) = kw;
+    *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(v_row(key))) = vw;
+    if (h == 0) *reinterpret_cast<u32x2*>(const_cast<uint16_t*>(kp_row(key))) = pw;
   }
 
   // ---- merge the four quarter-waves, then the waves

@@ -286,6 +286,102 @@ inline CheckResult check_decode_varlen(const void* q_nope, const void* q_pe, con
   return r;
 }
 
+// ---- decode over a paged cache, optionally appending the new token
+constexpr int64_t kPagedBlockMultiple = 32;  // a wave's 32 keys of one trip share a block
+
+inline CheckResult check_decode_paged(const void* q_nope, const void* q_pe, const void* k_nope,
+                                      const void* k_pe, const void* v, const void* block_table,
+                                      const void* seq_lens, const void* kn_new,
+                                      const void* kp_new, const void* v_new, const void* out,
+                                      const void* workspace, size_t workspace_bytes, int64_t B,
+                                      int64_t H, int64_t num_blocks, int64_t block_size,
+                                      int64_t max_blocks, int64_t max_len, float scale,
+                                      DecodePlan* plan_out) {
+  CheckResult r;
+  if (B < 0 || H < 0 || num_blocks < 0 || block_size < 0 || max_blocks < 0 || max_len < 0) {
+    std::snprintf(r.msg, sizeof(r.msg),
+                  "negative size: B=%lld H=%lld num_blocks=%lld block_size=%lld max_blocks=%lld "
+                  "max_seq_len=%lld",
+                  (long long)B, (long long)H, (long long)num_blocks, (long long)block_size,
+                  (long long)max_blocks, (long long)max_len);
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  if (B == 0 || H == 0) {
+    r.empty = true;
+    return r;
+  }
+  if (block_size == 0 || block_size % kPagedBlockMultiple != 0) {
+    std::snprintf(r.msg, sizeof(r.msg), "block_size %lld must be a positive multiple of %lld",
+                  (long long)block_size, (long long)kPagedBlockMultiple);
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  if (num_blocks < 1 || max_len > max_blocks * block_size) {
+    std::snprintf(r.msg, sizeof(r.msg),
+                  "max_seq_len %lld needs max_blocks * block_size >= it and at least one block "
+                  "(max_blocks=%lld, block_size=%lld, num_blocks=%lld)",
+                  (long long)max_len, (long long)max_blocks, (long long)block_size,
+                  (long long)num_blocks);
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  const int nnew = (kn_new != nullptr) + (kp_new != nullptr) + (v_new != nullptr);
+  if (nnew != 0 && nnew != 3) {
+    std::snprintf(r.msg, sizeof(r.msg),
+                  "append takes all of k_nope_new, k_pe_new and v_new, or none (%d given)", nnew);
+    r.status = MLA_ERR_NULL;
+    return r;
+  }
+  const void* ptrs[11] = {q_nope, q_pe, k_nope, k_pe, v, block_table, seq_lens, out,
+                          kn_new, kp_new, v_new};
+  static const char* const names[11] = {"q_nope", "q_pe", "k_nope_pages", "k_pe_pages",
+                                        "v_pages", "block_table", "seq_lens", "out",
+                                        "k_nope_new", "k_pe_new", "v_new"};
+  for (int i = 0; i < 11; ++i) {
+    if (ptrs[i] == nullptr && i < 8) {
+      std::snprintf(r.msg, sizeof(r.msg), "%s is NULL", names[i]);
+      r.status = MLA_ERR_NULL;
+      return r;
+    }
+    const uintptr_t align = (i == 5 || i == 6) ? 4u : 16u;
+    if ((reinterpret_cast<uintptr_t>(ptrs[i]) & (align - 1)) != 0) {
+      std::snprintf(r.msg, sizeof(r.msg), "%s is not %u-byte aligned", names[i], (unsigned)align);
+      r.status = MLA_ERR_ALIGN;
+      return r;
+    }
+  }
+  const float c = scale * 1.4426950408889634f;
+  if (!std::isfinite(scale) || !(scale > 0.0f) || !std::isfinite(c)) {
+    std::snprintf(r.msg, sizeof(r.msg), "softmax_scale %g must be finite and positive",
+                  (double)scale);
+    r.status = MLA_ERR_SCALE;
+    return r;
+  }
+  const DecodePlan plan = plan_decode_varlen(B, H, max_len);
+  if (B * H > kMaxGrid / plan.nsplit) {
+    std::snprintf(r.msg, sizeof(r.msg), "B*H*nsplit exceeds the grid limit");
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  if (plan.workspace_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) {
+      std::snprintf(r.msg, sizeof(r.msg), "workspace %s: %zu bytes given, %zu needed",
+                    workspace == nullptr ? "is NULL" : "too small", workspace_bytes,
+                    plan.workspace_bytes);
+      r.status = MLA_ERR_WORKSPACE;
+      return r;
+    }
+    if (misaligned(workspace)) {
+      std::snprintf(r.msg, sizeof(r.msg), "workspace is not 16-byte aligned");
+      r.status = MLA_ERR_ALIGN;
+      return r;
+    }
+  }
+  if (plan_out) *plan_out = plan;
+  return r;
+}
+
 // ---- decode over the compressed latent cache
 constexpr int64_t kLatentRank = 512;             // kv_lora_rank
 constexpr int64_t kLatentKeyWidth = 512 + 64;    // latent + shared rotary key, per key

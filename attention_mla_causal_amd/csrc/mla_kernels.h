@@ -26,6 +26,11 @@ struct DecodeArgs {
   const uint16_t* k_pe;    // [B,1,cap,64]
   const uint16_t* v;       // [B,H,cap,128]
   const int32_t* seq_lens; // [B] keys per sequence (rows [0, len) of the cache), or null: S each
+  const int32_t* block_table;  // [B, max_blocks] paged cache (k_nope/v [num_blocks,H,bs,128],
+                               // k_pe [num_blocks,bs,64]), or null: contiguous cache
+  const uint16_t* kn_new;  // appended token [B,H,1,128] (key seq_lens[b]-1), or null: no append
+  const uint16_t* kp_new;  // [B,1,1,64]
+  const uint16_t* v_new;   // [B,H,1,128]
   uint16_t* out;           // [B,H,1,128]
   float* ws_o;             // [B*H, nsplit, 128] partial outputs (nsplit > 1)
   float* ws_ml;            // [B*H, nsplit, 4] partial (max, sum, XCD id, unused)
@@ -33,6 +38,7 @@ struct DecodeArgs {
   unsigned long long tag;  // this call's tag
   int32_t B, H, S;         // S: keys per sequence, or the bound lengths are clamped to
   int32_t cap;             // cache rows per (b, h) slice (= S without seq_lens)
+  int32_t max_blocks, block_size, num_blocks;  // paged cache geometry
   int32_t nsplit, keys_per_split;
   int32_t fused;           // the last workgroup of each (b, h) merges the partials
   int32_t interleave;      // (b, h) -> XCD (b*H + h) % 8 (needs B*H % 8 == 0); else by sequence

@@ -33,8 +33,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from seeded_inputs import (LATENT_WORKLOADS, VARLEN_WORKLOADS, WORKLOADS, device_inputs,  # noqa: E402
-                           host_inputs, latent_device_inputs, latent_host_inputs, varlen_seq_lens)
+from seeded_inputs import (LATENT_WORKLOADS, PAGED_WORKLOADS, VARLEN_WORKLOADS, WORKLOADS,  # noqa: E402
+                           device_inputs, host_inputs, latent_device_inputs, latent_host_inputs,
+                           paged_device_inputs, paged_layout, varlen_seq_lens)
 
 METRIC = "prefill attn TFLOP/s & decode HBM GB/s, 1 MI355X, as fraction of peak"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
@@ -63,6 +64,16 @@ def varlen_bytes(wl, lens) -> int:
     H = wl.H
     L = int(np.asarray(lens, dtype=np.int64).sum())
     return H * L * (128 + 128) * 2 + L * 64 * 2 + wl.B * H * (192 + 128) * 2
+
+
+def paged_bytes(wl, lens) -> int:
+    """Paged decode with append: cached keys before the new one (k_nope + v per
+    head, the shared rotary key once), the new rows read and written once,
+    queries and output."""
+    H, B = wl.H, wl.B
+    L = int((np.asarray(lens, dtype=np.int64) - 1).clip(min=0).sum())
+    row = H * (128 + 128) * 2 + 64 * 2
+    return L * row + 2 * B * row + B * H * (192 + 128) * 2
 
 
 def latent_bytes(wl) -> int:
@@ -262,6 +273,51 @@ def run_varlen(wl, steps, warmup, seed=0, graph=True):
     return res
 
 
+def run_paged(wl, steps, warmup, seed=0, graph=True):
+    """mla_attn_decode_paged with append on a shuffled block layout (inputs
+    drawn on the device; every step appends the same rows to the same slots)."""
+    import torch
+    import attention_mla_causal_amd as mla
+    dev = torch.device("cuda:0")
+    lens = varlen_seq_lens(wl.B, wl.cap, seed=seed)
+    table, nblocks = paged_layout(lens, wl.block_size, seed=seed)
+    nbytes = paged_bytes(wl, lens)
+    log(f"[bench] {wl.name}: B={wl.B} H={wl.H} block_size={wl.block_size} blocks={nblocks} "
+        f"sum(lens)={int(lens.sum())} steps={steps}")
+    d = paged_device_inputs(wl.B, wl.H, nblocks, wl.block_size, dev, seed=seed)
+    tb = torch.as_tensor(table, device=dev)
+    sl = torch.as_tensor(lens, device=dev)
+    out = torch.empty((wl.B, wl.H, 1, 128), dtype=torch.bfloat16, device=dev)
+    need = mla.mla_attn_decode_paged_workspace_bytes(wl.B, wl.H, wl.cap)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+    new = (d["k_nope_new"], d["k_pe_new"], d["v_new"])
+
+    def step(i):
+        mla.mla_attn_decode_paged(d["q_nope"], d["q_pe"], d["k_nope_pages"], d["k_pe_pages"],
+                                  d["v_pages"], tb, sl, wl.cap, wl.softmax_scale, new=new, out=out,
+                                  workspace=ws)
+
+    if graph:
+        ms, wall_ms = time_graph(step, steps, warmup)
+    else:
+        ms, wall_ms = time_eager(step, steps, warmup)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    kernel = "mla_decode_kernel"
+    res = {
+        "workload": wl.name, "B": wl.B, "H": wl.H, "T": 1, "block_size": wl.block_size,
+        "num_blocks": nblocks, "sum_seq_lens": int(lens.sum()), "append": True, "inputs": "device",
+        "steps": steps, "timing": "hip_graph" if graph else "eager",
+        "ms_per_step": ms, "wall_ms_per_step": wall_ms, "value": gbs, "unit": "GB/s",
+        "algorithmic_bytes": nbytes,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(kernel, wl.name)},
+    }
+    del d
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_latent(wl, steps, warmup, seed=0, copies=None, graph=True):
     """mla_attn_decode_latent, graph-timed (or eager) over rotating input copies (weights too)."""
     import torch
@@ -405,7 +461,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_p1000",
-                    choices=sorted(WORKLOADS) + sorted(LATENT_WORKLOADS) + sorted(VARLEN_WORKLOADS))
+                    choices=sorted(WORKLOADS) + sorted(LATENT_WORKLOADS) + sorted(VARLEN_WORKLOADS)
+                    + sorted(PAGED_WORKLOADS))
     ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -440,7 +497,11 @@ def main():
         sys.exit(2)
 
     torch.cuda.synchronize()
-    if args.workload in VARLEN_WORKLOADS:
+    if args.workload in PAGED_WORKLOADS:
+        wl = PAGED_WORKLOADS[args.workload]
+        head = run_paged(wl, args.steps, args.warmup, graph=not args.eager)
+        cpu = None
+    elif args.workload in VARLEN_WORKLOADS:
         wl = VARLEN_WORKLOADS[args.workload]
         head = run_varlen(wl, args.steps, args.warmup, graph=not args.eager)
         cpu = None
@@ -475,6 +536,9 @@ def main():
         for name, w in VARLEN_WORKLOADS.items():
             if name != wl.name:
                 workloads[name] = run_varlen(w, args.extra_steps, 3)
+        for name, w in PAGED_WORKLOADS.items():
+            if name != wl.name:
+                workloads[name] = run_paged(w, args.extra_steps, 3)
         for name, w in LATENT_WORKLOADS.items():
             if name == wl.name:
                 continue

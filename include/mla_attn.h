@@ -156,6 +156,58 @@ mla_status mla_attn_decode_varlen(const void* q_nope, const void* q_pe,
                                   int32_t max_seq_len, float softmax_scale, void* stream);
 
 /*
+ * Bytes of device workspace mla_attn_decode_paged needs for (B, H,
+ * max_seq_len); 0 when no split is needed. A pure function of its arguments.
+ */
+size_t mla_attn_decode_paged_workspace_bytes(int32_t B, int32_t H, int32_t max_seq_len);
+
+/*
+ * Decode over a paged key-value cache, optionally appending the new token.
+ * The pages keep one growing cache per layer and append each new key and
+ * value to it before the new query attends ("Similarities" page, "Query-key
+ * similarity"); here the cache is stored in fixed blocks named by a table.
+ * Sequence b's key j is row j % block_size of block block_table[b * max_blocks
+ * + j / block_size]:
+ *
+ *   k_nope_pages  [num_blocks, H, block_size, 128]  bf16
+ *   k_pe_pages    [num_blocks, block_size, 64]      bf16 (shared rotary key)
+ *   v_pages       [num_blocks, H, block_size, 128]  bf16
+ *   block_table   [B, max_blocks] int32, device memory, 4-byte aligned
+ *   seq_lens      [B] int32, device memory: keys of sequence b after the call
+ *   q_nope [B, H, 1, 128], q_pe [B, H, 1, 64], out [B, H, 1, 128]  bf16
+ *
+ * block_size is a positive multiple of 32 (else MLA_ERR_SHAPE); max_seq_len
+ * <= max_blocks * block_size (else MLA_ERR_SHAPE) bounds every length, each
+ * clamped on the device to [0, max_seq_len]; block ids read from the table
+ * are clamped on the device to [0, num_blocks). Rows past a sequence's length
+ * are never read; a sequence of length 0 gives a zero row.
+ *
+ * Append: k_nope_new [B, H, 1, 128], k_pe_new [B, 1, 1, 64], v_new
+ * [B, H, 1, 128] (all three, or all NULL: MLA_ERR_NULL otherwise). When given,
+ * the new token is key seq_lens[b] - 1 of sequence b: the call attends to it
+ * from these tensors and writes them into that slot of the pages (each head's
+ * rows by that head's workgroup, the shared rotary row once), so the pages
+ * hold the appended token when the call completes. The slot's block must
+ * belong to sequence b alone. Without them the pages are only read.
+ *
+ * workspace: at least mla_attn_decode_paged_workspace_bytes(B, H,
+ * max_seq_len) bytes, 16-byte aligned (may be NULL when that is 0); contents
+ * on entry do not matter. Calls that may run at the same time must not share
+ * a workspace. The host reads neither the table nor the lengths, so a graph
+ * can capture the call and both change between replays. Other errors as for
+ * mla_attn_decode.
+ */
+mla_status mla_attn_decode_paged(const void* q_nope, const void* q_pe,
+                                 void* k_nope_pages, void* k_pe_pages, void* v_pages,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const void* k_nope_new, const void* k_pe_new,
+                                 const void* v_new, void* out,
+                                 void* workspace, size_t workspace_bytes,
+                                 int32_t B, int32_t H, int32_t num_blocks, int32_t block_size,
+                                 int32_t max_blocks, int32_t max_seq_len, float softmax_scale,
+                                 void* stream);
+
+/*
  * Bytes of device workspace mla_attn_decode_latent needs for (B, H, S); a pure
  * function of its arguments (never 0 for a non-empty call).
  */

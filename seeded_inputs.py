@@ -31,6 +31,14 @@ with S = cap, plus one length per sequence from PCG64(SeedSequence([seed,
 longest sequence fills the cache. The pages give no length mix; a uniform mix
 over the cache stands in for a serving batch.
 
+Paged-cache decode (blocks of `block_size` rows named by a table per
+sequence): the tensors q_nope, q_pe, k_nope_pages [N,H,bs,128], k_pe_pages
+[N,bs,64], v_pages [N,H,bs,128] and the appended token's k_nope_new,
+k_pe_new, v_new are drawn in that order, one SeedSequence child each
+(standard normal, bf16); the block layout gives sequence b ceil(L_b / bs)
+blocks taken in order from a PCG64(SeedSequence([seed, 2])) permutation of
+all blocks, table entries past a sequence's blocks left at 0.
+
 Device recipe (workloads whose inputs exceed a few GiB of host work, i.e. the
 batched decode): torch.Generator on the device seeded with `seed`, then for
 each tensor in the same order torch.randn(float32) * std rounded to bf16 by
@@ -254,3 +262,75 @@ def varlen_seq_lens(B: int, cap: int, seed: int = 0) -> np.ndarray:
     if B:
         lens[0] = cap
     return lens
+
+
+PAGED_TENSORS = ("q_nope", "q_pe", "k_nope_pages", "k_pe_pages", "v_pages",
+                 "k_nope_new", "k_pe_new", "v_new")
+
+
+def paged_layout(lens, block_size: int, seed: int = 0, spare: int = 0):
+    """(block_table int32 [B, max_blocks], num_blocks): sequence b owns
+    ceil(L_b / block_size) blocks, taken in order from a seeded permutation of
+    all num_blocks = (sum of those) + spare blocks."""
+    lens = np.asarray(lens, dtype=np.int64)
+    need = [int(-(-L // block_size)) for L in lens]
+    num_blocks = max(sum(need) + spare, 1)
+    M = max(max(need) if need else 0, 1)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 2])))
+    perm = g.permutation(num_blocks)
+    table = np.zeros((len(lens), M), dtype=np.int32)
+    k = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[k:k + n]
+        k += n
+    return table, num_blocks
+
+
+def paged_shapes(B: int, H: int, num_blocks: int, block_size: int) -> dict:
+    return {"q_nope": (B, H, 1, NOPE), "q_pe": (B, H, 1, ROPE),
+            "k_nope_pages": (num_blocks, H, block_size, NOPE),
+            "k_pe_pages": (num_blocks, block_size, ROPE),
+            "v_pages": (num_blocks, H, block_size, VDIM),
+            "k_nope_new": (B, H, 1, NOPE), "k_pe_new": (B, 1, 1, ROPE), "v_new": (B, H, 1, VDIM)}
+
+
+def paged_host_inputs(B: int, H: int, num_blocks: int, block_size: int, seed: int = 0) -> dict:
+    """The eight paged-decode tensors as uint16 bf16 bit arrays (host recipe)."""
+    kids = np.random.SeedSequence(seed).spawn(len(PAGED_TENSORS))
+    out = {}
+    for name, shape in paged_shapes(B, H, num_blocks, block_size).items():
+        g = np.random.Generator(np.random.PCG64(kids[PAGED_TENSORS.index(name)]))
+        out[name] = f32_to_bf16_bits(g.standard_normal(shape, dtype=np.float32))
+    return out
+
+
+def paged_device_inputs(B: int, H: int, num_blocks: int, block_size: int, device, seed: int = 0) -> dict:
+    """The eight paged-decode tensors drawn on a torch device (device recipe)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = {}
+    for name, shape in paged_shapes(B, H, num_blocks, block_size).items():
+        t = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        for i in range(shape[0]):
+            t[i].copy_(torch.randn(shape[1:], generator=g, dtype=torch.float32, device=device))
+        out[name] = t
+    return out
+
+
+@dataclass(frozen=True)
+class PagedWorkload:
+    """Decode with append over a paged cache: lengths as the variable-length
+    workload (uniform in [1, cap], first at cap), blocks of block_size rows."""
+    name: str
+    B: int
+    H: int
+    cap: int
+    block_size: int
+    softmax_scale: float = float(np.float32(192.0 ** -0.5))
+
+
+PAGED_WORKLOADS = {
+    "paged_batched_decode": PagedWorkload("paged_batched_decode", B=32, H=64, cap=8192, block_size=64),
+}

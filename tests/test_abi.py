@@ -34,6 +34,7 @@ def test_header_declares_the_boundary():
         "mla_attn_decode", "mla_attn_decode_workspace_bytes", "mla_attn_prefill",
         "mla_attn_decode_latent", "mla_attn_decode_latent_workspace_bytes",
         "mla_attn_decode_varlen", "mla_attn_decode_varlen_workspace_bytes",
+        "mla_attn_decode_paged", "mla_attn_decode_paged_workspace_bytes",
         "mla_last_error", "mla_status_string"])
 
 
@@ -171,3 +172,39 @@ def test_varlen_decode_errors(lib):
     assert _varlen(lib, ok, ALIGNED, need - 1, 1, 64, 2048, 1001) == 5
     assert _varlen(lib, ok, ALIGNED, need, 1, 64, 2048, 1001, 0.0) == 4
     assert "mla_attn_decode_varlen" in lib.mla_last_error().decode()
+
+
+def _paged(lib, ptrs, new, ws, ws_bytes, B, H, N, bs, M, L, scale=SC):
+    # ptrs: q_nope, q_pe, k_nope_pages, k_pe_pages, v_pages, block_table, seq_lens; then out
+    return lib.mla_attn_decode_paged(*ptrs, *new, ALIGNED, ws, ws_bytes, B, H, N, bs, M, L, scale, None)
+
+
+def test_paged_decode_errors(lib):
+    need = lib.mla_attn_decode_paged_workspace_bytes(4, 64, 4096)
+    assert need == lib.mla_attn_decode_varlen_workspace_bytes(4, 64, 4096) and need > 0
+    ok = [ALIGNED] * 7
+    none3 = [None] * 3
+    all3 = [ALIGNED] * 3
+    # block_size must be a positive multiple of 32; lengths must fit the table
+    for bs in (0, 16, 48):
+        assert _paged(lib, ok, none3, ALIGNED, need, 4, 64, 100, bs, 64, 1024) == 2
+    assert _paged(lib, ok, none3, ALIGNED, need, 4, 64, 100, 64, 63, 4096) == 2   # 63*64 < 4096
+    assert _paged(lib, ok, none3, ALIGNED, need, 4, 64, 0, 64, 64, 4096) == 2     # no blocks
+    assert _paged(lib, ok, none3, ALIGNED, need, -1, 64, 100, 64, 64, 4096) == 2
+    # append needs all three new tensors
+    assert _paged(lib, ok, [ALIGNED, None, None], ALIGNED, need, 4, 64, 100, 64, 64, 4096) == 1
+    assert "append takes all" in lib.mla_last_error().decode()
+    for i in range(7):
+        ptrs = list(ok)
+        ptrs[i] = None
+        assert _paged(lib, ptrs, none3, ALIGNED, need, 4, 64, 100, 64, 64, 4096) == 1
+        ptrs[i] = MISALIGNED
+        assert _paged(lib, ptrs, none3, ALIGNED, need, 4, 64, 100, 64, 64, 4096) == 3
+    for i in range(3):
+        new = list(all3)
+        new[i] = MISALIGNED
+        assert _paged(lib, ok, new, ALIGNED, need, 4, 64, 100, 64, 64, 4096) == 3
+    assert _paged(lib, ok, all3, None, need, 4, 64, 100, 64, 64, 4096) == 5
+    assert _paged(lib, ok, all3, ALIGNED, need, 4, 64, 100, 64, 64, 4096, float("inf")) == 4
+    assert _paged(lib, [None] * 7, none3, None, 0, 0, 64, 0, 0, 0, 0) == 0       # empty batch: no-op
+    assert "mla_attn_decode_paged" in lib.mla_last_error().decode()
