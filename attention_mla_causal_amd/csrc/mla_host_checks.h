@@ -434,10 +434,9 @@ inline CheckResult check_latent_decode(const void* q_nope, const void* q_pe, con
     r.status = MLA_ERR_SHAPE;
     return r;
   }
-  if (H % 16 != 0 || H > 64) {
+  if (H > 64) {
     std::snprintf(r.msg, sizeof(r.msg),
-                  "latent decode takes H a multiple of 16 and at most 64 (one wave per 16 heads), "
-                  "got H=%lld",
+                  "latent decode takes at most 64 heads (one 64-column MFMA tile), got H=%lld",
                   (long long)H);
     r.status = MLA_ERR_SHAPE;
     return r;

@@ -174,8 +174,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* seq,
 }
 
 // ---- 2. attention over the latent keys of one key split
-// Workgroup: one (batch, key split), four waves, always 64 head columns (heads
-// at or past H get zero queries and are never stored). Phase p of the loop
+// Workgroup: one (batch, key split), four waves, always 64 head columns (any
+// H up to 64; columns at or past H get zero queries and are never stored). Phase p of the loop
 // does two independent jobs in one straight run of code:
 //   * scores of tile p for heads 16w .. 16w+15 (wave w), the online-softmax
 //     update of their max and sum, and their probabilities, which go to LDS
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
   // absorbed queries of heads 16w + j (B operand): lane (g, j) holds dims
   // 32 ks + 8 g .. + 8; zero for heads at or past H
   bf16x8 qf[KSTEPS];
-  if (16 * wave < H) {
+  if (16 * wave + j < H) {
     const uint16_t* q = a.qt + ((int64_t)b * H + 16 * wave + j) * KW + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(q + 32 * ks);
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
   const int64_t row0 = ((int64_t)b * a.nsplit + split) * H;
 #pragma unroll
   for (int hg = 0; hg < NWAVE; ++hg) {
-    if (16 * hg < H) {
+    if (16 * hg + j < H) {
       float* po = a.po + (row0 + 16 * hg + j) * R + 128 * wave + 4 * g;
 #pragma unroll
       for (int d = 0; d < NDTW; ++d) *reinterpret_cast<f32x4*>(po + 16 * d) = o[hg * NDTW + d];
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
   }
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  if (16 * wave < H && g == 0) {
+  if (16 * wave + j < H && g == 0) {
     const int64_t row = row0 + 16 * wave + j;
     a.pml[2 * row] = m_run;
     a.pml[2 * row + 1] = l_tot;

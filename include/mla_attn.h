@@ -230,8 +230,7 @@ size_t mla_attn_decode_latent_workspace_bytes(int32_t B, int32_t H, int32_t S);
  *                                     rows 256h..256h+127 give head h's key,
  *                                     rows 256h+128..256h+255 its value
  *   out     [B, H, 1, 128]  bf16
- *   S = past_len + 1, at most 2,097,151; H a multiple of 16, at most 64
- *   (else MLA_ERR_SHAPE).
+ *   S = past_len + 1, at most 2,097,151; H at most 64 (else MLA_ERR_SHAPE).
  *
  * workspace: caller-owned device scratch of at least
  * mla_attn_decode_latent_workspace_bytes(B, H, S) bytes, 16-byte aligned;

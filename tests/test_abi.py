@@ -113,15 +113,15 @@ def test_latent_decode_errors(lib):
     need = lib.mla_attn_decode_latent_workspace_bytes(1, 64, 1001)
     assert need > 0 and need % 256 == 0
     ok = [ALIGNED] * 6
-    # shapes: S != past_len + 1, negative sizes, H not a multiple of 16 or above 64
+    # shapes: S != past_len + 1, negative sizes, H above 64
     assert _latent(lib, ok, ALIGNED, need, 1, 64, 1001, 999) == 2
     assert _latent(lib, ok, ALIGNED, need, -1, 64, 1001, 1000) == 2
     assert _latent(lib, ok, ALIGNED, 1 << 40, 1, 64, 2097152, 2097151) == 2   # S beyond the limit
     assert "exceeds the latent decode limit" in lib.mla_last_error().decode()
-    for H in (8, 24, 80):
+    for H in (65, 80):
         ws = lib.mla_attn_decode_latent_workspace_bytes(1, H, 11)
         assert _latent(lib, ok, ALIGNED, ws, 1, H, 11, 10) == 2
-    assert "multiple of 16" in lib.mla_last_error().decode()
+    assert "at most 64 heads" in lib.mla_last_error().decode()
     for i in range(6):
         ptrs = list(ok)
         ptrs[i] = None
