@@ -33,7 +33,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from seeded_inputs import (LATENT_WORKLOADS, PAGED_WORKLOADS, VARLEN_WORKLOADS, WORKLOADS,  # noqa: E402
+from seeded_inputs import (LATENT_WORKLOADS, PAGED_WORKLOADS, SHARD_WORKLOADS, VARLEN_WORKLOADS,  # noqa: E402
+                           WORKLOADS,
                            device_inputs, host_inputs, latent_device_inputs, latent_host_inputs,
                            paged_device_inputs, paged_layout, varlen_seq_lens)
 
@@ -533,6 +534,12 @@ def main():
                     r["cpu_baseline"] = cpu_baseline_prefill(w, x, min(args.cpu_seconds, 5.0))
                 del x
             workloads[name] = r
+        for name, w in SHARD_WORKLOADS.items():  # one GPU's share of 64 heads over 8 GPUs
+            if w.T == 1:
+                workloads[name] = run_decode(w, args.extra_steps, 3)
+            else:
+                workloads[name], x = run_prefill(w, args.extra_steps, 2)
+                del x
         for name, w in VARLEN_WORKLOADS.items():
             if name != wl.name:
                 workloads[name] = run_varlen(w, args.extra_steps, 3)

@@ -35,7 +35,8 @@ Paged-cache decode (blocks of `block_size` rows named by a table per
 sequence): the tensors q_nope, q_pe, k_nope_pages [N,H,bs,128], k_pe_pages
 [N,bs,64], v_pages [N,H,bs,128] and the appended token's k_nope_new,
 k_pe_new, v_new are drawn in that order, one SeedSequence child each
-(standard normal, bf16); the block layout gives sequence b ceil(L_b / bs)
+(standard normal, bf16; on the device, drawn in chunks of at most 64 MiB of
+fp32 along the leading index); the block layout gives sequence b ceil(L_b / bs)
 blocks taken in order from a PCG64(SeedSequence([seed, 2])) permutation of
 all blocks, table entries past a sequence's blocks left at 0.
 
@@ -93,6 +94,15 @@ WORKLOADS = {
     "causal_prefill": Workload("causal_prefill", B=1, H=64, T=4096, past_len=0),
     "chunked_prefill": Workload("chunked_prefill", B=1, H=64, T=2048, past_len=14336,
                                 std=float(np.sqrt(2.0))),
+}
+
+
+# One GPU's share when the 64 heads are split over 8 GPUs (heads shard with no
+# exchange inside attention): the same shapes at H = 8.
+SHARD_WORKLOADS = {
+    "batched_decode_h8": Workload("batched_decode_h8", B=32, H=8, T=1, past_len=8191),
+    "chunked_prefill_h8": Workload("chunked_prefill_h8", B=1, H=8, T=2048, past_len=14336,
+                                   std=float(np.sqrt(2.0))),
 }
 
 
@@ -313,8 +323,12 @@ def paged_device_inputs(B: int, H: int, num_blocks: int, block_size: int, device
     out = {}
     for name, shape in paged_shapes(B, H, num_blocks, block_size).items():
         t = torch.empty(shape, dtype=torch.bfloat16, device=device)
-        for i in range(shape[0]):
-            t[i].copy_(torch.randn(shape[1:], generator=g, dtype=torch.float32, device=device))
+        per = int(np.prod(shape[1:]))
+        step = max(1, (64 << 20) // (4 * per))  # leading-index rows per draw (<= 64 MiB of fp32)
+        for i in range(0, shape[0], step):
+            n = min(step, shape[0] - i)
+            t[i:i + n].copy_(torch.randn((n,) + tuple(shape[1:]), generator=g, dtype=torch.float32,
+                                         device=device))
         out[name] = t
     return out
 

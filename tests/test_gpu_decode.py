@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from oracle import mla_attention
-from seeded_inputs import WORKLOADS, device_inputs, host_inputs, random_inputs
+from seeded_inputs import SHARD_WORKLOADS, WORKLOADS, device_inputs, host_inputs, random_inputs
 
 from _gpu_util import assert_parity, log, to_host_bits, to_host_f64, upload
 
@@ -179,11 +179,13 @@ def test_decode_future_independence_and_determinism():
     assert np.array_equal(a, b)
 
 
-def test_batched_decode_full_size_sampled():
-    """The full batched decode (B=32, H=64, S=8192; 8.6 GB of keys and values),
-    inputs drawn on the device; the oracle checks sampled (b, h) rows."""
+@pytest.mark.parametrize("name", ["batched_decode", "batched_decode_h8"])
+def test_batched_decode_full_size_sampled(name):
+    """The full batched decode (B=32, H=64, S=8192; 8.6 GB of keys and values;
+    and one GPU's 8-head share of it), inputs drawn on the device; the oracle
+    checks sampled (b, h) rows."""
     import torch
-    wl = WORKLOADS["batched_decode"]
+    wl = WORKLOADS[name] if name in WORKLOADS else SHARD_WORKLOADS[name]
     log(f"case batched_decode B={wl.B} H={wl.H} P={wl.past_len}")
     d = device_inputs(wl, "cuda", seed=0)
     out = _gpu_decode(d, wl.past_len, wl.softmax_scale)

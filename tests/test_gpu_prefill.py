@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from oracle import mla_attention, mla_attention_rows
-from seeded_inputs import WORKLOADS, host_inputs, random_inputs
+from seeded_inputs import SHARD_WORKLOADS, WORKLOADS, host_inputs, random_inputs
 
 from _gpu_util import assert_parity, log, to_host_bits, to_host_f64, upload
 
@@ -159,11 +159,12 @@ def _sample_rows(B, H, T, n, seed):
 
 
 @pytest.mark.parametrize("name,std", [("causal_prefill", None), ("chunked_prefill", None),
-                                      ("chunked_prefill", 2.0)])
+                                      ("chunked_prefill", 2.0), ("chunked_prefill_h8", None)])
 def test_full_size_workloads_sampled(name, std):
-    """Full-size launch as benchmarked; the oracle checks sampled rows."""
+    """Full-size launch as benchmarked (and one GPU's 8-head share of the
+    chunked prefill); the oracle checks sampled rows."""
     import torch
-    wl = WORKLOADS[name]
+    wl = WORKLOADS[name] if name in WORKLOADS else SHARD_WORKLOADS[name]
     log(f"case full {name} std={std or wl.std} B={wl.B} H={wl.H} T={wl.T} P={wl.past_len}")
     x = host_inputs(wl, seed=0, std=std)
     out = _gpu_prefill(x, wl.past_len, wl.softmax_scale)
