@@ -35,6 +35,8 @@ MLA_ERR_SHAPE = 2
 _VP, _I32, _F32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "mla_attn_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _F32, _VP]),
+    "mla_attn_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "mla_attn_prefill_ws": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "mla_attn_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_attn_decode_varlen_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
@@ -130,12 +132,21 @@ def _shapes(q_nope, q_pe, k_nope, k_pe, v):
     return B, H, T, S
 
 
-def mla_attn_prefill(q_nope, q_pe, k_nope, k_pe, v, past_len: int, softmax_scale: float, out=None):
+def mla_attn_prefill_workspace_bytes(B: int, H: int, T: int, S: int) -> int:
+    """Bytes of device scratch the split prefill needs for (B, H, T, S) (0: none)."""
+    return int(_lib.mla_attn_prefill_workspace_bytes(int(B), int(H), int(T), int(S)))
+
+
+def mla_attn_prefill(q_nope, q_pe, k_nope, k_pe, v, past_len: int, softmax_scale: float, out=None,
+                     workspace=None, split=True):
     """Causal MLA attention of T new queries over S = past_len + T keys.
 
     q_nope [B,H,T,128], q_pe [B,H,T,64], k_nope [B,H,S,128], k_pe [B,1,S,64]
     (one rotary key for all heads), v [B,H,S,128]; bf16, contiguous, on one
     GPU. Returns out [B,H,T,128] bf16, enqueued on the current stream.
+    When the query tiles alone would leave the GPU part-empty and split is
+    true, the keys are split over several workgroups (mla_attn_prefill_ws,
+    with `workspace` or one allocated here); otherwise mla_attn_prefill.
     """
     import torch
 
@@ -146,6 +157,18 @@ def mla_attn_prefill(q_nope, q_pe, k_nope, k_pe, v, past_len: int, softmax_scale
         _check_tensor(out, "out")
         if tuple(out.shape) != (B, H, T, V_HEAD_DIM) or out.device != q_nope.device:
             raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, T, V_HEAD_DIM)}")
+    need = mla_attn_prefill_workspace_bytes(B, H, T, S) if split else 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q_nope.device)
+        if not (workspace.is_cuda and workspace.is_contiguous()):
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        st = _lib.mla_attn_prefill_ws(
+            q_nope.data_ptr(), q_pe.data_ptr(), k_nope.data_ptr(), k_pe.data_ptr(), v.data_ptr(),
+            out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            B, H, T, S, int(past_len), float(softmax_scale), _stream_handle(q_nope.device))
+        _raise_for(st, "mla_attn_prefill_ws")
+        return out
     st = _lib.mla_attn_prefill(
         q_nope.data_ptr(), q_pe.data_ptr(), k_nope.data_ptr(), k_pe.data_ptr(), v.data_ptr(),
         out.data_ptr(), B, H, T, S, int(past_len), float(softmax_scale), _stream_handle(q_nope.device))
@@ -366,6 +389,8 @@ def mla_attn_decode_latent(q_nope, q_pe, c_kv, k_pe, w_kv_b, past_len: int, soft
 
 
 __all__ = [
+    "mla_attn_prefill_ws",
+    "mla_attn_prefill_workspace_bytes",
     "mla_attn_decode_paged",
     "mla_attn_decode_paged_workspace_bytes",
     "mla_attn_decode_varlen",

@@ -120,7 +120,7 @@ mla_status mla_attn_prefill(const void* q_nope, const void* q_pe, const void* k_
                          mla::prefill_block_m());
   if (r.status != MLA_OK) return report("mla_attn_prefill", r);
   if (r.empty) return MLA_OK;
-  mla::PrefillArgs a;
+  mla::PrefillArgs a{};  // nsplit 0: one workgroup per query tile covers all its keys
   a.q_nope = static_cast<const uint16_t*>(q_nope);
   a.q_pe = static_cast<const uint16_t*>(q_pe);
   a.k_nope = static_cast<const uint16_t*>(k_nope);
@@ -136,6 +136,47 @@ mla_status mla_attn_prefill(const void* q_nope, const void* q_pe, const void* k_
   a.scale_log2 = softmax_scale * kLog2e;
   const hipError_t e = mla::launch_prefill(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error("mla_attn_prefill", e);
+  return MLA_OK;
+}
+
+size_t mla_attn_prefill_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t S) {
+  return mla::plan_prefill(B, H, T, S, mla::prefill_block_m(), mla::kPrefillKeyTile)
+      .workspace_bytes;
+}
+
+mla_status mla_attn_prefill_ws(const void* q_nope, const void* q_pe, const void* k_nope,
+                               const void* k_pe, const void* v, void* out, void* workspace,
+                               size_t workspace_bytes, int32_t B, int32_t H, int32_t T, int32_t S,
+                               int32_t past_len, float softmax_scale, void* stream) {
+  mla::PrefillPlan plan;
+  const mla::CheckResult r = mla::check_prefill_ws(
+      q_nope, q_pe, k_nope, k_pe, v, out, workspace, workspace_bytes, B, H, T, S, past_len,
+      softmax_scale, mla::prefill_block_m(), mla::kPrefillKeyTile, &plan);
+  if (r.status != MLA_OK) return report("mla_attn_prefill_ws", r);
+  if (r.empty) return MLA_OK;
+  mla::PrefillArgs a{};
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.k_nope = static_cast<const uint16_t*>(k_nope);
+  a.k_pe = static_cast<const uint16_t*>(k_pe);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<uint16_t*>(out);
+  a.B = B;
+  a.H = H;
+  a.T = T;
+  a.S = S;
+  a.past_len = past_len;
+  a.ntiles = (int32_t)((T + mla::prefill_block_m() - 1) / mla::prefill_block_m());
+  a.scale_log2 = softmax_scale * kLog2e;
+  a.nsplit = (int32_t)plan.nsplit;
+  a.tiles_per_split = (int32_t)plan.tiles_per_split;
+  if (plan.nsplit > 1) {
+    char* ws = static_cast<char*>(workspace);
+    a.ws_o = reinterpret_cast<float*>(ws);
+    a.ws_ml = reinterpret_cast<float*>(ws + plan.ws_o_bytes);
+  }
+  const hipError_t e = mla::launch_prefill(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error("mla_attn_prefill_ws", e);
   return MLA_OK;
 }
 

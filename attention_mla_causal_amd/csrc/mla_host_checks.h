@@ -161,6 +161,46 @@ inline CheckResult check_common(const void* q_nope, const void* q_pe, const void
   return r;
 }
 
+// Prefill key-range split: when B*H*ceil(T/block_m) workgroups would leave
+// the GPU part-empty (it holds two per CU), each query tile's keys are split
+// over several workgroups, each writing an fp32 partial that a second kernel
+// merges.
+constexpr int64_t kPrefillTargetWorkgroups = 512;
+constexpr int64_t kPrefillMinTilesPerSplit = 16;  // 512 keys: pipeline fill and drain stay small
+constexpr int64_t kPrefillMaxSplits = 16;
+
+struct PrefillPlan {
+  int64_t nsplit = 1;           // key ranges per query tile
+  int64_t tiles_per_split = 0;  // key tiles (kPrefillKeyTile keys) per range
+  size_t ws_o_bytes = 0;        // fp32 [B*H*T, nsplit, 128]
+  size_t ws_ml_bytes = 0;       // fp32 [B*H*T, nsplit, 2]
+  size_t workspace_bytes = 0;
+};
+
+inline PrefillPlan plan_prefill(int64_t B, int64_t H, int64_t T, int64_t S, int64_t block_m,
+                                int64_t key_tile) {
+  PrefillPlan p;
+  if (B <= 0 || H <= 0 || T <= 0 || S <= 0 || block_m <= 0 || key_tile <= 0) return p;
+  const int64_t wgs = B * H * ((T + block_m - 1) / block_m);
+  if (wgs >= kPrefillTargetWorkgroups) return p;
+  const int64_t tiles = (S + key_tile - 1) / key_tile;
+  int64_t n = (kPrefillTargetWorkgroups + wgs - 1) / wgs;
+  const int64_t by_len = tiles / kPrefillMinTilesPerSplit;
+  if (n > by_len) n = by_len;
+  if (n > kPrefillMaxSplits) n = kPrefillMaxSplits;
+  if (n <= 1) return p;
+  const int64_t tps = (tiles + n - 1) / n;
+  n = (tiles + tps - 1) / tps;  // every range starts inside the keys
+  if (n <= 1) return p;
+  const size_t rows = size_t(B) * size_t(H) * size_t(T);
+  p.nsplit = n;
+  p.tiles_per_split = tps;
+  p.ws_o_bytes = align256(rows * size_t(n) * 128 * sizeof(float));
+  p.ws_ml_bytes = align256(rows * size_t(n) * 2 * sizeof(float));
+  p.workspace_bytes = p.ws_o_bytes + p.ws_ml_bytes;
+  return p;
+}
+
 // block_m: queries per prefill workgroup (a property of the kernel build).
 inline CheckResult check_prefill(const void* q_nope, const void* q_pe, const void* k_nope,
                                  const void* k_pe, const void* v, const void* out, int64_t B,
@@ -180,6 +220,43 @@ inline CheckResult check_prefill(const void* q_nope, const void* q_pe, const voi
                   (long long)block_m, (long long)(B * H), (long long)tiles);
     r.status = MLA_ERR_SHAPE;
   }
+  return r;
+}
+
+// The prefill with a workspace: as check_prefill, plus the split plan's
+// workspace and grid.
+inline CheckResult check_prefill_ws(const void* q_nope, const void* q_pe, const void* k_nope,
+                                    const void* k_pe, const void* v, const void* out,
+                                    const void* workspace, size_t workspace_bytes, int64_t B,
+                                    int64_t H, int64_t T, int64_t S, int64_t past_len,
+                                    float scale, int64_t block_m, int64_t key_tile,
+                                    PrefillPlan* plan_out) {
+  CheckResult r = check_prefill(q_nope, q_pe, k_nope, k_pe, v, out, B, H, T, S, past_len, scale,
+                                block_m);
+  if (r.status != MLA_OK || r.empty) return r;
+  const PrefillPlan plan = plan_prefill(B, H, T, S, block_m, key_tile);
+  const int64_t tiles = (T + block_m - 1) / block_m;
+  if (B * H * tiles > kMaxGrid / plan.nsplit) {
+    std::snprintf(r.msg, sizeof(r.msg), "B*H*ceil(T/%lld)*nsplit exceeds the grid limit",
+                  (long long)block_m);
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  if (plan.workspace_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) {
+      std::snprintf(r.msg, sizeof(r.msg), "workspace %s: %zu bytes given, %zu needed",
+                    workspace == nullptr ? "is NULL" : "too small", workspace_bytes,
+                    plan.workspace_bytes);
+      r.status = MLA_ERR_WORKSPACE;
+      return r;
+    }
+    if (misaligned(workspace)) {
+      std::snprintf(r.msg, sizeof(r.msg), "workspace is not 16-byte aligned");
+      r.status = MLA_ERR_ALIGN;
+      return r;
+    }
+  }
+  if (plan_out) *plan_out = plan;
   return r;
 }
 

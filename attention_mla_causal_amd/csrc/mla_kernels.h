@@ -7,6 +7,10 @@
 
 namespace mla {
 
+// Keys per prefill tile (the kernel's BN); the host's key-range split plan
+// counts in these tiles.
+constexpr int kPrefillKeyTile = 32;
+
 struct PrefillArgs {
   const uint16_t* q_nope;  // [B,H,T,128] bf16 bits
   const uint16_t* q_pe;    // [B,H,T,64]
@@ -17,6 +21,12 @@ struct PrefillArgs {
   int32_t B, H, T, S, past_len;
   int32_t ntiles;          // ceil(T / prefill_block_m())
   float scale_log2;        // softmax_scale * log2(e)
+  // Key-range split: nsplit > 1 gives each workgroup key tiles
+  // [sp * tiles_per_split, +tiles_per_split) of its query tile; it writes an
+  // fp32 partial, merged by a second kernel into out.
+  int32_t nsplit, tiles_per_split;
+  float* ws_o;             // [B*H*T, nsplit, 128] partial outputs (unnormalised)
+  float* ws_ml;            // [B*H*T, nsplit, 2] partial (max, sum), max in the scaled log2 domain
 };
 
 struct DecodeArgs {

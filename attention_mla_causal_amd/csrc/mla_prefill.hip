@@ -49,6 +49,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int DN = 128;   // non-rotary query/key dims
@@ -59,6 +61,7 @@ constexpr int NT = NW * 64;
 constexpr int QW = 32;        // queries per wave (one MFMA column group)
 constexpr int BM = NW * QW;   // 128 queries per workgroup
 constexpr int BN = 32;        // keys per tile (one 32-key MFMA row group)
+static_assert(BN == kPrefillKeyTile, "the host plans key-range splits in these tiles");
 
 // LDS tile regions, bytes. A region of BN rows of 16-byte chunks is stored
 // as column blocks of 4 chunks (64 bytes): block cb = c / 4 holds chunks
@@ -337,7 +340,28 @@ __device__ __forceinline__ void rescale_o(Acc& acc, float alpha) {
   }
 }
 
-__global__ __launch_bounds__(NT, 2) void mla_prefill_kernel(PrefillArgs a) {
+// Split mode, a workgroup whose key range the query tile never reaches: the
+// empty partial (0, -inf, 0) for each of its rows, so the merge can read
+// every split.
+__device__ __forceinline__ void write_empty_partials(const PrefillArgs& a, int bh, int q0, int sp) {
+  static_assert(NT == 2 * BM, "two threads per query row");
+  const int64_t T = a.T;
+  const int r = threadIdx.x >> 1, half = threadIdx.x & 1;  // 128 rows x 2 halves of 64 dims
+  const int64_t q = q0 + r;
+  if (q >= T) return;
+  const int64_t slot = ((int64_t)bh * T + q) * a.nsplit + sp;
+  float* po = a.ws_o + slot * DV + 64 * half;
+#pragma unroll
+  for (int e = 0; e < 64; e += 4) *reinterpret_cast<f32x4*>(po + e) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (half == 0) *reinterpret_cast<f32x2*>(a.ws_ml + 2 * slot) = f32x2{-INFINITY, 0.0f};
+}
+
+// SPLIT: the workgroup covers one key range of its query tile and writes an
+// fp32 partial (merged by mla_prefill_merge_kernel); otherwise all keys and
+// the bf16 output. Two instantiations, so the unsplit kernel carries none of
+// the split's code.
+template <bool SPLIT>
+__device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   // separate LDS objects per buffer so the compiler can tell an in-flight copy
   // into one from reads of another
   __shared__ __attribute__((aligned(1024))) char kbuf0[K_BYTES];
@@ -353,11 +377,19 @@ __global__ __launch_bounds__(NT, 2) void mla_prefill_kernel(PrefillArgs a) {
   // XCD dispatches its tiles heaviest first across all of its heads
   // (longest-job-first); otherwise head by head, heaviest tile first, so a
   // head's K/V streams through the XCD's L2 for all its tiles at once.
-  int bh, qt;
+  int bh, qt, sp = 0;
   {
     const int per = nwg / 8, i = wg / 8;
     const bool uneven = 2 * (a.past_len + (int64_t)BM) < a.past_len + (int64_t)a.T;
-    if (nwg % 8 == 0 && per % a.ntiles == 0 && uneven) {
+    if (SPLIT) {
+      // key-range splits of one query tile are adjacent (same XCD when the
+      // grid is a multiple of 8), then query tiles, then heads
+      const int logical = (nwg % 8 == 0) ? (wg % 8) * per + i : wg;
+      sp = logical % a.nsplit;
+      const int rest = logical / a.nsplit;
+      bh = rest / a.ntiles;
+      qt = a.ntiles - 1 - rest % a.ntiles;
+    } else if (nwg % 8 == 0 && per % a.ntiles == 0 && uneven) {
       const int nh = per / a.ntiles;
       bh = (wg % 8) * nh + i % nh;
       qt = a.ntiles - 1 - i / nh;
@@ -374,25 +406,42 @@ __global__ __launch_bounds__(NT, 2) void mla_prefill_kernel(PrefillArgs a) {
   const int tid = threadIdx.x;
   geo.lane = tid & 63;
   geo.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  geo.S = a.S;
-  geo.P = a.past_len;
-  geo.kn_g = a.k_nope + (int64_t)bh * geo.S * DN;
-  geo.kp_g = a.k_pe + (int64_t)b * geo.S * DR;
-  geo.v_g = a.v + (int64_t)bh * geo.S * DV;
+  const int lane = geo.lane, hi = lane >> 5, l32 = lane & 31;
+  const int64_t T = a.T;
+  const int64_t q0w = q0 + geo.wave * QW;
+
+  // ---- key range of the workgroup: tiles [kt0, kt1) of [0, P + last query + 1)
+  const int64_t q_last = (q0 + BM < T ? q0 + BM : T) - 1;
+  const int nblocks_all = (int)((a.past_len + q_last + 1 + BN - 1) / BN);
+  int kt0 = 0, kt1 = nblocks_all;
+  if (SPLIT) {
+    kt0 = sp * a.tiles_per_split;
+    kt1 = kt0 + a.tiles_per_split < nblocks_all ? kt0 + a.tiles_per_split : nblocks_all;
+  }
+  const int nblocks = kt1 - kt0;
+  if (SPLIT && nblocks <= 0) {  // no key of this range is visible to the tile
+    write_empty_partials(a, bh, q0, sp);
+    return;
+  }
+  // Everything below sees keys relative to k0: the key slices start at row k0,
+  // and the last key query i sees is P + i with P = past_len - k0 (< 0 when the
+  // query sees no key of this range).
+  const int64_t k0 = (int64_t)kt0 * BN;
+  geo.S = a.S - k0;
+  geo.P = a.past_len - k0;
+  geo.kn_g = a.k_nope + (int64_t)bh * a.S * DN + k0 * DN;
+  geo.kp_g = a.k_pe + (int64_t)b * a.S * DR + k0 * DR;
+  geo.v_g = a.v + (int64_t)bh * a.S * DV + k0 * DV;
   geo.kn.init(geo.wave, geo.lane);
   geo.kp.init(geo.wave, geo.lane);
   geo.vv.init(geo.wave, geo.lane);
-  const int lane = geo.lane, hi = lane >> 5, l32 = lane & 31;
-  const int64_t T = a.T, S = geo.S, P = geo.P;
-  const int64_t q0w = q0 + geo.wave * QW;
-
-  // ---- key range of the workgroup: [0, P + last query + 1)
-  const int64_t q_last = (q0 + BM < T ? q0 + BM : T) - 1;
-  const int nblocks = (int)((P + q_last + 1 + BN - 1) / BN);
-  const bool wave_live = q0w < T;
+  const int64_t S = geo.S, P = geo.P;
+  const int64_t wq_last = q0w + QW - 1 < T ? q0w + QW - 1 : T - 1;
+  // a wave computes when some query of it sees a key of the range; its tile 0
+  // then always holds a visible key (key 0 of the range)
+  const bool wave_live = q0w < T && P + wq_last >= 0;
   // last tile holding a key that some query of this wave sees (-1: none)
-  const int wave_last =
-      wave_live ? (int)((P + (q0w + QW - 1 < T ? q0w + QW - 1 : T - 1)) / BN) : -1;
+  const int wave_last = wave_live ? (int)((P + wq_last) / BN) : -1;
   const int64_t lim = P + q0w + l32;  // last key this lane's query sees
 
   copy_k(geo, 0, kbuf0);
@@ -507,6 +556,27 @@ __global__ __launch_bounds__(NT, 2) void mla_prefill_kernel(PrefillArgs a) {
       mfma_stream<-1, false, true>(sb, kbuf0, acc, vbuf0, ln, qf, pa, st, sa, pb, cl2);
   }
 
+  if (SPLIT) {
+    // ---- split epilogue: the unnormalised partial and the row's (max, sum);
+    // a wave that saw no key writes the empty partial (0, -inf, 0)
+    if (q0w >= T) return;
+    const float l_tot = sum_pair32(acc.l_run);
+    const int64_t myq = q0w + l32;
+    if (myq >= T) return;
+    const int64_t slot = ((int64_t)bh * T + myq) * a.nsplit + sp;
+    float* po = a.ws_o + slot * DV;
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const int dv0 = 32 * n + 8 * gg + 4 * hi;
+        *reinterpret_cast<f32x4*>(po + dv0) =
+            f32x4{acc.o[n][4 * gg], acc.o[n][4 * gg + 1], acc.o[n][4 * gg + 2], acc.o[n][4 * gg + 3]};
+      }
+    if (hi == 0) *reinterpret_cast<f32x2*>(a.ws_ml + 2 * slot) = f32x2{acc.m_run, l_tot};
+    return;
+  }
+
   // ---- epilogue: divide by the full row sum and store bf16
   if (!wave_live) return;
   const float inv = 1.0f / sum_pair32(acc.l_run);
@@ -525,13 +595,48 @@ __global__ __launch_bounds__(NT, 2) void mla_prefill_kernel(PrefillArgs a) {
     }
 }
 
+__global__ __launch_bounds__(NT, 2) void mla_prefill_kernel(PrefillArgs a) { prefill_body<false>(a); }
+__global__ __launch_bounds__(NT, 2) void mla_prefill_split_kernel(PrefillArgs a) { prefill_body<true>(a); }
+
+// Log-sum-exp merge of the key-range partials of every query row: one wave
+// per row, lane l owns output dims 2l, 2l+1.
+__global__ __launch_bounds__(256) void mla_prefill_merge_kernel(PrefillArgs a) {
+  const int64_t rows = (int64_t)a.B * a.H * a.T;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const float* ml = a.ws_ml + row * a.nsplit * 2;
+  float M = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, ml[2 * s]);
+  float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float m = ml[2 * s];
+    const float w = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+    const f32x2 p = *reinterpret_cast<const f32x2*>(a.ws_o + (row * a.nsplit + s) * DV + 2 * lane);
+    L = __builtin_fmaf(w, ml[2 * s + 1], L);
+    o0 = __builtin_fmaf(w, p[0], o0);
+    o1 = __builtin_fmaf(w, p[1], o1);
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  const uint32_t packed = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(o0 * inv)) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(o1 * inv)) << 16);
+  *reinterpret_cast<uint32_t*>(a.out + row * DV + 2 * lane) = packed;
+}
+
 }  // namespace
 
 int prefill_block_m() { return BM; }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-  const int grid = a.B * a.H * a.ntiles;
-  hipLaunchKernelGGL(mla_prefill_kernel, dim3(grid), dim3(NT), 0, stream, a);
+  if (a.nsplit <= 1) {
+    hipLaunchKernelGGL(mla_prefill_kernel, dim3(a.B * a.H * a.ntiles), dim3(NT), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(mla_prefill_split_kernel, dim3(a.B * a.H * a.ntiles * a.nsplit), dim3(NT), 0,
+                       stream, a);
+    const int64_t rows = (int64_t)a.B * a.H * a.T;
+    hipLaunchKernelGGL(mla_prefill_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                       stream, a);
+  }
   return hipGetLastError();
 }
 

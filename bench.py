@@ -374,10 +374,12 @@ def run_prefill(wl, steps, warmup, seed=0):
     x = host_inputs(wl, seed=seed)
     d = {k: to_dev(v, dev) for k, v in x.items()}
     out = torch.empty((wl.B, wl.H, wl.T, 128), dtype=torch.bfloat16, device=dev)
+    need = mla.mla_attn_prefill_workspace_bytes(wl.B, wl.H, wl.T, wl.S)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)  # key-range split partials
 
     def step(i):
         mla.mla_attn_prefill(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], wl.past_len,
-                             wl.softmax_scale, out=out)
+                             wl.softmax_scale, out=out, workspace=ws)
 
     ms, wall_ms = time_eager(step, steps, warmup)
     flops = prefill_flops(wl)
@@ -386,6 +388,7 @@ def run_prefill(wl, steps, warmup, seed=0):
     res = {
         "workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "past_len": wl.past_len, "S": wl.S,
         "std": wl.std, "inputs": "host", "steps": steps, "timing": "eager",
+        "key_splits": max(1, need and int(need // (wl.B * wl.H * wl.T * 130 * 4)) or 1),
         "ms_per_step": ms, "wall_ms_per_step": wall_ms, "value": tfs, "unit": "TFLOP/s",
         "algorithmic_flops": flops,
         "roofline": {"bound": "mfma", "kernel": kernel, "achieved": tfs, "peak": MFMA_BF16_PEAK_TFS,

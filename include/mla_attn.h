@@ -77,6 +77,34 @@ mla_status mla_attn_prefill(const void* q_nope, const void* q_pe,
                             void* stream);
 
 /*
+ * Bytes of device workspace mla_attn_prefill_ws needs for (B, H, T, S); 0
+ * when one workgroup per query tile already fills the GPU. A pure function of
+ * its arguments.
+ */
+size_t mla_attn_prefill_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t S);
+
+/*
+ * mla_attn_prefill with a workspace: the same result (up to the order of
+ * rounding). When B*H*ceil(T/128) workgroups would leave the GPU part-empty
+ * (fewer than 512: it holds two per CU), the keys of each query tile are split
+ * into ranges of whole 32-key tiles (at least 512 keys, at most 16 ranges),
+ * each range's workgroup writes an fp32 partial (unnormalised output, max and
+ * sum per query) to the workspace, and a second kernel merges the partials by
+ * log-sum-exp into out. Otherwise it is exactly mla_attn_prefill.
+ * workspace: caller-owned device scratch of at least
+ * mla_attn_prefill_workspace_bytes(B, H, T, S) bytes, 16-byte aligned (may
+ * be NULL when that is 0); contents on entry do not matter. Calls that may
+ * run at the same time must not share a workspace. Errors as for
+ * mla_attn_prefill, plus MLA_ERR_WORKSPACE.
+ */
+mla_status mla_attn_prefill_ws(const void* q_nope, const void* q_pe,
+                               const void* k_nope, const void* k_pe,
+                               const void* v, void* out,
+                               void* workspace, size_t workspace_bytes,
+                               int32_t B, int32_t H, int32_t T, int32_t S, int32_t past_len,
+                               float softmax_scale, void* stream);
+
+/*
  * Bytes of device workspace mla_attn_decode needs for (B, H, S). A pure
  * function of its arguments (no device query); 0 means no workspace is
  * needed. Returns 0 for negative sizes.

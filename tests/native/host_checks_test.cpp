@@ -126,6 +126,33 @@ int main() {
     EXPECT(check_decode_varlen(p, p, nullptr, nullptr, nullptr, p, p, nullptr, 0, 2, 8, 0, 0, sc, &pl).status == MLA_OK);
     EXPECT(check_decode_varlen(p, p, nullptr, p, p, p, p, nullptr, 0, 2, 8, 16, 0, sc, &pl).status == MLA_ERR_NULL);
   }
+  // prefill key-range split plan
+  {
+    for (long long B : {1LL, 2LL}) for (long long H : {1LL, 2LL, 8LL, 64LL})
+      for (long long T : {1LL, 100LL, 256LL, 2048LL}) for (long long P : {0LL, 3840LL, 14336LL}) {
+        const long long S = P + T;
+        const PrefillPlan pl = plan_prefill(B, H, T, S, 128, 32);
+        const long long tiles = (S + 31) / 32, wgs = B * H * ((T + 127) / 128);
+        EXPECT(pl.nsplit >= 1 && pl.nsplit <= kPrefillMaxSplits);
+        if (pl.nsplit > 1) {
+          EXPECT(wgs < kPrefillTargetWorkgroups);
+          EXPECT(pl.tiles_per_split >= kPrefillMinTilesPerSplit);
+          EXPECT(pl.tiles_per_split * pl.nsplit >= tiles);          // every key covered
+          EXPECT(pl.tiles_per_split * (pl.nsplit - 1) < tiles);     // every range starts inside
+          EXPECT(pl.workspace_bytes == pl.ws_o_bytes + pl.ws_ml_bytes);
+          EXPECT(pl.ws_o_bytes >= size_t(B * H * T) * pl.nsplit * 128 * 4);
+        } else {
+          EXPECT(pl.workspace_bytes == 0);
+        }
+      }
+    EXPECT(plan_prefill(1, 8, 2048, 16384, 128, 32).nsplit == 4);   // one GPU's 8-head share
+    EXPECT(plan_prefill(1, 64, 2048, 16384, 128, 32).nsplit == 1);
+    PrefillPlan pl;
+    const size_t need = plan_prefill(1, 8, 2048, 16384, 128, 32).workspace_bytes;
+    EXPECT(check_prefill_ws(p, p, p, p, p, p, p, need, 1, 8, 2048, 16384, 14336, sc, 128, 32, &pl).status == MLA_OK);
+    EXPECT(check_prefill_ws(p, p, p, p, p, p, p, need - 1, 1, 8, 2048, 16384, 14336, sc, 128, 32, &pl).status == MLA_ERR_WORKSPACE);
+    EXPECT(check_prefill_ws(p, p, p, p, p, p, nullptr, 0, 1, 64, 2048, 16384, 14336, sc, 128, 32, &pl).status == MLA_OK);
+  }
   // latent decode: S limit (1024-byte rows in a 32-bit byte range)
   {
     LatentPlan lp;

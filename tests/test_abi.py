@@ -35,6 +35,7 @@ def test_header_declares_the_boundary():
         "mla_attn_decode_latent", "mla_attn_decode_latent_workspace_bytes",
         "mla_attn_decode_varlen", "mla_attn_decode_varlen_workspace_bytes",
         "mla_attn_decode_paged", "mla_attn_decode_paged_workspace_bytes",
+        "mla_attn_prefill_ws", "mla_attn_prefill_workspace_bytes",
         "mla_last_error", "mla_status_string"])
 
 
@@ -208,3 +209,27 @@ def test_paged_decode_errors(lib):
     assert _paged(lib, ok, all3, ALIGNED, need, 4, 64, 100, 64, 64, 4096, float("inf")) == 4
     assert _paged(lib, [None] * 7, none3, None, 0, 0, 64, 0, 0, 0, 0) == 0       # empty batch: no-op
     assert "mla_attn_decode_paged" in lib.mla_last_error().decode()
+
+
+def test_prefill_ws_errors(lib):
+    # a small grid (2 heads, 2 query tiles, 4096 keys) splits its keys; a full one does not
+    need = lib.mla_attn_prefill_workspace_bytes(1, 2, 256, 4096)
+    assert need >= 2 * 256 * 2 * 128 * 4
+    assert lib.mla_attn_prefill_workspace_bytes(1, 64, 4096, 4096) == 0
+    assert lib.mla_attn_prefill_workspace_bytes(1, 2, 256, 256) == 0       # too few keys to split
+    ok = [ALIGNED] * 6
+
+    def call(ptrs, ws, ws_bytes, B, H, T, S, P, scale=SC):
+        return lib.mla_attn_prefill_ws(*ptrs, ws, ws_bytes, B, H, T, S, P, scale, None)
+
+    assert call(ok, ALIGNED, need, 1, 2, 256, 4096, 3839) == 2             # S != past_len + T
+    assert call(ok, None, need, 1, 2, 256, 4096, 3840) == 5
+    assert call(ok, ALIGNED, need - 1, 1, 2, 256, 4096, 3840) == 5
+    assert call(ok, MISALIGNED, need, 1, 2, 256, 4096, 3840) == 3
+    assert call(ok, ALIGNED, need, 1, 2, 256, 4096, 3840, float("nan")) == 4
+    for i in range(6):
+        ptrs = list(ok)
+        ptrs[i] = None
+        assert call(ptrs, ALIGNED, need, 1, 2, 256, 4096, 3840) == 1
+    assert "mla_attn_prefill_ws" in lib.mla_last_error().decode()
+    assert call([None] * 6, None, 0, 0, 2, 256, 4096, 3840) == 0           # empty batch

@@ -149,6 +149,37 @@ def test_chunked_prefill_matches_full_prefill_suffix():
     assert_parity(chunk, _oracle(y, P), "chunk vs oracle")
 
 
+# (B, H, T, P): grids too small to fill the GPU, so the keys of each query
+# tile split over several workgroups: several ranges, a ragged last range,
+# causal tiles that see no key of the later ranges, 2..5 ranges.
+SPLIT = [(1, 2, 256, 3840), (1, 1, 100, 5000), (2, 4, 1024, 0), (1, 3, 777, 2000), (1, 8, 129, 1023)]
+
+
+@pytest.mark.parametrize("B,H,T,P", SPLIT)
+def test_key_range_splits(B, H, T, P):
+    """The split prefill against the oracle and against the unsplit kernel;
+    a workspace full of NaN bits changes nothing (every partial is written)."""
+    import torch
+    m = _lib()
+    need = m.mla_attn_prefill_workspace_bytes(B, H, T, P + T)
+    log(f"case prefill split B={B} H={H} T={T} P={P} ws={need}")
+    assert need > 0
+    x = random_inputs(B, H, T, P, seed=B * 1000 + H * 100 + T + P)
+    d = upload(x)
+    args = (d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], P, ALPHA)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    split = m.mla_attn_prefill(*args, workspace=ws)
+    whole = m.mla_attn_prefill(*args, split=False)
+    fresh = m.mla_attn_prefill(*args)
+    torch.cuda.synchronize()
+    ref = _oracle(x, P)
+    assert_parity(to_host_f64(split), ref, "split")
+    assert_parity(to_host_f64(whole), ref, "unsplit")
+    assert np.array_equal(to_host_bits(split), to_host_bits(fresh))
+    diff = np.abs(to_host_f64(split) - to_host_f64(whole))
+    assert diff.max() <= 1e-2, diff.max()
+
+
 def _sample_rows(B, H, T, n, seed):
     rng = np.random.default_rng(seed)
     rows = {(0, 0, 0), (B - 1, H - 1, T - 1), (0, H - 1, T // 2), (B - 1, 0, min(T - 1, 127)),
