@@ -32,3 +32,4 @@ from .mla_paged import (  # noqa: F401
     gather_sequence,
     mla_decode_paged,
 )
+from .mla_prefill_varlen import mla_prefill_varlen  # noqa: F401
