@@ -37,6 +37,7 @@ SIGNATURES = {
     "mla_attn_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_attn_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "mla_attn_prefill_ws": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _I32, _F32, _VP]),
+    "mla_attn_prefill_varlen": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "mla_attn_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_attn_decode_varlen_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
@@ -173,6 +174,37 @@ def mla_attn_prefill(q_nope, q_pe, k_nope, k_pe, v, past_len: int, softmax_scale
         q_nope.data_ptr(), q_pe.data_ptr(), k_nope.data_ptr(), k_pe.data_ptr(), v.data_ptr(),
         out.data_ptr(), B, H, T, S, int(past_len), float(softmax_scale), _stream_handle(q_nope.device))
     _raise_for(st, "mla_attn_prefill")
+    return out
+
+
+def mla_attn_prefill_varlen(q_nope, q_pe, k_nope, k_pe, v, q_lens, past_lens, softmax_scale: float,
+                            out=None):
+    """Causal MLA prefill of a right-padded batch with a length per sequence.
+
+    q_nope [B,H,Tmax,128], q_pe [B,H,Tmax,64], k_nope [B,H,Smax,128],
+    k_pe [B,1,Smax,64], v [B,H,Smax,128] bf16; q_lens and past_lens int32 GPU
+    tensors [B]: sequence b has q_lens[b] new queries (rows [0, q_lens[b]))
+    over past_lens[b] cached keys (its keys are rows [0, past_lens[b] +
+    q_lens[b])). Both are clamped on the device (q_lens to [0, Tmax],
+    past_lens to [0, Smax - q_lens]). Returns out [B,H,Tmax,128] bf16 with
+    padded query rows set to 0.
+    """
+    import torch
+
+    B, H, Tmax, Smax = _shapes(q_nope, q_pe, k_nope, k_pe, v)
+    _check_int32(q_lens, "q_lens", (B,), q_nope.device)
+    _check_int32(past_lens, "past_lens", (B,), q_nope.device)
+    if out is None:
+        out = torch.empty((B, H, Tmax, V_HEAD_DIM), dtype=torch.bfloat16, device=q_nope.device)
+    else:
+        _check_tensor(out, "out")
+        if tuple(out.shape) != (B, H, Tmax, V_HEAD_DIM) or out.device != q_nope.device:
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, Tmax, V_HEAD_DIM)}")
+    st = _lib.mla_attn_prefill_varlen(
+        q_nope.data_ptr(), q_pe.data_ptr(), k_nope.data_ptr(), k_pe.data_ptr(), v.data_ptr(),
+        q_lens.data_ptr(), past_lens.data_ptr(), out.data_ptr(), B, H, Tmax, Smax,
+        float(softmax_scale), _stream_handle(q_nope.device))
+    _raise_for(st, "mla_attn_prefill_varlen")
     return out
 
 

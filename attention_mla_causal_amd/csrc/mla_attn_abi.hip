@@ -180,6 +180,37 @@ mla_status mla_attn_prefill_ws(const void* q_nope, const void* q_pe, const void*
   return MLA_OK;
 }
 
+mla_status mla_attn_prefill_varlen(const void* q_nope, const void* q_pe, const void* k_nope,
+                                   const void* k_pe, const void* v, const int32_t* q_lens,
+                                   const int32_t* past_lens, void* out, int32_t B, int32_t H,
+                                   int32_t max_q_len, int32_t max_kv_len, float softmax_scale,
+                                   void* stream) {
+  const mla::CheckResult r = mla::check_prefill_varlen(
+      q_nope, q_pe, k_nope, k_pe, v, q_lens, past_lens, out, B, H, max_q_len, max_kv_len,
+      softmax_scale, mla::prefill_block_m());
+  if (r.status != MLA_OK) return report("mla_attn_prefill_varlen", r);
+  if (r.empty) return MLA_OK;
+  mla::PrefillArgs a{};
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.k_nope = static_cast<const uint16_t*>(k_nope);
+  a.k_pe = static_cast<const uint16_t*>(k_pe);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<uint16_t*>(out);
+  a.q_lens = q_lens;
+  a.past_lens = past_lens;
+  a.B = B;
+  a.H = H;
+  a.T = max_q_len;
+  a.S = max_kv_len;
+  a.past_len = 0;  // the lengths stay on the device
+  a.ntiles = (int32_t)((max_q_len + mla::prefill_block_m() - 1) / mla::prefill_block_m());
+  a.scale_log2 = softmax_scale * kLog2e;
+  const hipError_t e = mla::launch_prefill(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error("mla_attn_prefill_varlen", e);
+  return MLA_OK;
+}
+
 size_t mla_attn_decode_workspace_bytes(int32_t B, int32_t H, int32_t S) {
   return mla::plan_decode(B, H, S).workspace_bytes;
 }

@@ -260,6 +260,72 @@ inline CheckResult check_prefill_ws(const void* q_nope, const void* q_pe, const 
   return r;
 }
 
+// ---- prefill of a padded, variable-length batch: sequence b has q_lens[b]
+// new queries (rows [0, q_lens[b]) of its [max_q_len] query rows) over
+// past_lens[b] cached keys (its keys are rows [0, past_lens[b] + q_lens[b])
+// of its [max_kv_len] key rows); both arrays live in device memory.
+inline CheckResult check_prefill_varlen(const void* q_nope, const void* q_pe, const void* k_nope,
+                                        const void* k_pe, const void* v, const void* q_lens,
+                                        const void* past_lens, const void* out, int64_t B,
+                                        int64_t H, int64_t max_q, int64_t max_kv, float scale,
+                                        int64_t block_m) {
+  CheckResult r;
+  if (B < 0 || H < 0 || max_q < 0 || max_kv < 0) {
+    std::snprintf(r.msg, sizeof(r.msg),
+                  "negative size: B=%lld H=%lld max_q_len=%lld max_kv_len=%lld", (long long)B,
+                  (long long)H, (long long)max_q, (long long)max_kv);
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  if (max_q > max_kv) {
+    std::snprintf(r.msg, sizeof(r.msg),
+                  "max_q_len %lld exceeds max_kv_len %lld (every query's own key is a key)",
+                  (long long)max_q, (long long)max_kv);
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  if (B == 0 || H == 0 || max_q == 0) {
+    r.empty = true;
+    return r;
+  }
+  const void* ptrs[8] = {q_nope, q_pe, k_nope, k_pe, v, q_lens, past_lens, out};
+  static const char* const names[8] = {"q_nope", "q_pe", "k_nope", "k_pe",
+                                       "v", "q_lens", "past_lens", "out"};
+  for (int i = 0; i < 8; ++i) {
+    if (ptrs[i] == nullptr) {
+      std::snprintf(r.msg, sizeof(r.msg), "%s is NULL", names[i]);
+      r.status = MLA_ERR_NULL;
+      return r;
+    }
+    const uintptr_t align = (i == 5 || i == 6) ? 4u : 16u;
+    if ((reinterpret_cast<uintptr_t>(ptrs[i]) & (align - 1)) != 0) {
+      std::snprintf(r.msg, sizeof(r.msg), "%s is not %u-byte aligned", names[i], (unsigned)align);
+      r.status = MLA_ERR_ALIGN;
+      return r;
+    }
+  }
+  const float c = scale * 1.4426950408889634f;
+  if (!std::isfinite(scale) || !(scale > 0.0f) || !std::isfinite(c)) {
+    std::snprintf(r.msg, sizeof(r.msg), "softmax_scale %g must be finite and positive",
+                  (double)scale);
+    r.status = MLA_ERR_SCALE;
+    return r;
+  }
+  if (max_kv > kMaxPrefillKeys) {
+    std::snprintf(r.msg, sizeof(r.msg), "max_kv_len=%lld keys exceeds the prefill limit of %lld",
+                  (long long)max_kv, (long long)kMaxPrefillKeys);
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  const int64_t tiles = (max_q + block_m - 1) / block_m;
+  if (B * H > kMaxGrid / tiles) {
+    std::snprintf(r.msg, sizeof(r.msg), "B*H*ceil(max_q_len/%lld) = %lld*%lld exceeds the grid limit",
+                  (long long)block_m, (long long)(B * H), (long long)tiles);
+    r.status = MLA_ERR_SHAPE;
+  }
+  return r;
+}
+
 inline CheckResult check_decode(const void* q_nope, const void* q_pe, const void* k_nope,
                                 const void* k_pe, const void* v, const void* out,
                                 const void* workspace, size_t workspace_bytes, int64_t B,

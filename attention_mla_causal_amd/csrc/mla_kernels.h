@@ -27,6 +27,12 @@ struct PrefillArgs {
   int32_t nsplit, tiles_per_split;
   float* ws_o;             // [B*H*T, nsplit, 128] partial outputs (unnormalised)
   float* ws_ml;            // [B*H*T, nsplit, 2] partial (max, sum), max in the scaled log2 domain
+  // Padded variable-length batch (both null otherwise): T and S are then the
+  // padded row counts of the query and key slices, sequence b has
+  // q_lens[b] new queries over past_lens[b] cached keys (clamped on the
+  // device); past_len is unused.
+  const int32_t* q_lens;   // [B]
+  const int32_t* past_lens;  // [B]
 };
 
 struct DecodeArgs {

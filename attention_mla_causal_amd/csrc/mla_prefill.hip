@@ -37,7 +37,9 @@
 //  * Workgroup order: all query tiles of one head are placed on one XCD; with
 //    many cached keys they are dispatched head by head (K/V blocks stream
 //    through that XCD's L2 once for all of a head's tiles), and when the causal
-//    triangle dominates, heaviest tile first across the XCD's heads.
+//    triangle dominates, heaviest tile first across the XCD's heads. In a
+//    padded batch of sequences of different lengths, (batch, head) pairs are
+//    dealt round-robin over the XCDs and run longest sequence first.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -356,12 +358,61 @@ __device__ __forceinline__ void write_empty_partials(const PrefillArgs& a, int b
   if (half == 0) *reinterpret_cast<f32x2*>(a.ws_ml + 2 * slot) = f32x2{-INFINITY, 0.0f};
 }
 
-// SPLIT: the workgroup covers one key range of its query tile and writes an
-// fp32 partial (merged by mla_prefill_merge_kernel); otherwise all keys and
-// the bf16 output. Two instantiations, so the unsplit kernel carries none of
-// the split's code.
-template <bool SPLIT>
+// Padded variable-length batch: zero the output rows [r0, r1) of one (b, h)
+// slice (query rows past the sequence's own count), 16 bytes per store.
+__device__ __forceinline__ void zero_rows(uint16_t* out, int64_t r0, int64_t r1) {
+  constexpr int CHUNKS = DV * 2 / 16;  // 16-byte chunks per row
+  const int64_t n = (r1 - r0) * CHUNKS;
+  u32x4* base = reinterpret_cast<u32x4*>(out + r0 * DV);
+  for (int64_t c = threadIdx.x; c < n; c += NT) base[c] = u32x4{0, 0, 0, 0};
+}
+
+enum { kDense = 0, kSplit = 1, kVarlen = 2 };
+
+// Padded variable-length batch: sequence b's query count and cached keys,
+// clamped as the kernel uses them (T to [0, Tst], past to [0, Sst - T]).
+__device__ __forceinline__ void seq_lens_of(const PrefillArgs& a, int b, int64_t& T, int64_t& past) {
+  const int64_t tq = a.q_lens[b], pl = a.past_lens[b];
+  T = tq < 0 ? 0 : (tq > a.T ? a.T : tq);
+  past = pl < 0 ? 0 : (pl > a.S - T ? a.S - T : pl);
+}
+
+// Beyond this batch size the sequences are taken in index order.
+constexpr int kMaxRankedBatch = 1024;
+
+// The sequence at position r when sequences are ordered by visible (query,
+// key) pairs, most first (ties by index), so the longest jobs start first.
+// Each thread ranks a few sequences against all others; the one whose rank is
+// r publishes itself. All threads of the workgroup must call it.
+__device__ __forceinline__ int seq_at_rank(const PrefillArgs& a, int r) {
+  __shared__ int s_seq;
+  if (a.B > kMaxRankedBatch) return r;
+  for (int t = threadIdx.x; t < a.B; t += NT) {
+    int64_t T, P;
+    seq_lens_of(a, t, T, P);
+    const int64_t wt = T * P + T * (T + 1) / 2;
+    int rank = 0;
+    for (int u = 0; u < a.B; ++u) {
+      int64_t Tu, Pu;
+      seq_lens_of(a, u, Tu, Pu);
+      const int64_t wu = Tu * Pu + Tu * (Tu + 1) / 2;
+      rank += (wu > wt || (wu == wt && u < t)) ? 1 : 0;
+    }
+    if (rank == r) s_seq = t;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(s_seq);
+}
+
+// MODE kSplit: the workgroup covers one key range of its query tile and writes
+// an fp32 partial (merged by mla_prefill_merge_kernel). kDense: all keys and
+// the bf16 output. kVarlen: as kDense, with each sequence's query and key
+// counts read from device memory and the padded query rows set to zero. One
+// instantiation each, so the dense kernel carries none of the others' code.
+template <int MODE>
 __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
+  constexpr bool SPLIT = MODE == kSplit;
+  constexpr bool VARLEN = MODE == kVarlen;
   // separate LDS objects per buffer so the compiler can tell an in-flight copy
   // into one from reads of another
   __shared__ __attribute__((aligned(1024))) char kbuf0[K_BYTES];
@@ -378,7 +429,25 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   // (longest-job-first); otherwise head by head, heaviest tile first, so a
   // head's K/V streams through the XCD's L2 for all its tiles at once.
   int bh, qt, sp = 0;
-  {
+  if (VARLEN) {
+    // (b, h) groups dealt round-robin over the XCDs (each XCD gets H/8 heads
+    // of every sequence when H is a multiple of 8, so the XCDs stay even
+    // whatever the lengths); each XCD runs its groups longest sequence first,
+    // a group's query tiles back to back (its K/V streams through that XCD's
+    // L2 once), heaviest tile first.
+    const int G = a.B * a.H;
+    int gi, t;
+    if (G % 8 == 0) {
+      gi = (wg / 8 / a.ntiles) * 8 + wg % 8;
+      t = (wg / 8) % a.ntiles;
+    } else {
+      gi = wg / a.ntiles;
+      t = wg % a.ntiles;
+    }
+    const int seq = seq_at_rank(a, gi / a.H);
+    bh = seq * a.H + gi % a.H;
+    qt = a.ntiles - 1 - t;
+  } else {
     const int per = nwg / 8, i = wg / 8;
     const bool uneven = 2 * (a.past_len + (int64_t)BM) < a.past_len + (int64_t)a.T;
     if (SPLIT) {
@@ -401,18 +470,31 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   }
   const int b = bh / a.H;
   const int q0 = qt * BM;
+  // Tst / Sst: rows per (b, h) slice of the queries and output / of the keys.
+  // T, S_seq, past: this sequence's query count, key count and cached keys
+  // (the same as the slice sizes except for a padded variable-length batch).
+  const int64_t Tst = a.T, Sst = a.S;
+  int64_t T = a.T, S_seq = a.S, past = a.past_len;
+  if (VARLEN) {
+    seq_lens_of(a, b, T, past);
+    S_seq = past + T;
+    if (q0 >= T) {  // every row of this tile is padding
+      const int64_t r1 = q0 + BM < Tst ? q0 + BM : Tst;
+      zero_rows(a.out + (int64_t)bh * Tst * DV, q0, r1);
+      return;
+    }
+  }
 
   Geo geo;
   const int tid = threadIdx.x;
   geo.lane = tid & 63;
   geo.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = geo.lane, hi = lane >> 5, l32 = lane & 31;
-  const int64_t T = a.T;
   const int64_t q0w = q0 + geo.wave * QW;
 
   // ---- key range of the workgroup: tiles [kt0, kt1) of [0, P + last query + 1)
   const int64_t q_last = (q0 + BM < T ? q0 + BM : T) - 1;
-  const int nblocks_all = (int)((a.past_len + q_last + 1 + BN - 1) / BN);
+  const int nblocks_all = (int)((past + q_last + 1 + BN - 1) / BN);
   int kt0 = 0, kt1 = nblocks_all;
   if (SPLIT) {
     kt0 = sp * a.tiles_per_split;
@@ -427,11 +509,11 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   // and the last key query i sees is P + i with P = past_len - k0 (< 0 when the
   // query sees no key of this range).
   const int64_t k0 = (int64_t)kt0 * BN;
-  geo.S = a.S - k0;
-  geo.P = a.past_len - k0;
-  geo.kn_g = a.k_nope + (int64_t)bh * a.S * DN + k0 * DN;
-  geo.kp_g = a.k_pe + (int64_t)b * a.S * DR + k0 * DR;
-  geo.v_g = a.v + (int64_t)bh * a.S * DV + k0 * DV;
+  geo.S = S_seq - k0;
+  geo.P = past - k0;
+  geo.kn_g = a.k_nope + (int64_t)bh * Sst * DN + k0 * DN;
+  geo.kp_g = a.k_pe + (int64_t)b * Sst * DR + k0 * DR;
+  geo.v_g = a.v + (int64_t)bh * Sst * DV + k0 * DV;
   geo.kn.init(geo.wave, geo.lane);
   geo.kp.init(geo.wave, geo.lane);
   geo.vv.init(geo.wave, geo.lane);
@@ -451,8 +533,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   {
     const int64_t myq = q0w + l32;
     const bool ok = myq < T;
-    const uint16_t* qn = a.q_nope + ((int64_t)bh * T + myq) * DN + 8 * hi;
-    const uint16_t* qp = a.q_pe + ((int64_t)bh * T + myq) * DR + 8 * hi;
+    const uint16_t* qn = a.q_nope + ((int64_t)bh * Tst + myq) * DN + 8 * hi;
+    const uint16_t* qp = a.q_pe + ((int64_t)bh * Tst + myq) * DR + 8 * hi;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) qf[kk] = as_bf16x8(ok ? ldg16(qn + 16 * kk) : u32x4{0, 0, 0, 0});
 #pragma unroll
@@ -563,7 +645,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
     const float l_tot = sum_pair32(acc.l_run);
     const int64_t myq = q0w + l32;
     if (myq >= T) return;
-    const int64_t slot = ((int64_t)bh * T + myq) * a.nsplit + sp;
+    const int64_t slot = ((int64_t)bh * Tst + myq) * a.nsplit + sp;
     float* po = a.ws_o + slot * DV;
 #pragma unroll
     for (int n = 0; n < 4; ++n)
@@ -577,12 +659,15 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
     return;
   }
 
-  // ---- epilogue: divide by the full row sum and store bf16
-  if (!wave_live) return;
-  const float inv = 1.0f / sum_pair32(acc.l_run);
+  // ---- epilogue: divide by the full row sum and store bf16; in a padded
+  // batch, rows past the sequence's query count (still inside the slice) get 0
   const int64_t myq = q0w + l32;
-  if (myq >= T) return;
-  uint16_t* out_row = a.out + ((int64_t)bh * T + myq) * DV;
+  const bool pad_row = VARLEN && myq >= T && myq < Tst;
+  if (!wave_live && !pad_row) return;
+  float inv = 0.0f;
+  if (wave_live) inv = 1.0f / sum_pair32(acc.l_run);
+  if (myq >= T && !pad_row) return;
+  uint16_t* out_row = a.out + ((int64_t)bh * Tst + myq) * DV;
 #pragma unroll
   for (int n = 0; n < 4; ++n)
 #pragma unroll
@@ -590,13 +675,14 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
       const int dv0 = 32 * n + 8 * gg + 4 * hi;
       bf16x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc.o[n][4 * gg + e] * inv);
+      for (int e = 0; e < 4; ++e) w[e] = pad_row ? (__bf16)0.0f : (__bf16)(acc.o[n][4 * gg + e] * inv);
       *reinterpret_cast<bf16x4*>(out_row + dv0) = w;
     }
 }
 
-__global__ __launch_bounds__(NT, 2) void mla_prefill_kernel(PrefillArgs a) { prefill_body<false>(a); }
-__global__ __launch_bounds__(NT, 2) void mla_prefill_split_kernel(PrefillArgs a) { prefill_body<true>(a); }
+__global__ __launch_bounds__(NT, 2) void mla_prefill_kernel(PrefillArgs a) { prefill_body<kDense>(a); }
+__global__ __launch_bounds__(NT, 2) void mla_prefill_split_kernel(PrefillArgs a) { prefill_body<kSplit>(a); }
+__global__ __launch_bounds__(NT, 2) void mla_prefill_varlen_kernel(PrefillArgs a) { prefill_body<kVarlen>(a); }
 
 // Log-sum-exp merge of the key-range partials of every query row: one wave
 // per row, lane l owns output dims 2l, 2l+1.
@@ -628,7 +714,9 @@ __global__ __launch_bounds__(256) void mla_prefill_merge_kernel(PrefillArgs a) {
 int prefill_block_m() { return BM; }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-  if (a.nsplit <= 1) {
+  if (a.q_lens != nullptr) {
+    hipLaunchKernelGGL(mla_prefill_varlen_kernel, dim3(a.B * a.H * a.ntiles), dim3(NT), 0, stream, a);
+  } else if (a.nsplit <= 1) {
     hipLaunchKernelGGL(mla_prefill_kernel, dim3(a.B * a.H * a.ntiles), dim3(NT), 0, stream, a);
   } else {
     hipLaunchKernelGGL(mla_prefill_split_kernel, dim3(a.B * a.H * a.ntiles * a.nsplit), dim3(NT), 0,

@@ -34,9 +34,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from seeded_inputs import (LATENT_WORKLOADS, PAGED_WORKLOADS, SHARD_WORKLOADS, VARLEN_WORKLOADS,  # noqa: E402
-                           WORKLOADS,
+                           VARLEN_PREFILL_WORKLOADS, WORKLOADS,
                            device_inputs, host_inputs, latent_device_inputs, latent_host_inputs,
-                           paged_device_inputs, paged_layout, varlen_seq_lens)
+                           paged_device_inputs, paged_layout, varlen_prefill_lens, varlen_seq_lens)
 
 METRIC = "prefill attn TFLOP/s & decode HBM GB/s, 1 MI355X, as fraction of peak"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
@@ -95,6 +95,12 @@ def prefill_flops(wl) -> int:
     T, P = wl.T, wl.past_len
     n_vis = T * P + T * (T + 1) // 2
     return 2 * wl.B * wl.H * (192 + 128) * n_vis
+
+
+def varlen_prefill_flops(wl, q_lens, past_lens) -> int:
+    """Each sequence's own visible (query, key) pairs; padded rows count nothing."""
+    n_vis = sum(int(t) * int(p) + int(t) * (int(t) + 1) // 2 for t, p in zip(q_lens, past_lens))
+    return 2 * wl.H * (192 + 128) * n_vis
 
 
 def source_hash(kernel: str) -> str:
@@ -400,6 +406,42 @@ def run_prefill(wl, steps, warmup, seed=0):
     return res, x
 
 
+def run_prefill_varlen(wl, steps, warmup, seed=0):
+    """mla_attn_prefill_varlen on a right-padded batch of chunked prefills
+    (inputs drawn on the device)."""
+    import torch
+    import attention_mla_causal_amd as mla
+    dev = torch.device("cuda:0")
+    tq, pl = varlen_prefill_lens(wl.B, wl.max_q, wl.max_kv, seed=seed)
+    flops = varlen_prefill_flops(wl, tq, pl)
+    log(f"[bench] {wl.name}: B={wl.B} H={wl.H} max_q={wl.max_q} max_kv={wl.max_kv} "
+        f"sum(q_lens)={int(tq.sum())} steps={steps}")
+    d = device_inputs(wl.padded(), dev, seed=seed)
+    ql = torch.as_tensor(tq, device=dev)
+    pp = torch.as_tensor(pl, device=dev)
+    out = torch.empty((wl.B, wl.H, wl.max_q, 128), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        mla.mla_attn_prefill_varlen(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], ql, pp,
+                                    wl.softmax_scale, out=out)
+
+    ms, wall_ms = time_eager(step, steps, warmup)
+    tfs = flops / (ms * 1e-3) / 1e12
+    kernel = "mla_prefill_kernel"
+    res = {
+        "workload": wl.name, "B": wl.B, "H": wl.H, "max_q_len": wl.max_q, "max_kv_len": wl.max_kv,
+        "q_lens": tq.tolist(), "past_lens": pl.tolist(), "std": wl.std, "inputs": "device",
+        "steps": steps, "timing": "eager", "ms_per_step": ms, "wall_ms_per_step": wall_ms,
+        "value": tfs, "unit": "TFLOP/s", "algorithmic_flops": flops,
+        "roofline": {"bound": "mfma", "kernel": "mla_prefill_varlen_kernel", "achieved": tfs,
+                     "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": tfs / MFMA_BF16_PEAK_TFS,
+                     "traffic": measured_traffic(kernel, wl.name)},
+    }
+    del d
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline_decode(wl, seconds):
     """The fp64 oracle on the whole decode workload, repeated for ~`seconds`."""
     from oracle import mla_attention
@@ -466,7 +508,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_p1000",
                     choices=sorted(WORKLOADS) + sorted(LATENT_WORKLOADS) + sorted(VARLEN_WORKLOADS)
-                    + sorted(PAGED_WORKLOADS))
+                    + sorted(PAGED_WORKLOADS) + sorted(VARLEN_PREFILL_WORKLOADS))
     ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -501,7 +543,11 @@ def main():
         sys.exit(2)
 
     torch.cuda.synchronize()
-    if args.workload in PAGED_WORKLOADS:
+    if args.workload in VARLEN_PREFILL_WORKLOADS:
+        wl = VARLEN_PREFILL_WORKLOADS[args.workload]
+        head = run_prefill_varlen(wl, args.steps, args.warmup)
+        cpu = None
+    elif args.workload in PAGED_WORKLOADS:
         wl = PAGED_WORKLOADS[args.workload]
         head = run_paged(wl, args.steps, args.warmup, graph=not args.eager)
         cpu = None
@@ -549,6 +595,9 @@ def main():
         for name, w in PAGED_WORKLOADS.items():
             if name != wl.name:
                 workloads[name] = run_paged(w, args.extra_steps, 3)
+        for name, w in VARLEN_PREFILL_WORKLOADS.items():
+            if name != wl.name:
+                workloads[name] = run_prefill_varlen(w, args.extra_steps, 2)
         for name, w in LATENT_WORKLOADS.items():
             if name == wl.name:
                 continue

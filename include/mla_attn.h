@@ -105,6 +105,40 @@ mla_status mla_attn_prefill_ws(const void* q_nope, const void* q_pe,
                                float softmax_scale, void* stream);
 
 /*
+ * Prefill of a padded batch whose sequences differ in length. The "Causal
+ * mask" page ("Construct causal mask") numbers positions from each cached
+ * length and passes the caller's 2D padding mask (1 keeps a position, 0 pads
+ * it) with that length to the 4D mask builder. Here both the queries and the
+ * keys of each sequence are right-padded: sequence b has Tb = q_lens[b] new
+ * queries, rows [0, Tb) of its max_q_len query rows, over Pb = past_lens[b]
+ * cached keys; its keys are rows [0, Pb + Tb) of its max_kv_len key rows, and
+ * its query i (at position Pb + i) sees keys 0 .. Pb + i, as mla_attn_prefill
+ * with T = Tb, past_len = Pb on that sequence alone.
+ *
+ *   q_nope [B, H, max_q_len, 128], q_pe [B, H, max_q_len, 64]      bf16
+ *   k_nope [B, H, max_kv_len, 128], k_pe [B, 1, max_kv_len, 64],
+ *   v      [B, H, max_kv_len, 128]                                   bf16
+ *   q_lens, past_lens  [B] int32 in device memory, 4-byte aligned; read by
+ *                      the kernel only (the host never looks at them), so a
+ *                      captured graph can replay the call with new lengths
+ *   out    [B, H, max_q_len, 128]                                     bf16
+ *
+ * Padded query rows (i >= Tb) are written as 0: they attend to nothing. Padded
+ * rows of the inputs are never read. On the device Tb is clamped to
+ * [0, max_q_len] and Pb to [0, max_kv_len - Tb], so no row outside the slices
+ * is read whatever the arrays hold. max_q_len > max_kv_len is MLA_ERR_SHAPE
+ * (a sequence's own keys follow its cache); max_kv_len is at most 8,388,607.
+ * B == 0, H == 0 or max_q_len == 0 is a valid empty call. Other errors as for
+ * mla_attn_prefill. One kernel is enqueued on `stream`.
+ */
+mla_status mla_attn_prefill_varlen(const void* q_nope, const void* q_pe,
+                                   const void* k_nope, const void* k_pe,
+                                   const void* v, const int32_t* q_lens,
+                                   const int32_t* past_lens, void* out,
+                                   int32_t B, int32_t H, int32_t max_q_len,
+                                   int32_t max_kv_len, float softmax_scale, void* stream);
+
+/*
  * Bytes of device workspace mla_attn_decode needs for (B, H, S). A pure
  * function of its arguments (no device query); 0 means no workspace is
  * needed. Returns 0 for negative sizes.

@@ -274,6 +274,43 @@ def varlen_seq_lens(B: int, cap: int, seed: int = 0) -> np.ndarray:
     return lens
 
 
+@dataclass(frozen=True)
+class VarlenPrefillWorkload:
+    """A right-padded batch of chunked prefills: sequence b has T_b new
+    queries over P_b cached keys, in slices of max_q query rows and max_kv key
+    rows."""
+    name: str
+    B: int
+    H: int
+    max_q: int
+    max_kv: int
+    std: float = 1.0
+    softmax_scale: float = float(np.float32(192.0 ** -0.5))
+
+    def padded(self) -> Workload:
+        """The tensors: a prefill workload with T = max_q, S = max_kv."""
+        return Workload(self.name, self.B, self.H, self.max_q, self.max_kv - self.max_q, self.std)
+
+
+# Eight chunked-prefill requests batched together, the longest being the
+# chunked-prefill workload's own (2048 new queries over 14336 cached keys).
+VARLEN_PREFILL_WORKLOADS = {
+    "varlen_prefill": VarlenPrefillWorkload("varlen_prefill", B=8, H=64, max_q=2048, max_kv=16384,
+                                            std=float(np.sqrt(2.0))),
+}
+
+
+def varlen_prefill_lens(B: int, max_q: int, max_kv: int, seed: int = 0):
+    """(q_lens, past_lens) int32 [B]: T_b uniform in [1, max_q], P_b uniform in
+    [0, max_kv - max_q]; the first sequence takes both maxima."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 3])))
+    tq = g.integers(1, max_q + 1, size=B).astype(np.int32)
+    pl = g.integers(0, max_kv - max_q + 1, size=B).astype(np.int32)
+    if B:
+        tq[0], pl[0] = max_q, max_kv - max_q
+    return tq, pl
+
+
 PAGED_TENSORS = ("q_nope", "q_pe", "k_nope_pages", "k_pe_pages", "v_pages",
                  "k_nope_new", "k_pe_new", "v_new")
 

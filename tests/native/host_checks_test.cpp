@@ -153,6 +153,28 @@ int main() {
     EXPECT(check_prefill_ws(p, p, p, p, p, p, p, need - 1, 1, 8, 2048, 16384, 14336, sc, 128, 32, &pl).status == MLA_ERR_WORKSPACE);
     EXPECT(check_prefill_ws(p, p, p, p, p, p, nullptr, 0, 1, 64, 2048, 16384, 14336, sc, 128, 32, &pl).status == MLA_OK);
   }
+  // padded variable-length prefill: sizes, pointers (lengths need 4-byte
+  // alignment only), scale and limits
+  {
+    const void* l4 = reinterpret_cast<const void*>(uintptr_t(0x10004));
+    EXPECT(check_prefill_varlen(p, p, p, p, p, p, p, p, 8, 64, 2048, 16384, sc, 128).status == MLA_OK);
+    EXPECT(check_prefill_varlen(p, p, p, p, p, l4, l4, p, 8, 64, 2048, 16384, sc, 128).status == MLA_OK);
+    EXPECT(check_prefill_varlen(p, p, p, p, p, p, p, p, 8, 64, 2049, 2048, sc, 128).status == MLA_ERR_SHAPE);
+    EXPECT(check_prefill_varlen(p, p, p, p, p, p, p, p, -1, 64, 16, 16, sc, 128).status == MLA_ERR_SHAPE);
+    EXPECT(check_prefill_varlen(p, p, p, p, p, p, p, p, 1, 64, 16, 8388608, sc, 128).status == MLA_ERR_SHAPE);
+    EXPECT(check_prefill_varlen(p, p, p, p, p, p, p, p, 1, 64, 16, 8388607, sc, 128).status == MLA_OK);
+    EXPECT(check_prefill_varlen(p, p, p, p, p, p, p, p, 1, 64, 16, 16, 0.0f, 128).status == MLA_ERR_SCALE);
+    const CheckResult e = check_prefill_varlen(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                               nullptr, nullptr, 4, 64, 0, 100, sc, 128);
+    EXPECT(e.status == MLA_OK && e.empty);
+    for (int i = 0; i < 8; ++i) {
+      const void* q[8] = {p, p, p, p, p, p, p, p};
+      q[i] = nullptr;
+      EXPECT(check_prefill_varlen(q[0], q[1], q[2], q[3], q[4], q[5], q[6], q[7], 2, 4, 16, 32, sc, 128).status == MLA_ERR_NULL);
+      q[i] = reinterpret_cast<const void*>(uintptr_t(0x10002));
+      EXPECT(check_prefill_varlen(q[0], q[1], q[2], q[3], q[4], q[5], q[6], q[7], 2, 4, 16, 32, sc, 128).status == MLA_ERR_ALIGN);
+    }
+  }
   // latent decode: S limit (1024-byte rows in a 32-bit byte range)
   {
     LatentPlan lp;

@@ -36,6 +36,7 @@ def test_header_declares_the_boundary():
         "mla_attn_decode_varlen", "mla_attn_decode_varlen_workspace_bytes",
         "mla_attn_decode_paged", "mla_attn_decode_paged_workspace_bytes",
         "mla_attn_prefill_ws", "mla_attn_prefill_workspace_bytes",
+        "mla_attn_prefill_varlen",
         "mla_last_error", "mla_status_string"])
 
 
@@ -233,3 +234,29 @@ def test_prefill_ws_errors(lib):
         assert call(ptrs, ALIGNED, need, 1, 2, 256, 4096, 3840) == 1
     assert "mla_attn_prefill_ws" in lib.mla_last_error().decode()
     assert call([None] * 6, None, 0, 0, 2, 256, 4096, 3840) == 0           # empty batch
+
+
+def test_prefill_varlen_errors(lib):
+    ok = [ALIGNED] * 8   # q_nope, q_pe, k_nope, k_pe, v, q_lens, past_lens, out
+
+    def call(ptrs, B, H, Tmax, Smax, scale=SC):
+        return lib.mla_attn_prefill_varlen(*ptrs, B, H, Tmax, Smax, scale, None)
+
+    assert call(ok, 2, 64, 2049, 2048) == 2                 # a sequence's keys follow its cache
+    assert "exceeds max_kv_len" in lib.mla_last_error().decode()
+    assert call(ok, -1, 64, 16, 16) == 2
+    assert call(ok, 1, 64, 16, 8388608) == 2                # past the 32-bit byte range of a slice
+    for i in range(8):
+        ptrs = list(ok)
+        ptrs[i] = None
+        assert call(ptrs, 2, 4, 16, 32) == 1
+        ptrs[i] = MISALIGNED
+        assert call(ptrs, 2, 4, 16, 32) == 3
+    # the length arrays need only 4-byte alignment: the call then stops at the scale
+    ptrs = list(ok)
+    ptrs[5] = ptrs[6] = ctypes.c_void_p(0x10004)
+    assert call(ptrs, 2, 4, 16, 32, float("nan")) == 4
+    assert call(ok, 2, 4, 16, 32, -1.0) == 4
+    assert "mla_attn_prefill_varlen" in lib.mla_last_error().decode()
+    assert call([None] * 8, 2, 4, 0, 32) == 0               # no query rows: empty call
+    assert call([None] * 8, 0, 4, 16, 32) == 0
