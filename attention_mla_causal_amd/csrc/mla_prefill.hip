@@ -377,25 +377,32 @@ __device__ __forceinline__ void seq_lens_of(const PrefillArgs& a, int b, int64_t
   past = pl < 0 ? 0 : (pl > a.S - T ? a.S - T : pl);
 }
 
-// Beyond this batch size the sequences are taken in index order.
-constexpr int kMaxRankedBatch = 1024;
+// Beyond this batch size (one sequence per thread) the sequences are taken
+// in index order.
+constexpr int kMaxRankedBatch = NT;
 
 // The sequence at position r when sequences are ordered by visible (query,
 // key) pairs, most first (ties by index), so the longest jobs start first.
-// Each thread ranks a few sequences against all others; the one whose rank is
-// r publishes itself. All threads of the workgroup must call it.
+// Thread t computes sequence t's pair count into LDS, then ranks it against
+// all others there; the one whose rank is r publishes itself. All threads of
+// the workgroup must call it.
 __device__ __forceinline__ int seq_at_rank(const PrefillArgs& a, int r) {
+  __shared__ int64_t s_work[kMaxRankedBatch];
   __shared__ int s_seq;
   if (a.B > kMaxRankedBatch) return r;
-  for (int t = threadIdx.x; t < a.B; t += NT) {
+  const int t = threadIdx.x;
+  int64_t wt = 0;
+  if (t < a.B) {
     int64_t T, P;
     seq_lens_of(a, t, T, P);
-    const int64_t wt = T * P + T * (T + 1) / 2;
+    wt = T * P + T * (T + 1) / 2;
+    s_work[t] = wt;
+  }
+  __syncthreads();
+  if (t < a.B) {
     int rank = 0;
     for (int u = 0; u < a.B; ++u) {
-      int64_t Tu, Pu;
-      seq_lens_of(a, u, Tu, Pu);
-      const int64_t wu = Tu * Pu + Tu * (Tu + 1) / 2;
+      const int64_t wu = s_work[u];
       rank += (wu > wt || (wu == wt && u < t)) ? 1 : 0;
     }
     if (rank == r) s_seq = t;

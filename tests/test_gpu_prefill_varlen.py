@@ -92,6 +92,23 @@ def test_edge_cases(B, H, Tmax, Smax, tq, pp):
     assert_parity(to_host_f64(out), _oracle(x, eq, ep), "prefill varlen edge")
 
 
+@pytest.mark.parametrize("B", [256, 300])
+def test_many_sequences(B):
+    """Up to 256 sequences the workgroups rank them by work; beyond that they
+    are taken in index order: both orders cover every row."""
+    H, Tmax, Smax = 1, 40, 100
+    g = np.random.default_rng(B)
+    tq = g.integers(0, Tmax + 1, size=B)
+    pp = g.integers(0, Smax - Tmax + 1, size=B)
+    log(f"case prefill varlen many B={B} H={H} Tmax={Tmax} Smax={Smax}")
+    x = _inputs(B, H, Tmax, Smax, B, tq, pp)
+    out = _gpu(upload(x), tq, pp)
+    bits = to_host_bits(out)
+    for b in range(B):
+        assert not np.any(bits[b, :, tq[b]:]), b
+    assert_parity(to_host_f64(out), _oracle(x, tq, pp), f"prefill varlen B={B}")
+
+
 @pytest.mark.parametrize("B,H,T,P", [(2, 4, 300, 77), (1, 64, 256, 1024)])
 def test_full_lengths_equal_dense_prefill(B, H, T, P):
     """Every sequence at the slice sizes: bit-identical to mla_attn_prefill."""
