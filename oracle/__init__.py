@@ -33,3 +33,4 @@ from .mla_paged import (  # noqa: F401
     mla_decode_paged,
 )
 from .mla_prefill_varlen import mla_prefill_varlen  # noqa: F401
+from .mla_masked import mla_attention_masked, visible_keys  # noqa: F401
