@@ -38,6 +38,8 @@ SIGNATURES = {
     "mla_attn_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "mla_attn_prefill_ws": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_attn_prefill_varlen": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _F32, _VP]),
+    "mla_attn_prefill_masked": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _F32, _VP]),
+    "mla_attn_decode_masked": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "mla_attn_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_attn_decode_varlen_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
@@ -205,6 +207,69 @@ def mla_attn_prefill_varlen(q_nope, q_pe, k_nope, k_pe, v, q_lens, past_lens, so
         q_lens.data_ptr(), past_lens.data_ptr(), out.data_ptr(), B, H, Tmax, Smax,
         float(softmax_scale), _stream_handle(q_nope.device))
     _raise_for(st, "mla_attn_prefill_varlen")
+    return out
+
+
+def _check_mask(attn_mask, B, S, device):
+    import torch
+    if not (isinstance(attn_mask, torch.Tensor) and attn_mask.dtype in (torch.uint8, torch.bool)
+            and attn_mask.is_cuda and attn_mask.is_contiguous() and tuple(attn_mask.shape) == (B, S)
+            and attn_mask.device == device):
+        raise ValueError(f"attn_mask must be a contiguous uint8 or bool tensor of shape {(B, S)} on {device}")
+
+
+def mla_attn_prefill_masked(q_nope, q_pe, k_nope, k_pe, v, attn_mask, past_len: int,
+                            softmax_scale: float, out=None):
+    """mla_attn_prefill under the caller's 2D padding mask attn_mask [B, S]
+    (uint8 or bool on the GPU, nonzero keeps key j of sequence b). Query i sees
+    key j iff j <= past_len + i and the mask keeps j; a query with no visible
+    key gives a zero row."""
+    import torch
+
+    B, H, T, S = _shapes(q_nope, q_pe, k_nope, k_pe, v)
+    _check_mask(attn_mask, B, S, q_nope.device)
+    if out is None:
+        out = torch.empty((B, H, T, V_HEAD_DIM), dtype=torch.bfloat16, device=q_nope.device)
+    else:
+        _check_tensor(out, "out")
+        if tuple(out.shape) != (B, H, T, V_HEAD_DIM) or out.device != q_nope.device:
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, T, V_HEAD_DIM)}")
+    st = _lib.mla_attn_prefill_masked(
+        q_nope.data_ptr(), q_pe.data_ptr(), k_nope.data_ptr(), k_pe.data_ptr(), v.data_ptr(),
+        attn_mask.data_ptr(), out.data_ptr(), B, H, T, S, int(past_len), float(softmax_scale),
+        _stream_handle(q_nope.device))
+    _raise_for(st, "mla_attn_prefill_masked")
+    return out
+
+
+def mla_attn_decode_masked(q_nope, q_pe, k_nope, k_pe, v, attn_mask, past_len: int,
+                           softmax_scale: float, out=None, workspace=None):
+    """mla_attn_decode under the caller's 2D padding mask attn_mask [B, S]
+    (uint8 or bool on the GPU, nonzero keeps); a sequence with no visible key
+    gives a zero row."""
+    import torch
+
+    B, H, T, S = _shapes(q_nope, q_pe, k_nope, k_pe, v)
+    if T != 1:
+        raise ValueError(f"decode takes one query per sequence, got T={T}")
+    _check_mask(attn_mask, B, S, q_nope.device)
+    if out is None:
+        out = torch.empty((B, H, 1, V_HEAD_DIM), dtype=torch.bfloat16, device=q_nope.device)
+    else:
+        _check_tensor(out, "out")
+        if tuple(out.shape) != (B, H, 1, V_HEAD_DIM) or out.device != q_nope.device:
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, 1, V_HEAD_DIM)}")
+    need = mla_attn_decode_workspace_bytes(B, H, S)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_nope.device)
+    if not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    st = _lib.mla_attn_decode_masked(
+        q_nope.data_ptr(), q_pe.data_ptr(), k_nope.data_ptr(), k_pe.data_ptr(), v.data_ptr(),
+        attn_mask.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), B, H, S, int(past_len), float(softmax_scale),
+        _stream_handle(q_nope.device))
+    _raise_for(st, "mla_attn_decode_masked")
     return out
 
 

@@ -46,6 +46,7 @@ struct DecodeExtras {
   const void* kn_new = nullptr;
   const void* kp_new = nullptr;
   const void* v_new = nullptr;
+  const uint8_t* key_mask = nullptr;  // [B, S] 2D padding mask
 };
 
 // Every decode entry point: fill the arguments from a checked plan and launch.
@@ -64,6 +65,7 @@ mla_status launch_decode_call(const char* where, const void* q_nope, const void*
   a.kn_new = static_cast<const uint16_t*>(x.kn_new);
   a.kp_new = static_cast<const uint16_t*>(x.kp_new);
   a.v_new = static_cast<const uint16_t*>(x.v_new);
+  a.key_mask = x.key_mask;
   a.cap = cap;
   a.q_nope = static_cast<const uint16_t*>(q_nope);
   a.q_pe = static_cast<const uint16_t*>(q_pe);
@@ -211,6 +213,36 @@ mla_status mla_attn_prefill_varlen(const void* q_nope, const void* q_pe, const v
   return MLA_OK;
 }
 
+mla_status mla_attn_prefill_masked(const void* q_nope, const void* q_pe, const void* k_nope,
+                                   const void* k_pe, const void* v, const uint8_t* attn_mask,
+                                   void* out, int32_t B, int32_t H, int32_t T, int32_t S,
+                                   int32_t past_len, float softmax_scale, void* stream) {
+  mla::CheckResult r = mla::check_prefill(q_nope, q_pe, k_nope, k_pe, v, out, B, H, T, S, past_len,
+                                          softmax_scale, mla::prefill_block_m());
+  if (r.status == MLA_OK && !r.empty && attn_mask == nullptr)
+    r = mla::fail(MLA_ERR_NULL, "attn_mask is NULL");
+  if (r.status != MLA_OK) return report("mla_attn_prefill_masked", r);
+  if (r.empty) return MLA_OK;
+  mla::PrefillArgs a{};  // one workgroup per query tile covers all its keys
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.k_nope = static_cast<const uint16_t*>(k_nope);
+  a.k_pe = static_cast<const uint16_t*>(k_pe);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<uint16_t*>(out);
+  a.key_mask = attn_mask;
+  a.B = B;
+  a.H = H;
+  a.T = T;
+  a.S = S;
+  a.past_len = past_len;
+  a.ntiles = (int32_t)((T + mla::prefill_block_m() - 1) / mla::prefill_block_m());
+  a.scale_log2 = softmax_scale * kLog2e;
+  const hipError_t e = mla::launch_prefill(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error("mla_attn_prefill_masked", e);
+  return MLA_OK;
+}
+
 size_t mla_attn_decode_workspace_bytes(int32_t B, int32_t H, int32_t S) {
   return mla::plan_decode(B, H, S).workspace_bytes;
 }
@@ -227,6 +259,24 @@ mla_status mla_attn_decode(const void* q_nope, const void* q_pe, const void* k_n
   if (r.empty) return MLA_OK;
   return launch_decode_call("mla_attn_decode", q_nope, q_pe, k_nope, k_pe, v, DecodeExtras{},
                             out, workspace, plan, B, H, S, S, softmax_scale, stream);
+}
+
+mla_status mla_attn_decode_masked(const void* q_nope, const void* q_pe, const void* k_nope,
+                                  const void* k_pe, const void* v, const uint8_t* attn_mask,
+                                  void* out, void* workspace, size_t workspace_bytes, int32_t B,
+                                  int32_t H, int32_t S, int32_t past_len, float softmax_scale,
+                                  void* stream) {
+  mla::DecodePlan plan;
+  mla::CheckResult r = mla::check_decode(q_nope, q_pe, k_nope, k_pe, v, out, workspace,
+                                         workspace_bytes, B, H, S, past_len, softmax_scale, &plan);
+  if (r.status == MLA_OK && !r.empty && attn_mask == nullptr)
+    r = mla::fail(MLA_ERR_NULL, "attn_mask is NULL");
+  if (r.status != MLA_OK) return report("mla_attn_decode_masked", r);
+  if (r.empty) return MLA_OK;
+  DecodeExtras x;
+  x.key_mask = attn_mask;
+  return launch_decode_call("mla_attn_decode_masked", q_nope, q_pe, k_nope, k_pe, v, x, out,
+                            workspace, plan, B, H, S, S, softmax_scale, stream);
 }
 
 size_t mla_attn_decode_varlen_workspace_bytes(int32_t B, int32_t H, int32_t max_seq_len) {

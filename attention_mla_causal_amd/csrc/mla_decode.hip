@@ -104,7 +104,11 @@ __device__ __forceinline__ void merge_xor(float& m, float& l, float (&o)[8], int
   m = M;
 }
 
-__global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
+// MASKED: the caller's 2D padding mask hides keys (a.key_mask, [B, S] bytes,
+// nonzero keeps); one instantiation each, so the unmasked kernel carries none
+// of its code.
+template <bool MASKED>
+__device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   __shared__ float red_o[NW][DV];
   __shared__ float red_ml[NW][2];
 
@@ -213,6 +217,7 @@ __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
     u32x4 kn[KEYS_PER_LANE], vv[KEYS_PER_LANE];
     u32x2 kp[KEYS_PER_LANE];
     bool ok[KEYS_PER_LANE];
+    uint8_t keep[KEYS_PER_LANE];
     const uint16_t* kn_t;  // rows base .. base+31 are consecutive
     const uint16_t* v_t;
     const uint16_t* kp_t;
@@ -231,6 +236,7 @@ __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
     for (int u = 0; u < KEYS_PER_LANE; ++u) {
       const int64_t key = base + 4 * u + qq;
       ok[u] = key < s1;
+      if (MASKED) keep[u] = ok[u] ? a.key_mask[(int64_t)b * a.S + key] : 0;
       if (ok[u]) {
         kn[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kn_t + (4 * u + qq) * DN));
         kp[u] = *reinterpret_cast<const u32x2*>(kp_t + (4 * u + qq) * DR);
@@ -239,6 +245,15 @@ __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
         kn[u] = u32x4{0, 0, 0, 0};
         kp[u] = u32x2{0, 0};
         vv[u] = u32x4{0, 0, 0, 0};
+      }
+    }
+    if (MASKED) {
+      // a hidden key scores -inf below; its value row is cleared so that
+      // whatever it holds (NaN included) cannot reach the output
+#pragma unroll
+      for (int u = 0; u < KEYS_PER_LANE; ++u) {
+        ok[u] = ok[u] && keep[u] != 0;
+        if (!ok[u]) vv[u] = u32x4{0, 0, 0, 0};
       }
     }
     float t[KEYS_PER_LANE];
@@ -444,6 +459,9 @@ __global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) {
   }
 }
 
+__global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) { decode_body<false>(a); }
+__global__ __launch_bounds__(NT) void mla_decode_masked_kernel(DecodeArgs a) { decode_body<true>(a); }
+
 // Log-sum-exp merge of the nsplit partials of each (b, h): one wave per (b, h);
 // quarter-wave qq merges splits qq, qq+4, ..., then the quarters merge.
 __global__ __launch_bounds__(64) void mla_decode_combine_kernel(DecodeArgs a) {
@@ -485,7 +503,10 @@ __global__ __launch_bounds__(64) void mla_decode_combine_kernel(DecodeArgs a) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const int grid = a.B * a.H * a.nsplit;
-  hipLaunchKernelGGL(mla_decode_kernel, dim3(grid), dim3(NT), 0, stream, a);
+  if (a.key_mask != nullptr)
+    hipLaunchKernelGGL(mla_decode_masked_kernel, dim3(grid), dim3(NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL(mla_decode_kernel, dim3(grid), dim3(NT), 0, stream, a);
   if (a.nsplit > 1 && !a.fused)
     hipLaunchKernelGGL(mla_decode_combine_kernel, dim3(a.B * a.H), dim3(64), 0, stream, a);
   return hipGetLastError();

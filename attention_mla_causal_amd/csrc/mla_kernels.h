@@ -33,6 +33,8 @@ struct PrefillArgs {
   // device); past_len is unused.
   const int32_t* q_lens;   // [B]
   const int32_t* past_lens;  // [B]
+  // 2D padding mask [B, S] (nonzero keeps key j of sequence b), or null
+  const uint8_t* key_mask;
 };
 
 struct DecodeArgs {
@@ -59,6 +61,7 @@ struct DecodeArgs {
   int32_t fused;           // the last workgroup of each (b, h) merges the partials
   int32_t interleave;      // (b, h) -> XCD (b*H + h) % 8 (needs B*H % 8 == 0); else by sequence
   float scale_log2;
+  const uint8_t* key_mask; // [B, S] 2D padding mask (nonzero keeps key j of sequence b), or null
 };
 
 struct LatentArgs {

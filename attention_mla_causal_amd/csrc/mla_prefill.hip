@@ -367,7 +367,22 @@ __device__ __forceinline__ void zero_rows(uint16_t* out, int64_t r0, int64_t r1)
   for (int64_t c = threadIdx.x; c < n; c += NT) base[c] = u32x4{0, 0, 0, 0};
 }
 
-enum { kDense = 0, kSplit = 1, kVarlen = 2 };
+enum { kDense = 0, kSplit = 1, kVarlen = 2, kMasked = 3 };
+
+// The caller's 2D padding mask on one score tile. kbyte is this lane's mask
+// byte for key (lane % 32) of the tile; a ballot turns the 32 bytes into one
+// wave-uniform bit per key, and the lane hides its 16 keys (8g + 4hi + e) whose
+// bit is clear. A tile with every key kept costs the ballot and one compare.
+__device__ __forceinline__ void key_mask_tile(f32x16& sc, uint32_t kbyte, int hi) {
+  const uint32_t vis = (uint32_t)__ballot(kbyte != 0);
+  if (vis == 0xffffffffu) return;
+  const uint32_t m = vis >> (4 * hi);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int off = 8 * (r >> 2) + (r & 3);
+    if (!((m >> off) & 1u)) sc[r] = -INFINITY;
+  }
+}
 
 // Padded variable-length batch: sequence b's query count and cached keys,
 // clamped as the kernel uses them (T to [0, Tst], past to [0, Sst - T]).
@@ -420,6 +435,7 @@ template <int MODE>
 __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   constexpr bool SPLIT = MODE == kSplit;
   constexpr bool VARLEN = MODE == kVarlen;
+  constexpr bool MASKED = MODE == kMasked;
   // separate LDS objects per buffer so the compiler can tell an in-flight copy
   // into one from reads of another
   __shared__ __attribute__((aligned(1024))) char kbuf0[K_BYTES];
@@ -535,6 +551,22 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
 
   copy_k(geo, 0, kbuf0);
 
+  // ---- 2D padding mask: each lane fetches one byte per key tile, key
+  // (lane % 32) of the tile, two tiles ahead of its use (with the K copies);
+  // bytes past the sequence's keys read as 0 (buffer range check).
+  __amdgpu_buffer_rsrc_t mrs;
+  uint32_t km0 = 0, km1 = 0;  // mask bytes of even / odd tiles
+  auto load_km = [&](int t) -> uint32_t {
+    return __builtin_amdgcn_raw_buffer_load_b8(mrs, t * BN + (geo.lane & 31), 0, 0);
+  };
+  if (MASKED) {
+    const int64_t left = S_seq - k0;
+    mrs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.key_mask + (int64_t)b * Sst + k0), (short)0,
+                                            left > 0 ? (int)left : 0, 0x00020000);
+    km0 = load_km(0);
+    km1 = load_km(1);
+  }
+
   // ---- query fragments (B operand): 8 dims of the lane's query per K-step
   bf16x8 qf[12];
   {
@@ -583,6 +615,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   if (wave_live) {
     mfma_stream<-1, true, false>(sa, kbuf0, acc, vbuf0, ln, qf, pa, st, sb, pb, cl2);
     if (needs_mask(0)) mask_tile(sa, 0, lim, S, hi);
+    if (MASKED) key_mask_tile(sa, km0, hi);
   }
 
   // step 0: QK of tile 1 with the softmax of tile 0; no PV yet
@@ -590,6 +623,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   __syncthreads();
   if (2 < nblocks) copy_k(geo, 2, kbuf0);
   copy_v(geo, 0, vbuf0);
+  if (MASKED) km0 = load_km(2);
   if (wave_live) {
     st.mx = -INFINITY;
     st.psum = 0.0f;
@@ -597,12 +631,13 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
     smx_rest<12, SMX_SLOTS>(st, sa, pa, acc, cl2);
     rescale_o(acc, st.alpha);
     if (needs_mask(1)) mask_tile(sb, BN, lim, S, hi);
+    if (MASKED) key_mask_tile(sb, km1, hi);
   }
 
   // steps j >= 1
   auto step = [&](int j, f32x16& cur, f32x16& nxt, bf16x8 (&pcur)[2],
                   const bf16x8 (&pprev)[2], const char* knxt, const char* vprev, char* kfree,
-                  char* vfree) {
+                  char* vfree, uint32_t& km_apply, uint32_t& km_load) {
     // The two workgroups sharing a CU take turns at the higher issue priority.
     // Left to age-based arbitration, the older one runs ~25% faster per step,
     // and the round of workgroups that follows ends unevenly.
@@ -614,6 +649,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
     __syncthreads();  // K_{j+1} and V_{j-1} have landed; kfree and vfree are no longer read
     if (j + 2 < nblocks) copy_k(geo, j + 2, kfree);
     copy_v(geo, j, vfree);
+    if (MASKED) km_load = load_km(j + 2);  // tile j+2's register was freed by tile j
     if (j <= wave_last + 1) {
       st.mx = -INFINITY;
       st.psum = 0.0f;
@@ -621,6 +657,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
       mfma_stream<0, true, true>(nxt, knxt, acc, vprev, ln, qf, pprev, st, cur, pcur, cl2);
       rescale_o(acc, st.alpha);
       if (needs_mask(j + 1)) mask_tile(nxt, (int64_t)(j + 1) * BN, lim, S, hi);
+      if (MASKED) key_mask_tile(nxt, km_apply, hi);
     }
   };
 
@@ -628,11 +665,12 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   // and write sa / pb; even steps the reverse. The loop is unrolled by two so
   // that every LDS buffer and register role is fixed in each copy of the step.
   int j = 1;
+  // (j odd: tile j+1 is even and its mask byte is in km0; tile j+2 is odd.)
   for (; j + 1 < nblocks; j += 2) {
-    step(j, sb, sa, pb, pa, kbuf0, vbuf0, kbuf1, vbuf1);
-    step(j + 1, sa, sb, pa, pb, kbuf1, vbuf1, kbuf0, vbuf0);
+    step(j, sb, sa, pb, pa, kbuf0, vbuf0, kbuf1, vbuf1, km0, km1);
+    step(j + 1, sa, sb, pa, pb, kbuf1, vbuf1, kbuf0, vbuf0, km1, km0);
   }
-  if (j < nblocks) step(j, sb, sa, pb, pa, kbuf0, vbuf0, kbuf1, vbuf1);
+  if (j < nblocks) step(j, sb, sa, pb, pa, kbuf0, vbuf0, kbuf1, vbuf1, km0, km1);
 
   // ---- drain: PV of the last tile
   wait_vmem();
@@ -672,7 +710,11 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   const bool pad_row = VARLEN && myq >= T && myq < Tst;
   if (!wave_live && !pad_row) return;
   float inv = 0.0f;
-  if (wave_live) inv = 1.0f / sum_pair32(acc.l_run);
+  if (wave_live) {
+    const float l_tot = sum_pair32(acc.l_run);
+    // with a 2D mask a row may see no key at all: its output is 0
+    inv = (MASKED && !(l_tot > 0.0f)) ? 0.0f : 1.0f / l_tot;
+  }
   if (myq >= T && !pad_row) return;
   uint16_t* out_row = a.out + ((int64_t)bh * Tst + myq) * DV;
 #pragma unroll
@@ -690,6 +732,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
 __global__ __launch_bounds__(NT, 2) void mla_prefill_kernel(PrefillArgs a) { prefill_body<kDense>(a); }
 __global__ __launch_bounds__(NT, 2) void mla_prefill_split_kernel(PrefillArgs a) { prefill_body<kSplit>(a); }
 __global__ __launch_bounds__(NT, 2) void mla_prefill_varlen_kernel(PrefillArgs a) { prefill_body<kVarlen>(a); }
+__global__ __launch_bounds__(NT, 2) void mla_prefill_masked_kernel(PrefillArgs a) { prefill_body<kMasked>(a); }
 
 // Log-sum-exp merge of the key-range partials of every query row: one wave
 // per row, lane l owns output dims 2l, 2l+1.
@@ -723,6 +766,8 @@ int prefill_block_m() { return BM; }
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (a.q_lens != nullptr) {
     hipLaunchKernelGGL(mla_prefill_varlen_kernel, dim3(a.B * a.H * a.ntiles), dim3(NT), 0, stream, a);
+  } else if (a.key_mask != nullptr) {
+    hipLaunchKernelGGL(mla_prefill_masked_kernel, dim3(a.B * a.H * a.ntiles), dim3(NT), 0, stream, a);
   } else if (a.nsplit <= 1) {
     hipLaunchKernelGGL(mla_prefill_kernel, dim3(a.B * a.H * a.ntiles), dim3(NT), 0, stream, a);
   } else {

@@ -139,6 +139,32 @@ mla_status mla_attn_prefill_varlen(const void* q_nope, const void* q_pe,
                                    int32_t max_kv_len, float softmax_scale, void* stream);
 
 /*
+ * mla_attn_prefill under the caller's 2D padding mask. The "Causal mask"
+ * page ("Construct causal mask") hands the caller's 2D attention mask (1 keeps
+ * a position, 0 pads it) with the cached length to the 4D mask builder; the
+ * two combine, so key j is visible to query i of sequence b iff
+ * j <= past_len + i and attn_mask[b * S + j] != 0. This covers left padding
+ * (leading zeros), right padding and any other pattern.
+ *
+ *   attn_mask  [B, S] uint8 in device memory (S = past_len + T: every key,
+ *              cached and new), nonzero keeps; no alignment needed
+ *   other tensors and errors as for mla_attn_prefill (attn_mask NULL is
+ *   MLA_ERR_NULL)
+ *
+ * A query with no visible key (a position inside left padding, say) has no
+ * defined softmax; its output row is 0. Hidden keys get weight exactly 0;
+ * their rows must hold finite values, as every input must (a NaN or infinite
+ * value row would still meet its zero weight in the value contraction; a
+ * non-finite key row is harmless). One kernel is enqueued on `stream` (no
+ * key-range splits).
+ */
+mla_status mla_attn_prefill_masked(const void* q_nope, const void* q_pe,
+                                   const void* k_nope, const void* k_pe,
+                                   const void* v, const uint8_t* attn_mask, void* out,
+                                   int32_t B, int32_t H, int32_t T, int32_t S,
+                                   int32_t past_len, float softmax_scale, void* stream);
+
+/*
  * Bytes of device workspace mla_attn_decode needs for (B, H, S). A pure
  * function of its arguments (no device query); 0 means no workspace is
  * needed. Returns 0 for negative sizes.
@@ -167,6 +193,23 @@ mla_status mla_attn_decode(const void* q_nope, const void* q_pe,
                            void* workspace, size_t workspace_bytes,
                            int32_t B, int32_t H, int32_t S, int32_t past_len,
                            float softmax_scale, void* stream);
+
+/*
+ * mla_attn_decode under the caller's 2D padding mask ("Causal mask" page,
+ * "Construct causal mask"): the new query of sequence b sees key j iff
+ * attn_mask[b * S + j] != 0 (the causal mask hides no key from the last
+ * position). attn_mask is [B, S] uint8 in device memory, nonzero keeps, no
+ * alignment needed; NULL is MLA_ERR_NULL. A sequence with no visible key
+ * gives a zero row; hidden keys do not reach the output whatever their rows
+ * hold. Workspace, shapes and other errors as for mla_attn_decode (the same
+ * mla_attn_decode_workspace_bytes(B, H, S)).
+ */
+mla_status mla_attn_decode_masked(const void* q_nope, const void* q_pe,
+                                  const void* k_nope, const void* k_pe,
+                                  const void* v, const uint8_t* attn_mask, void* out,
+                                  void* workspace, size_t workspace_bytes,
+                                  int32_t B, int32_t H, int32_t S, int32_t past_len,
+                                  float softmax_scale, void* stream);
 
 /*
  * Bytes of device workspace mla_attn_decode_varlen needs for (B, H,

@@ -37,6 +37,7 @@ def test_header_declares_the_boundary():
         "mla_attn_decode_paged", "mla_attn_decode_paged_workspace_bytes",
         "mla_attn_prefill_ws", "mla_attn_prefill_workspace_bytes",
         "mla_attn_prefill_varlen",
+        "mla_attn_prefill_masked", "mla_attn_decode_masked",
         "mla_last_error", "mla_status_string"])
 
 
@@ -260,3 +261,30 @@ def test_prefill_varlen_errors(lib):
     assert "mla_attn_prefill_varlen" in lib.mla_last_error().decode()
     assert call([None] * 8, 2, 4, 0, 32) == 0               # no query rows: empty call
     assert call([None] * 8, 0, 4, 16, 32) == 0
+
+
+def test_masked_errors(lib):
+    ok = [ALIGNED] * 7   # q_nope, q_pe, k_nope, k_pe, v, attn_mask, out
+
+    def pre(ptrs, B, H, T, S, P, scale=SC):
+        return lib.mla_attn_prefill_masked(*ptrs, B, H, T, S, P, scale, None)
+
+    def dec(ptrs, ws, ws_bytes, B, H, S, P, scale=SC):
+        return lib.mla_attn_decode_masked(*ptrs, ws, ws_bytes, B, H, S, P, scale, None)
+
+    assert pre(ok, 1, 4, 16, 20, 3) == 2                       # S != past_len + T
+    mask_none = list(ok)
+    mask_none[5] = None
+    assert pre(mask_none, 1, 4, 16, 20, 4) == 1
+    assert "attn_mask is NULL" in lib.mla_last_error().decode()
+    odd = list(ok)
+    odd[5] = ctypes.c_void_p(0x10003)                           # the mask needs no alignment: stops at the scale
+    assert pre(odd, 1, 4, 16, 20, 4, 0.0) == 4
+    assert pre([None] * 7, 0, 4, 16, 20, 4) == 0               # empty call
+    need = lib.mla_attn_decode_workspace_bytes(1, 64, 1001)
+    assert dec(ok, ALIGNED, need, 1, 64, 1001, 999) == 2
+    assert dec(mask_none, ALIGNED, need, 1, 64, 1001, 1000) == 1
+    assert dec(ok, None, need, 1, 64, 1001, 1000) == 5
+    assert dec(odd, ALIGNED, need, 1, 64, 1001, 1000, float("inf")) == 4
+    assert "mla_attn_decode_masked" in lib.mla_last_error().decode()
+    assert dec([None] * 7, None, 0, 1, 0, 1001, 1000) == 0
