@@ -246,7 +246,9 @@ def mla_attn_decode_masked(q_nope, q_pe, k_nope, k_pe, v, attn_mask, past_len: i
                            softmax_scale: float, out=None, workspace=None):
     """mla_attn_decode under the caller's 2D padding mask attn_mask [B, S]
     (uint8 or bool on the GPU, nonzero keeps); a sequence with no visible key
-    gives a zero row."""
+    gives a zero row. workspace: at least
+    mla_attn_decode_varlen_workspace_bytes(B, H, S) bytes (allocated here when
+    omitted)."""
     import torch
 
     B, H, T, S = _shapes(q_nope, q_pe, k_nope, k_pe, v)
@@ -259,7 +261,7 @@ def mla_attn_decode_masked(q_nope, q_pe, k_nope, k_pe, v, attn_mask, past_len: i
         _check_tensor(out, "out")
         if tuple(out.shape) != (B, H, 1, V_HEAD_DIM) or out.device != q_nope.device:
             raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, 1, V_HEAD_DIM)}")
-    need = mla_attn_decode_workspace_bytes(B, H, S)
+    need = mla_attn_decode_varlen_workspace_bytes(B, H, S)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_nope.device)
     if not (workspace.is_cuda and workspace.is_contiguous()):

@@ -94,7 +94,7 @@ mla_status launch_decode_call(const char* where, const void* q_nope, const void*
     // together by construction.
     const int64_t bh = (int64_t)B * H;
     const int64_t grid = bh * plan.nsplit;
-    a.interleave = (seq_lens != nullptr && bh % 8 == 0) ? 1 : 0;
+    a.interleave = ((seq_lens != nullptr || x.key_mask != nullptr) && bh % 8 == 0) ? 1 : 0;
     const bool together = a.interleave || (grid % 8 == 0 && (grid / 8) % plan.nsplit == 0);
     a.fused = (plan.nsplit > 1 && plan.nsplit <= 64 && together) ? 1 : 0;
   }
@@ -266,11 +266,25 @@ mla_status mla_attn_decode_masked(const void* q_nope, const void* q_pe, const vo
                                   void* out, void* workspace, size_t workspace_bytes, int32_t B,
                                   int32_t H, int32_t S, int32_t past_len, float softmax_scale,
                                   void* stream) {
+  // Padding differs by sequence, as lengths do: the variable-length plan
+  // (pieces of at most 1024 keys) keeps long-visible sequences from trailing.
   mla::DecodePlan plan;
   mla::CheckResult r = mla::check_decode(q_nope, q_pe, k_nope, k_pe, v, out, workspace,
-                                         workspace_bytes, B, H, S, past_len, softmax_scale, &plan);
-  if (r.status == MLA_OK && !r.empty && attn_mask == nullptr)
-    r = mla::fail(MLA_ERR_NULL, "attn_mask is NULL");
+                                         workspace_bytes, B, H, S, past_len, softmax_scale, nullptr);
+  if (r.status == MLA_OK && !r.empty) {
+    plan = mla::plan_decode_varlen(B, H, S);
+    if (attn_mask == nullptr) {
+      r = mla::fail(MLA_ERR_NULL, "attn_mask is NULL");
+    } else if (B * (int64_t)H > mla::kMaxGrid / plan.nsplit) {
+      r = mla::fail(MLA_ERR_SHAPE, "B*H*nsplit exceeds the grid limit");
+    } else if (plan.workspace_bytes > 0 &&
+               (workspace == nullptr || workspace_bytes < plan.workspace_bytes)) {
+      r = mla::fail(MLA_ERR_WORKSPACE,
+                    "workspace is NULL or smaller than mla_attn_decode_varlen_workspace_bytes(B, H, S)");
+    } else if (plan.workspace_bytes > 0 && mla::misaligned(workspace)) {
+      r = mla::fail(MLA_ERR_ALIGN, "workspace is not 16-byte aligned");
+    }
+  }
   if (r.status != MLA_OK) return report("mla_attn_decode_masked", r);
   if (r.empty) return MLA_OK;
   DecodeExtras x;

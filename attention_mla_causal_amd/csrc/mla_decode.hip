@@ -212,6 +212,18 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     const int64_t kb = base0 + (int64_t)KEYS_PER_TRIP * lane;
     if (kb < s1) blk_lane = (int32_t)block_of(kb);
   }
+  // 2D mask: the mask bytes of each trip's keys are fetched one trip ahead
+  // (the first trip's here, before the loop), so the rows of hidden keys are
+  // never fetched and trips whose keys are all hidden are skipped.
+  const uint8_t* mrow = MASKED ? a.key_mask + (int64_t)b * a.S : nullptr;
+  uint8_t pre[KEYS_PER_LANE];
+  if (MASKED) {
+#pragma unroll
+    for (int u = 0; u < KEYS_PER_LANE; ++u) {
+      const int64_t key = base0 + 4 * u + qq;
+      pre[u] = key < s1 ? mrow[key] : 0;
+    }
+  }
   int trip = 0;
   for (int64_t base = base0; base < s1; base += KEYS_PER_TRIP, ++trip) {
     u32x4 kn[KEYS_PER_LANE], vv[KEYS_PER_LANE];
@@ -232,11 +244,23 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
       v_t = v_g + base * DV;
       kp_t = kp_g + base * DR;
     }
+    if (MASKED) {
+      bool any = false;
+#pragma unroll
+      for (int u = 0; u < KEYS_PER_LANE; ++u) {
+        const int64_t key = base + 4 * u + qq;
+        keep[u] = pre[u];
+        ok[u] = key < s1 && keep[u] != 0;
+        any = any || ok[u];
+        const int64_t next = key + KEYS_PER_TRIP;
+        pre[u] = next < s1 ? mrow[next] : 0;
+      }
+      // a trip whose keys are all hidden is skipped whole
+      if (!__any(any)) continue;
+    }
 #pragma unroll
     for (int u = 0; u < KEYS_PER_LANE; ++u) {
-      const int64_t key = base + 4 * u + qq;
-      ok[u] = key < s1;
-      if (MASKED) keep[u] = ok[u] ? a.key_mask[(int64_t)b * a.S + key] : 0;
+      if (!MASKED) ok[u] = base + 4 * u + qq < s1;
       if (ok[u]) {
         kn[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kn_t + (4 * u + qq) * DN));
         kp[u] = *reinterpret_cast<const u32x2*>(kp_t + (4 * u + qq) * DR);

@@ -369,6 +369,59 @@ __device__ __forceinline__ void zero_rows(uint16_t* out, int64_t r0, int64_t r1)
 
 enum { kDense = 0, kSplit = 1, kVarlen = 2, kMasked = 3 };
 
+// 2D mask: the first and last kept key among keys [0, limit) of one mask row
+// (first > last when none is kept), over all threads of the workgroup. Rows
+// that start on a 4-byte boundary are read a dword at a time, others a byte at
+// a time. All threads must call it.
+__device__ __forceinline__ void kept_key_range(const uint8_t* row, int64_t limit, int64_t& first,
+                                               int64_t& last) {
+  __shared__ int64_t s_first[NW], s_last[NW];
+  int64_t f = INT64_MAX, l = -1;
+  if ((reinterpret_cast<uintptr_t>(row) & 3) == 0) {
+    const int64_t nw = limit / 4;
+    const uint32_t* row4 = reinterpret_cast<const uint32_t*>(row);
+    for (int64_t w = threadIdx.x; w < nw; w += NT) {
+      const uint32_t x = row4[w];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((x >> (8 * e)) & 0xffu) {
+          f = f < 4 * w + e ? f : 4 * w + e;
+          l = l > 4 * w + e ? l : 4 * w + e;
+        }
+    }
+    for (int64_t j = 4 * nw + threadIdx.x; j < limit; j += NT)
+      if (row[j]) {
+        f = f < j ? f : j;
+        l = l > j ? l : j;
+      }
+  } else {
+    for (int64_t j = threadIdx.x; j < limit; j += NT)
+      if (row[j]) {
+        f = f < j ? f : j;
+        l = l > j ? l : j;
+      }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const int64_t f2 = __shfl_xor(f, off), l2 = __shfl_xor(l, off);
+    f = f < f2 ? f : f2;
+    l = l > l2 ? l : l2;
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_first[wave] = f;
+    s_last[wave] = l;
+  }
+  __syncthreads();
+  first = s_first[0];
+  last = s_last[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    first = first < s_first[w] ? first : s_first[w];
+    last = last > s_last[w] ? last : s_last[w];
+  }
+}
+
 // The caller's 2D padding mask on one score tile. kbyte is this lane's mask
 // byte for key (lane % 32) of the tile; a ballot turns the 32 bytes into one
 // wave-uniform bit per key, and the lane hides its 16 keys (8g + 4hi + e) whose
@@ -452,27 +505,35 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   // (longest-job-first); otherwise head by head, heaviest tile first, so a
   // head's K/V streams through the XCD's L2 for all its tiles at once.
   int bh, qt, sp = 0;
-  if (VARLEN) {
+  const bool uneven = 2 * (a.past_len + (int64_t)BM) < a.past_len + (int64_t)a.T;
+  if (VARLEN || MASKED) {
     // (b, h) groups dealt round-robin over the XCDs (each XCD gets H/8 heads
     // of every sequence when H is a multiple of 8, so the XCDs stay even
     // whatever the lengths); each XCD runs its groups longest sequence first,
     // a group's query tiles back to back (its K/V streams through that XCD's
     // L2 once), heaviest tile first.
+    // With a 2D mask the padding, and so the work, differs by sequence in a
+    // way the grid cannot see: the groups are dealt round-robin over the XCDs
+    // the same way, in index order, and when the causal triangle dominates
+    // each XCD runs its tiles heaviest first across all of its groups.
     const int G = a.B * a.H;
     int gi, t;
-    if (G % 8 == 0) {
+    if (G % 8 == 0 && MASKED && uneven) {
+      const int per_x = G / 8;
+      gi = ((wg / 8) % per_x) * 8 + wg % 8;
+      t = (wg / 8) / per_x;
+    } else if (G % 8 == 0) {
       gi = (wg / 8 / a.ntiles) * 8 + wg % 8;
       t = (wg / 8) % a.ntiles;
     } else {
       gi = wg / a.ntiles;
       t = wg % a.ntiles;
     }
-    const int seq = seq_at_rank(a, gi / a.H);
+    const int seq = VARLEN ? seq_at_rank(a, gi / a.H) : gi / a.H;
     bh = seq * a.H + gi % a.H;
     qt = a.ntiles - 1 - t;
   } else {
     const int per = nwg / 8, i = wg / 8;
-    const bool uneven = 2 * (a.past_len + (int64_t)BM) < a.past_len + (int64_t)a.T;
     if (SPLIT) {
       // key-range splits of one query tile are adjacent (same XCD when the
       // grid is a multiple of 8), then query tiles, then heads
@@ -522,6 +583,20 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   if (SPLIT) {
     kt0 = sp * a.tiles_per_split;
     kt1 = kt0 + a.tiles_per_split < nblocks_all ? kt0 + a.tiles_per_split : nblocks_all;
+  }
+  if (MASKED) {
+    // only the tiles between the first and the last key the 2D mask keeps
+    // (of those the tile's queries can see) are visited: leading padding
+    // costs a scan of its mask bytes, not its attention
+    int64_t first, last;
+    kept_key_range(a.key_mask + (int64_t)b * Sst, past + q_last + 1, first, last);
+    if (first > last) {  // no query of this tile sees a kept key
+      const int64_t r1 = q0 + BM < T ? q0 + BM : T;
+      zero_rows(a.out + (int64_t)bh * Tst * DV, q0, r1);
+      return;
+    }
+    kt0 = (int)(first / BN);
+    kt1 = (int)(last / BN) + 1;
   }
   const int nblocks = kt1 - kt0;
   if (SPLIT && nblocks <= 0) {  // no key of this range is visible to the tile
@@ -707,7 +782,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   // ---- epilogue: divide by the full row sum and store bf16; in a padded
   // batch, rows past the sequence's query count (still inside the slice) get 0
   const int64_t myq = q0w + l32;
-  const bool pad_row = VARLEN && myq >= T && myq < Tst;
+  // rows written as 0: padded query rows of a variable-length batch, and with
+  // a 2D mask the rows of a wave that sees no kept key
+  const bool pad_row = (VARLEN && myq >= T && myq < Tst) || (MASKED && !wave_live && myq < T);
   if (!wave_live && !pad_row) return;
   float inv = 0.0f;
   if (wave_live) {

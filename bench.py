@@ -34,9 +34,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from seeded_inputs import (LATENT_WORKLOADS, PAGED_WORKLOADS, SHARD_WORKLOADS, VARLEN_WORKLOADS,  # noqa: E402
-                           VARLEN_PREFILL_WORKLOADS, WORKLOADS,
+                           VARLEN_PREFILL_WORKLOADS, WORKLOADS, MASKED_WORKLOADS,
                            device_inputs, host_inputs, latent_device_inputs, latent_host_inputs,
-                           paged_device_inputs, paged_layout, varlen_prefill_lens, varlen_seq_lens)
+                           left_pad_mask, left_pads, paged_device_inputs, paged_layout,
+                           varlen_prefill_lens, varlen_seq_lens)
 
 METRIC = "prefill attn TFLOP/s & decode HBM GB/s, 1 MI355X, as fraction of peak"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
@@ -100,6 +101,23 @@ def prefill_flops(wl) -> int:
 def varlen_prefill_flops(wl, q_lens, past_lens) -> int:
     """Each sequence's own visible (query, key) pairs; padded rows count nothing."""
     n_vis = sum(int(t) * int(p) + int(t) * (int(t) + 1) // 2 for t, p in zip(q_lens, past_lens))
+    return 2 * wl.H * (192 + 128) * n_vis
+
+
+def masked_decode_bytes(wl, pads) -> int:
+    """Visible rows only (k_nope + v per head, the shared rotary key once), the
+    mask bytes, queries and output."""
+    L = int((wl.S - np.asarray(pads, dtype=np.int64)).clip(min=0).sum())
+    return wl.H * L * (128 + 128) * 2 + L * 64 * 2 + wl.B * wl.S + wl.B * wl.H * (192 + 128) * 2
+
+
+def masked_prefill_flops(wl, pads) -> int:
+    """Visible (query, key) pairs only: query i of sequence b sees keys
+    pads[b] .. past_len + i."""
+    n_vis = 0
+    for p in np.asarray(pads, dtype=np.int64):
+        i = np.arange(wl.T, dtype=np.int64)
+        n_vis += int(np.clip(wl.past_len + i - p + 1, 0, None).sum())
     return 2 * wl.H * (192 + 128) * n_vis
 
 
@@ -442,6 +460,52 @@ def run_prefill_varlen(wl, steps, warmup, seed=0):
     return res
 
 
+def run_masked(wl, steps, warmup, seed=0):
+    """mla_attn_decode_masked / mla_attn_prefill_masked with a left-padding 2D
+    mask (inputs drawn on the device). Decode is graph-timed, prefill eager."""
+    import torch
+    import attention_mla_causal_amd as mla
+    dev = torch.device("cuda:0")
+    pads = left_pads(wl, seed=seed)
+    mask = torch.as_tensor(left_pad_mask(wl.S, pads), device=dev)
+    d = device_inputs(wl, dev, seed=seed)
+    log(f"[bench] {wl.name}: B={wl.B} H={wl.H} T={wl.T} S={wl.S} sum(pads)={int(pads.sum())} steps={steps}")
+    out = torch.empty((wl.B, wl.H, wl.T, 128), dtype=torch.bfloat16, device=dev)
+    if wl.T == 1:
+        need = mla.mla_attn_decode_varlen_workspace_bytes(wl.B, wl.H, wl.S)
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+
+        def step(i):
+            mla.mla_attn_decode_masked(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], mask,
+                                       wl.past_len, wl.softmax_scale, out=out, workspace=ws)
+
+        ms, wall_ms = time_graph(step, steps, warmup)
+        work = masked_decode_bytes(wl, pads)
+        rate, unit, bound, peak, kernel = work / (ms * 1e-3) / 1e9, "GB/s", "hbm", HBM_PEAK_GBS, "mla_decode_masked_kernel"
+    else:
+        def step(i):
+            mla.mla_attn_prefill_masked(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], mask,
+                                        wl.past_len, wl.softmax_scale, out=out)
+
+        ms, wall_ms = time_eager(step, steps, warmup)
+        work = masked_prefill_flops(wl, pads)
+        rate, unit, bound, peak, kernel = (work / (ms * 1e-3) / 1e12, "TFLOP/s", "mfma", MFMA_BF16_PEAK_TFS,
+                                           "mla_prefill_masked_kernel")
+    res = {
+        "workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "past_len": wl.past_len, "S": wl.S,
+        "left_pads": pads.tolist() if wl.B <= 8 else f"sum {int(pads.sum())}", "inputs": "device",
+        "steps": steps, "timing": "hip_graph" if wl.T == 1 else "eager",
+        "ms_per_step": ms, "wall_ms_per_step": wall_ms, "value": rate, "unit": unit,
+        ("algorithmic_bytes" if wl.T == 1 else "algorithmic_flops"): work,
+        "roofline": {"bound": bound, "kernel": kernel, "achieved": rate, "peak": peak, "unit": unit,
+                     "frac": rate / peak, "traffic": measured_traffic(
+                         "mla_decode_kernel" if wl.T == 1 else "mla_prefill_kernel", wl.name)},
+    }
+    del d
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline_decode(wl, seconds):
     """The fp64 oracle on the whole decode workload, repeated for ~`seconds`."""
     from oracle import mla_attention
@@ -508,7 +572,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_p1000",
                     choices=sorted(WORKLOADS) + sorted(LATENT_WORKLOADS) + sorted(VARLEN_WORKLOADS)
-                    + sorted(PAGED_WORKLOADS) + sorted(VARLEN_PREFILL_WORKLOADS))
+                    + sorted(PAGED_WORKLOADS) + sorted(VARLEN_PREFILL_WORKLOADS) + sorted(MASKED_WORKLOADS))
     ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -543,7 +607,11 @@ def main():
         sys.exit(2)
 
     torch.cuda.synchronize()
-    if args.workload in VARLEN_PREFILL_WORKLOADS:
+    if args.workload in MASKED_WORKLOADS:
+        wl = MASKED_WORKLOADS[args.workload]
+        head = run_masked(wl, args.steps, args.warmup)
+        cpu = None
+    elif args.workload in VARLEN_PREFILL_WORKLOADS:
         wl = VARLEN_PREFILL_WORKLOADS[args.workload]
         head = run_prefill_varlen(wl, args.steps, args.warmup)
         cpu = None
@@ -598,6 +666,9 @@ def main():
         for name, w in VARLEN_PREFILL_WORKLOADS.items():
             if name != wl.name:
                 workloads[name] = run_prefill_varlen(w, args.extra_steps, 2)
+        for name, w in MASKED_WORKLOADS.items():
+            if name != wl.name:
+                workloads[name] = run_masked(w, args.extra_steps, 2)
         for name, w in LATENT_WORKLOADS.items():
             if name == wl.name:
                 continue

@@ -201,8 +201,12 @@ mla_status mla_attn_decode(const void* q_nope, const void* q_pe,
  * position). attn_mask is [B, S] uint8 in device memory, nonzero keeps, no
  * alignment needed; NULL is MLA_ERR_NULL. A sequence with no visible key
  * gives a zero row; hidden keys do not reach the output whatever their rows
- * hold. Workspace, shapes and other errors as for mla_attn_decode (the same
- * mla_attn_decode_workspace_bytes(B, H, S)).
+ * hold (from the second 128-key trip of a workgroup on, their rows are not
+ * even fetched). Padding differs by sequence, so the keys are split as in
+ * mla_attn_decode_varlen: workspace of at least
+ * mla_attn_decode_varlen_workspace_bytes(B, H, S) bytes, 16-byte aligned
+ * (may be NULL when that is 0). Shapes and other errors as for
+ * mla_attn_decode.
  */
 mla_status mla_attn_decode_masked(const void* q_nope, const void* q_pe,
                                   const void* k_nope, const void* k_pe,

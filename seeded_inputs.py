@@ -311,6 +311,34 @@ def varlen_prefill_lens(B: int, max_q: int, max_kv: int, seed: int = 0):
     return tq, pl
 
 
+# The caller's 2D padding mask, left padding: sequence b's first pads[b] key
+# positions are padding. A batched decode whose sequences end together (the
+# batched-decode shape, lengths as the variable-length decode's), and a batch
+# of left-padded prompts prefilled together (pads up to half the prompt).
+MASKED_WORKLOADS = {
+    "masked_batched_decode": Workload("masked_batched_decode", B=32, H=64, T=1, past_len=8191),
+    "masked_prefill": Workload("masked_prefill", B=4, H=64, T=4096, past_len=0),
+}
+
+
+def left_pads(wl: Workload, seed: int = 0) -> np.ndarray:
+    """Padding positions per sequence [B] int64. Decode: S - L_b with L_b the
+    variable-length decode's lengths (uniform in [1, S], the first S). Prefill:
+    uniform in [0, S/2], the first 0."""
+    if wl.T == 1:
+        return (wl.S - varlen_seq_lens(wl.B, wl.S, seed=seed)).astype(np.int64)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 4])))
+    pads = g.integers(0, wl.S // 2 + 1, size=wl.B).astype(np.int64)
+    if wl.B:
+        pads[0] = 0
+    return pads
+
+
+def left_pad_mask(S: int, pads) -> np.ndarray:
+    """The 2D mask [B, S] uint8: 0 on each sequence's padding, 1 after it."""
+    return (np.arange(S)[None, :] >= np.asarray(pads)[:, None]).astype(np.uint8)
+
+
 PAGED_TENSORS = ("q_nope", "q_pe", "k_nope_pages", "k_pe_pages", "v_pages",
                  "k_nope_new", "k_pe_new", "v_new")
 

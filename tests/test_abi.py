@@ -281,8 +281,13 @@ def test_masked_errors(lib):
     odd[5] = ctypes.c_void_p(0x10003)                           # the mask needs no alignment: stops at the scale
     assert pre(odd, 1, 4, 16, 20, 4, 0.0) == 4
     assert pre([None] * 7, 0, 4, 16, 20, 4) == 0               # empty call
-    need = lib.mla_attn_decode_workspace_bytes(1, 64, 1001)
+    need = lib.mla_attn_decode_varlen_workspace_bytes(1, 64, 1001)
     assert dec(ok, ALIGNED, need, 1, 64, 1001, 999) == 2
+    # the variable-length split plan: B*H fills the GPU, yet 8192 keys split in pieces
+    big = lib.mla_attn_decode_varlen_workspace_bytes(32, 64, 8192)
+    assert big > 0 and lib.mla_attn_decode_workspace_bytes(32, 64, 8192) == 0
+    assert dec(ok, ALIGNED, big - 1, 32, 64, 8192, 8191) == 5
+    assert dec(ok, MISALIGNED, big, 32, 64, 8192, 8191) == 3
     assert dec(mask_none, ALIGNED, need, 1, 64, 1001, 1000) == 1
     assert dec(ok, None, need, 1, 64, 1001, 1000) == 5
     assert dec(odd, ALIGNED, need, 1, 64, 1001, 1000, float("inf")) == 4

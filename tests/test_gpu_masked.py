@@ -173,3 +173,44 @@ def test_bool_mask_is_accepted():
                                          _dev_mask(mask).bool(), P, ALPHA)
     torch.cuda.synchronize()
     assert_parity(to_host_f64(out), _oracle(x, mask, P), "prefill masked bool")
+
+
+def test_full_size_workloads_sampled():
+    """The benchmarked launches (left padding): a batched decode of 32
+    sequences over 8192 positions and a prefill of 4 left-padded 4096-token
+    prompts, 64 heads; the oracle checks sampled rows, each on its own keys."""
+    import torch
+    from seeded_inputs import MASKED_WORKLOADS, device_inputs, left_pad_mask, left_pads
+    for name, wl in MASKED_WORKLOADS.items():
+        pads = left_pads(wl, seed=0)
+        mask = left_pad_mask(wl.S, pads)
+        log(f"case full {name} B={wl.B} H={wl.H} T={wl.T} S={wl.S} sum(pads)={int(pads.sum())}")
+        d = device_inputs(wl, "cuda", seed=0)
+        m = _dev_mask(mask)
+        if wl.T == 1:
+            out = _lib().mla_attn_decode_masked(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], m,
+                                                wl.past_len, wl.softmax_scale)
+        else:
+            out = _lib().mla_attn_prefill_masked(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], m,
+                                                 wl.past_len, wl.softmax_scale)
+        torch.cuda.synchronize()
+        g = np.random.default_rng(1)
+        rows = [(int(g.integers(0, wl.B)), int(g.integers(0, wl.H)), int(g.integers(0, wl.T)))
+                for _ in range(24)]
+        rows += [(b, 0, wl.T - 1) for b in range(wl.B)]
+        if wl.T > 1:   # the first query row that sees a key, and one inside the padding
+            rows += [(b, 1, int(min(pads[b], wl.T - 1))) for b in range(wl.B)]
+            rows += [(b, 2, int(pads[b]) - 1) for b in range(wl.B) if pads[b] > 0]
+        got, ref = [], []
+        for b, h, i in rows:
+            S_i = wl.past_len + i + 1           # keys 0 .. past_len + i
+            sl = {k: to_host_bits(d[k][b:b + 1, h:h + 1, i:i + 1]) for k in ("q_nope", "q_pe")}
+            sl.update({k: to_host_bits(d[k][b:b + 1, h:h + 1, :S_i]) for k in ("k_nope", "v")})
+            sl["k_pe"] = to_host_bits(d["k_pe"][b:b + 1, :, :S_i])
+            ref.append(mla_attention_masked(sl["q_nope"], sl["q_pe"], sl["k_nope"], sl["k_pe"], sl["v"],
+                                            mask[b:b + 1, :S_i], S_i - 1, wl.softmax_scale)[0, 0, 0])
+            got.append(to_host_f64(out[b, h, i]))
+        assert_parity(np.stack(got), np.stack(ref), f"{name} sampled")
+        assert torch.isfinite(out).all().item()
+        del d, out
+        torch.cuda.empty_cache()
