@@ -460,7 +460,7 @@ def run_prefill_varlen(wl, steps, warmup, seed=0):
     return res
 
 
-def run_masked(wl, steps, warmup, seed=0):
+def run_masked(wl, steps, warmup, seed=0, graph=True):
     """mla_attn_decode_masked / mla_attn_prefill_masked with a left-padding 2D
     mask (inputs drawn on the device). Decode is graph-timed, prefill eager."""
     import torch
@@ -479,7 +479,7 @@ def run_masked(wl, steps, warmup, seed=0):
             mla.mla_attn_decode_masked(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], mask,
                                        wl.past_len, wl.softmax_scale, out=out, workspace=ws)
 
-        ms, wall_ms = time_graph(step, steps, warmup)
+        ms, wall_ms = (time_graph if graph else time_eager)(step, steps, warmup)
         work = masked_decode_bytes(wl, pads)
         rate, unit, bound, peak, kernel = work / (ms * 1e-3) / 1e9, "GB/s", "hbm", HBM_PEAK_GBS, "mla_decode_masked_kernel"
     else:
@@ -494,7 +494,7 @@ def run_masked(wl, steps, warmup, seed=0):
     res = {
         "workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "past_len": wl.past_len, "S": wl.S,
         "left_pads": pads.tolist() if wl.B <= 8 else f"sum {int(pads.sum())}", "inputs": "device",
-        "steps": steps, "timing": "hip_graph" if wl.T == 1 else "eager",
+        "steps": steps, "timing": "hip_graph" if wl.T == 1 and graph else "eager",
         "ms_per_step": ms, "wall_ms_per_step": wall_ms, "value": rate, "unit": unit,
         ("algorithmic_bytes" if wl.T == 1 else "algorithmic_flops"): work,
         "roofline": {"bound": bound, "kernel": kernel, "achieved": rate, "peak": peak, "unit": unit,
@@ -609,7 +609,7 @@ def main():
     torch.cuda.synchronize()
     if args.workload in MASKED_WORKLOADS:
         wl = MASKED_WORKLOADS[args.workload]
-        head = run_masked(wl, args.steps, args.warmup)
+        head = run_masked(wl, args.steps, args.warmup, graph=not args.eager)
         cpu = None
     elif args.workload in VARLEN_PREFILL_WORKLOADS:
         wl = VARLEN_PREFILL_WORKLOADS[args.workload]
