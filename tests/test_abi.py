@@ -293,3 +293,22 @@ def test_masked_errors(lib):
     assert dec(odd, ALIGNED, need, 1, 64, 1001, 1000, float("inf")) == 4
     assert "mla_attn_decode_masked" in lib.mla_last_error().decode()
     assert dec([None] * 7, None, 0, 1, 0, 1001, 1000) == 0
+
+
+def test_product_path_never_touches_the_oracle():
+    """The package (binding and HIP sources) names neither the oracle package
+    nor any of its modules, and the oracle imports nothing from the package."""
+    pkg = os.path.join(ROOT, "attention_mla_causal_amd")
+    oracle_dir = os.path.join(ROOT, "oracle")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if not f.endswith((".py", ".hip", ".h", ".cpp")):
+                continue
+            text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+            assert not re.search(r"\b(from|import)\s+oracle\b", text), f
+            assert not re.search(r"\boracle[./]", text), f
+            assert "importlib" not in text or "oracle" not in text, f
+    for f in os.listdir(oracle_dir):
+        if f.endswith(".py"):
+            text = open(os.path.join(oracle_dir, f), encoding="utf-8").read()
+            assert "attention_mla_causal_amd" not in text, f
