@@ -311,4 +311,5 @@ def test_product_path_never_touches_the_oracle():
     for f in os.listdir(oracle_dir):
         if f.endswith(".py"):
             text = open(os.path.join(oracle_dir, f), encoding="utf-8").read()
-            assert "attention_mla_causal_amd" not in text, f
+            assert not re.search(r"\b(from|import)\s+attention_mla_causal_amd\b", text), f
+            assert "libmla_attn" not in text, f
