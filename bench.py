@@ -571,7 +571,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_p1000",
-                    choices=sorted(WORKLOADS) + sorted(LATENT_WORKLOADS) + sorted(VARLEN_WORKLOADS)
+                    choices=sorted(WORKLOADS) + sorted(SHARD_WORKLOADS) + sorted(LATENT_WORKLOADS)
+                    + sorted(VARLEN_WORKLOADS)
                     + sorted(PAGED_WORKLOADS) + sorted(VARLEN_PREFILL_WORKLOADS) + sorted(MASKED_WORKLOADS))
     ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -627,12 +628,12 @@ def main():
         wl = LATENT_WORKLOADS[args.workload]
         head = run_latent(wl, args.steps, args.warmup, graph=not args.eager)
         cpu = None if args.no_cpu else cpu_baseline_latent(wl, args.cpu_seconds)
-    elif WORKLOADS[args.workload].T == 1:
-        wl = WORKLOADS[args.workload]
+    elif {**WORKLOADS, **SHARD_WORKLOADS}[args.workload].T == 1:
+        wl = {**WORKLOADS, **SHARD_WORKLOADS}[args.workload]
         head = run_decode(wl, args.steps, args.warmup, graph=not args.eager)
         cpu = None if args.no_cpu else cpu_baseline_decode(wl, args.cpu_seconds)
     else:
-        wl = WORKLOADS[args.workload]
+        wl = {**WORKLOADS, **SHARD_WORKLOADS}[args.workload]
         head, x = run_prefill(wl, args.steps, args.warmup)
         cpu = None if args.no_cpu else cpu_baseline_prefill(wl, x, args.cpu_seconds)
         del x
