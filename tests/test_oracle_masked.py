@@ -118,3 +118,29 @@ def test_visible_keys_and_errors():
         mla_attention_masked(*x, np.ones((1, 4)), 3, ALPHA)       # mask narrower than the keys
     with pytest.raises(ValueError):
         mla_attention_masked(*x, np.ones((2, 5)), 3, ALPHA)       # one row per sequence
+
+
+@pytest.mark.parametrize("B,H,T,P", [(2, 3, 6, 4), (3, 2, 1, 20)])
+def test_against_torch_sdpa_fp64(B, H, T, P):
+    """An independent library routine: torch SDPA in fp64 on the CPU with the
+    combined boolean mask (causal offset AND 2D mask); rows with a visible key
+    compared (SDPA leaves rows with none undefined)."""
+    torch = pytest.importorskip("torch")
+    S = P + T
+    qn, qp, kn, kp, v = _rand(B, H, T, S, 30 + B + T)
+    rng = np.random.default_rng(31 + B)
+    mask = (rng.random((B, S)) < 0.6).astype(np.uint8)
+    got = mla_attention_masked(qn, qp, kn, kp, v, mask, P, ALPHA)
+    q = torch.from_numpy(np.concatenate([qn, qp], -1))
+    k = torch.from_numpy(np.concatenate([kn, np.broadcast_to(kp, (B, H, S, 64))], -1))
+    allowed = (torch.arange(S)[None, None, :] <= (P + torch.arange(T))[None, :, None]) & \
+        torch.from_numpy(mask.astype(bool))[:, None, :]
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, torch.from_numpy(v),
+                                                           attn_mask=allowed[:, None], scale=ALPHA)
+    live = allowed.any(-1).numpy()                      # [B, T]
+    for b in range(B):
+        for i in range(T):
+            if live[b, i]:
+                np.testing.assert_allclose(got[b, :, i], ref.numpy()[b, :, i], rtol=0, atol=1e-12)
+            else:
+                assert not np.any(got[b, :, i])
