@@ -197,6 +197,16 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   const int64_t S_loop = append ? S - 1 : S;
   const int64_t s1 = (s0 + a.keys_per_split < S_loop) ? s0 + a.keys_per_split : S_loop;
   const bool owns_new = append && S - 1 >= s0 && S - 1 < s0 + a.keys_per_split;
+  // With a length per sequence, only the splits that hold a key of it take
+  // part (at least split 0, which gives an empty sequence its zero row); the
+  // others leave at once, and the in-kernel merge waits for and reads the
+  // active ones only. (Workgroup-uniform, before any barrier.)
+  int nact = a.nsplit;
+  if (a.seq_lens != nullptr && a.fused) {
+    const int64_t n = (S + a.keys_per_split - 1) / a.keys_per_split;
+    nact = n < 1 ? 1 : (n > a.nsplit ? a.nsplit : (int)n);
+    if (split >= nact) return;
+  }
 
   float m = -INFINITY, l = 0.0f, o[8];
 #pragma unroll
@@ -426,7 +436,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   const __amdgpu_buffer_rsrc_t rf = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.ws_flag + (int64_t)bh * a.nsplit), (short)0, a.nsplit * 8, 0x00020000);
   bool done = true;
-  for (int sp = lane; sp < a.nsplit; sp += 64) {
+  for (int sp = lane; sp < nact; sp += 64) {
     const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(rf, sp * 8, 0, 1);      // sc0: past L1
     const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(rf, sp * 8 + 4, 0, 1);
     done = done && (((unsigned long long)hi << 32 | lo) == a.tag);
@@ -438,7 +448,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   // split of this call has already set its flag (that is why this workgroup
   // merges), so none is written again in this call; a workgroup still
   // reading them sees a cleared flag and leaves the merge to this one.
-  for (int sp = lane; sp < a.nsplit; sp += 64) a.ws_flag[(int64_t)bh * a.nsplit + sp] = 0ull;
+  for (int sp = lane; sp < nact; sp += 64) a.ws_flag[(int64_t)bh * a.nsplit + sp] = 0ull;
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   const uint32_t my_xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);
   const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
@@ -449,7 +459,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   bool same_xcd = true;
 #pragma unroll
   for (int e = 0; e < 8; ++e) oo[e] = 0.0f;
-  for (int sp = qq; sp < a.nsplit; sp += 4) {
+  for (int sp = qq; sp < nact; sp += 4) {
     const u32x4 mlw = __builtin_amdgcn_raw_buffer_load_b128(rm, sp * 16, 0, 1);
     const u32x4 w0 = __builtin_amdgcn_raw_buffer_load_b128(ro, (sp * DV + 8 * cl) * 4, 0, 1);
     const u32x4 w1 = __builtin_amdgcn_raw_buffer_load_b128(ro, (sp * DV + 8 * cl + 4) * 4, 0, 1);
