@@ -546,6 +546,78 @@ def cpu_baseline_latent(wl, seconds):
             "sample": f"{rows} of {wl.B * wl.H} (batch, head) rows, {el:.1f} s"}
 
 
+def cpu_baseline_head_rows(name, run_one, units, work_per_unit, total_work, unit, seconds):
+    """Time `run_one(k)` for k = 0, 1, ... (each one unit of the workload,
+    doing work_per_unit(k)) until ~`seconds` pass or the units run out;
+    effective rate = work done / time, in the workload's unit."""
+    done, k, t0 = 0.0, 0, time.perf_counter()
+    while k < units:
+        run_one(k)
+        done += work_per_unit(k)
+        k += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    scale = 1e12 if unit == "TFLOP/s" else 1e9
+    return {"value": done / el / scale, "unit": unit, "cores": blas_threads(),
+            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{name}: {k} of {units} units, {done / total_work:.3%} of the workload, {el:.1f} s"}
+
+
+def cpu_baseline_varlen_prefill(wl, seconds, seed=0):
+    """The fp64 padded-batch oracle, one (sequence, head) at a time from the
+    longest sequence on, on host-drawn inputs of the first sequence's shape."""
+    from oracle import mla_prefill_varlen
+    from seeded_inputs import random_inputs
+    tq, pl = varlen_prefill_lens(wl.B, wl.max_q, wl.max_kv, seed=seed)
+    T0, P0 = int(tq[0]), int(pl[0])
+    x = random_inputs(1, 1, wl.max_q, wl.max_kv - wl.max_q, seed=seed, std=wl.std)
+    per = 2 * (192 + 128) * (T0 * P0 + T0 * (T0 + 1) // 2)
+
+    def one(k):
+        mla_prefill_varlen(x["q_nope"], x["q_pe"], x["k_nope"], x["k_pe"], x["v"], np.array([T0]),
+                           np.array([P0]), wl.softmax_scale)
+
+    return cpu_baseline_head_rows("heads of the longest sequence", one, wl.H, lambda k: per,
+                                  varlen_prefill_flops(wl, tq, pl), "TFLOP/s", seconds)
+
+
+def cpu_baseline_masked(wl, seconds, seed=0):
+    """The fp64 2D-mask oracle, one head of the first sequence at a time
+    (prefill: its queries in blocks of 64 rows; decode: its one query)."""
+    from oracle import mla_attention_masked
+    from seeded_inputs import random_inputs
+    pads = left_pads(wl, seed=seed)
+    mask = left_pad_mask(wl.S, pads)[:1]
+    x = random_inputs(1, 1, wl.T, wl.past_len, seed=seed)
+    if wl.T == 1:
+        per = masked_decode_bytes(wl, pads[:1]) / wl.H
+
+        def one(k):
+            mla_attention_masked(x["q_nope"], x["q_pe"], x["k_nope"], x["k_pe"], x["v"], mask,
+                                 wl.past_len, wl.softmax_scale)
+
+        return cpu_baseline_head_rows("heads of sequence 0", one, wl.H, lambda k: per,
+                                      masked_decode_bytes(wl, pads), "GB/s", seconds)
+    rows = 64
+    nblk = -(-wl.T // rows)
+    p0 = int(pads[0])
+
+    def blk_pairs(k):
+        i = np.arange(k * rows, min(wl.T, (k + 1) * rows), dtype=np.int64)
+        return 2 * (192 + 128) * int(np.clip(wl.past_len + i - p0 + 1, 0, None).sum())
+
+    def one(k):
+        lo, hi = k * rows, min(wl.T, (k + 1) * rows)
+        S_hi = wl.past_len + hi
+        mla_attention_masked(x["q_nope"][:, :, lo:hi], x["q_pe"][:, :, lo:hi], x["k_nope"][:, :, :S_hi],
+                             x["k_pe"][:, :, :S_hi], x["v"][:, :, :S_hi], mask[:, :S_hi],
+                             wl.past_len + lo, wl.softmax_scale)
+
+    return cpu_baseline_head_rows("64-query blocks of head 0, sequence 0", one, nblk, blk_pairs,
+                                  masked_prefill_flops(wl, pads), "TFLOP/s", seconds)
+
+
 def cpu_baseline_prefill(wl, x, seconds):
     """The fp64 oracle on the first heads of the workload until ~`seconds` pass;
     effective rate = algorithmic flops of the heads done / time."""
@@ -667,9 +739,13 @@ def main():
         for name, w in VARLEN_PREFILL_WORKLOADS.items():
             if name != wl.name:
                 workloads[name] = run_prefill_varlen(w, args.extra_steps, 2)
+                if not args.no_cpu:
+                    workloads[name]["cpu_baseline"] = cpu_baseline_varlen_prefill(w, min(args.cpu_seconds, 5.0))
         for name, w in MASKED_WORKLOADS.items():
             if name != wl.name:
                 workloads[name] = run_masked(w, args.extra_steps, 2)
+                if not args.no_cpu:
+                    workloads[name]["cpu_baseline"] = cpu_baseline_masked(w, min(args.cpu_seconds, 5.0))
         for name, w in LATENT_WORKLOADS.items():
             if name == wl.name:
                 continue
