@@ -5,7 +5,9 @@
 // to the 4D mask builder, for right padding); a sequence with no key gives 0.
 // The cache may be paged (blocks named by a table per sequence), and the new
 // token's key and value may be appended by the call itself (the cache update
-// the "Similarities" page runs before attending).
+// the "Similarities" page runs before attending). A second instantiation
+// takes the caller's general 2D padding mask ([B, S] bytes, nonzero keeps):
+// it fetches each trip's mask bytes a trip ahead and loads only kept rows.
 //
 // The same computation as prefill with T = 1 (the Kimi K2 "Similarities"
 // page shows it in decode mode with p = 1000: scores [B, 64, 1, 1001]); the

@@ -40,6 +40,12 @@
 //    triangle dominates, heaviest tile first across the XCD's heads. In a
 //    padded batch of sequences of different lengths, (batch, head) pairs are
 //    dealt round-robin over the XCDs and run longest sequence first.
+//  * Four instantiations of one body: all keys per query tile (the common
+//    case), key-range splits merged by a second kernel (small grids), a padded
+//    variable-length batch (lengths read on the device), and the caller's 2D
+//    padding mask (a mask byte per lane per key tile, fetched two tiles ahead
+//    and turned into a wave-uniform bitmask by ballot; only the key tiles
+//    between the first and last kept key are visited).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
