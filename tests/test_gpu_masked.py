@@ -214,3 +214,50 @@ def test_full_size_workloads_sampled():
         assert torch.isfinite(out).all().item()
         del d, out
         torch.cuda.empty_cache()
+
+
+def test_graph_replays_follow_the_device_mask():
+    """The host never reads the mask: captured masked calls, replayed after
+    the mask is rewritten in place, follow each new mask (every replay is
+    checked against the oracle)."""
+    import torch
+    B, H, T, P = 2, 4, 64, 100
+    S = P + T
+    x = random_inputs(B, H, T, P, seed=41)
+    xd = random_inputs(B, H, 1, S - 1, seed=42)
+    d, dd = upload(x), upload(xd)
+    m = _dev_mask(np.ones((B, S), dtype=np.uint8))
+    out = torch.empty((B, H, T, 128), dtype=torch.bfloat16, device="cuda")
+    outd = torch.empty((B, H, 1, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(max(_lib().mla_attn_decode_varlen_workspace_bytes(B, H, S), 16), dtype=torch.uint8,
+                     device="cuda")
+
+    def calls():
+        _lib().mla_attn_prefill_masked(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], m, P, ALPHA,
+                                       out=out)
+        _lib().mla_attn_decode_masked(dd["q_nope"], dd["q_pe"], dd["k_nope"], dd["k_pe"], dd["v"], m, S - 1,
+                                      ALPHA, out=outd, workspace=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(43)
+    for pads in ([0, 0], [30, 150], [120, 5]):
+        mask = _left_pad_mask(S, pads)
+        mask[:, -3:] = (rng.random((B, 3)) < 0.5).astype(np.uint8)   # holes near the end too
+        log(f"  replay pads={pads}")
+        m.copy_(_dev_mask(mask))
+        out.fill_(1.0)
+        outd.fill_(1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_parity(to_host_f64(out), _oracle(x, mask, P), f"graph prefill pads={pads}")
+        assert_parity(to_host_f64(outd), _oracle(xd, mask, S - 1), f"graph decode pads={pads}")
