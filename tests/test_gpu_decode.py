@@ -206,3 +206,42 @@ def test_batched_decode_full_size_sampled(name):
         ref.append(_oracle(xs, wl.past_len, wl.softmax_scale)[0, 0, 0])
         got.append(to_host_f64(out[b, h, 0]))
     assert_parity(np.stack(got), np.stack(ref), "batched_decode sampled")
+
+
+def test_concurrent_calls_on_two_streams():
+    """Two decodes (each with its own workspace) and a prefill enqueued on two
+    streams at once: the library keeps no state between calls beyond the
+    workspaces, so each result matches the oracle."""
+    import torch
+    xa = random_inputs(1, 64, 1, 1500, seed=61)
+    xb = random_inputs(2, 16, 1, 700, seed=62)
+    xp = random_inputs(1, 8, 200, 300, seed=63)
+    da, db, dp = upload(xa), upload(xb), upload(xp)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    wa = torch.empty(max(_lib().mla_attn_decode_workspace_bytes(1, 64, 1501), 16), dtype=torch.uint8,
+                     device="cuda")
+    wb = torch.empty(max(_lib().mla_attn_decode_workspace_bytes(2, 16, 701), 16), dtype=torch.uint8,
+                     device="cuda")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(sa):
+        oa = _lib().mla_attn_decode(da["q_nope"], da["q_pe"], da["k_nope"], da["k_pe"], da["v"], 1500, ALPHA,
+                                    workspace=wa)
+        op = _lib().mla_attn_prefill(dp["q_nope"], dp["q_pe"], dp["k_nope"], dp["k_pe"], dp["v"], 300, ALPHA)
+    with torch.cuda.stream(sb):
+        ob = _lib().mla_attn_decode(db["q_nope"], db["q_pe"], db["k_nope"], db["k_pe"], db["v"], 700, ALPHA,
+                                    workspace=wb)
+    torch.cuda.synchronize()
+    log("case two streams")
+    assert_parity(to_host_f64(oa), _oracle(xa, 1500), "stream a decode")
+    assert_parity(to_host_f64(ob), _oracle(xb, 700), "stream b decode")
+    assert_parity(to_host_f64(op), mla_attention(xp["q_nope"], xp["q_pe"], xp["k_nope"], xp["k_pe"],
+                                                 xp["v"], 300, ALPHA), "stream a prefill")
+
+
+def test_many_sequences_and_heads():
+    """B*H = 16384 (b, h) pairs of 64 keys: a grid far larger than the GPU."""
+    B, H, P = 256, 64, 63
+    log(f"case decode many B={B} H={H} P={P}")
+    x = random_inputs(B, H, 1, P, seed=64)
+    out = _gpu_decode(upload(x), P)
+    assert_parity(to_host_f64(out), _oracle(x, P), "decode many sequences")
