@@ -244,3 +244,32 @@ def test_split_prefill_graph_replays():
         g.replay()
         torch.cuda.synchronize()
         assert_parity(to_host_f64(out), _oracle(x, P), f"split prefill replay {i}")
+
+
+def test_empty_calls_through_the_binding():
+    """Empty batches, heads or query counts are valid no-ops at every entry
+    point (as torch's empty tensors): nothing is launched, shapes come back."""
+    import torch
+    m = _lib()
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    # prefill with T = 0 (S = past_len)
+    q = torch.empty((1, 4, 0, 128), **bf)
+    qp = torch.empty((1, 4, 0, 64), **bf)
+    k = torch.zeros((1, 4, 5, 128), **bf)
+    kp = torch.zeros((1, 1, 5, 64), **bf)
+    out = m.mla_attn_prefill(q, qp, k, kp, k.clone(), 5, ALPHA)
+    assert tuple(out.shape) == (1, 4, 0, 128)
+    # decode with B = 0
+    q0 = torch.empty((0, 64, 1, 128), **bf)
+    out = m.mla_attn_decode(q0, torch.empty((0, 64, 1, 64), **bf), torch.empty((0, 64, 9, 128), **bf),
+                            torch.empty((0, 1, 9, 64), **bf), torch.empty((0, 64, 9, 128), **bf), 8, ALPHA)
+    assert tuple(out.shape) == (0, 64, 1, 128)
+    # padded variable-length prefill with no query rows
+    lens = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = m.mla_attn_prefill_varlen(q, qp, k, kp, k.clone(), lens, lens, ALPHA)
+    assert tuple(out.shape) == (1, 4, 0, 128)
+    # 2D-mask prefill with no query rows
+    out = m.mla_attn_prefill_masked(q, qp, k, kp, k.clone(), torch.ones((1, 5), dtype=torch.uint8, device="cuda"),
+                                    5, ALPHA)
+    assert tuple(out.shape) == (1, 4, 0, 128)
+    torch.cuda.synchronize()
