@@ -59,9 +59,6 @@ constexpr int LAT_COPIES = LAT_BLOCKS * CB_BYTES / 1024;  // 32 of them latent
 constexpr int KSTEPS = KW / 32;              // 18 score K-steps
 constexpr int NDT = R / 16;                  // 32 latent-output tiles of 16 dims
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
-  return __builtin_bit_cast(float, (uint32_t)x << 16);
-}
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
