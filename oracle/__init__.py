@@ -34,3 +34,11 @@ from .mla_paged import (  # noqa: F401
 )
 from .mla_prefill_varlen import mla_prefill_varlen  # noqa: F401
 from .mla_masked import mla_attention_masked, visible_keys  # noqa: F401
+from .mla_rope import (  # noqa: F401
+    KIMI_K2_ROPE,
+    ROPE_DIM,
+    apply_rope,
+    rope_cos_sin,
+    rope_positions,
+    yarn_inv_freq,
+)
