@@ -49,6 +49,10 @@ SIGNATURES = {
                                              _I32, _I32, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_attn_decode_latent_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "mla_attn_decode_latent": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _F32, _VP]),
+    "mla_rope_table_bytes": (_SZ, [_I32]),
+    "mla_rope_table": (ctypes.c_int, [_VP, _I32, ctypes.c_double, ctypes.c_double, _I32, ctypes.c_double,
+                                      ctypes.c_double, _VP]),
+    "mla_rope_apply": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP]),
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_last_error": (ctypes.c_char_p, []),
 }
@@ -487,7 +491,57 @@ def mla_attn_decode_latent(q_nope, q_pe, c_kv, k_pe, w_kv_b, past_len: int, soft
     return out
 
 
+def mla_rope_table_bytes(max_pos: int) -> int:
+    """Bytes of the rotary table for positions 0..max_pos-1 (256 per position)."""
+    return int(_lib.mla_rope_table_bytes(int(max_pos)))
+
+
+def mla_rope_table(max_pos: int, theta: float = 50000.0, factor: float = 32.0,
+                   original_max_position: int = 4096, beta_fast: float = 1.0, beta_slow: float = 1.0,
+                   device=None, out=None):
+    """cos/sin table [max_pos, 32, 2] fp32 of YaRN-scaled RoPE (defaults: the
+    released configuration's rope_theta and rope_scaling), built on the GPU."""
+    import torch
+
+    if out is None:
+        dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        out = torch.empty((max(int(max_pos), 0), 32, 2), dtype=torch.float32, device=dev)
+    if not (out.dtype == torch.float32 and out.is_cuda and out.is_contiguous()
+            and tuple(out.shape) == (int(max_pos), 32, 2)):
+        raise ValueError(f"out must be a contiguous float32 GPU tensor of shape ({int(max_pos)}, 32, 2)")
+    st = _lib.mla_rope_table(out.data_ptr(), int(max_pos), float(theta), float(factor),
+                             int(original_max_position), float(beta_fast), float(beta_slow),
+                             _stream_handle(out.device))
+    _raise_for(st, "mla_rope_table")
+    return out
+
+
+def mla_rope_apply(x, table, past_len: int = 0, past_lens=None):
+    """Rotate x [B, R, T, 64] bf16 in place (R = H for q_pe, 1 for the shared
+    k_pe): row t of sequence b at position past_len + t, or past_lens[b] + t
+    (int32 [B] on the device). Returns x."""
+    import torch
+
+    _check_tensor(x, "x")
+    B, R, T, D = x.shape
+    if D != QK_ROPE_HEAD_DIM:
+        raise ValueError(f"x must have {QK_ROPE_HEAD_DIM} rotary dims, got shape {tuple(x.shape)}")
+    if not (isinstance(table, torch.Tensor) and table.dtype == torch.float32 and table.is_contiguous()
+            and table.dim() == 3 and tuple(table.shape[1:]) == (32, 2) and table.device == x.device):
+        raise ValueError(f"table must be a contiguous float32 [max_pos, 32, 2] tensor on {x.device}")
+    if past_lens is not None:
+        _check_int32(past_lens, "past_lens", (B,), x.device)
+    st = _lib.mla_rope_apply(x.data_ptr(), past_lens.data_ptr() if past_lens is not None else None,
+                             table.data_ptr(), int(table.shape[0]), B, R, T, int(past_len),
+                             _stream_handle(x.device))
+    _raise_for(st, "mla_rope_apply")
+    return x
+
+
 __all__ = [
+    "mla_rope_table",
+    "mla_rope_table_bytes",
+    "mla_rope_apply",
     "mla_attn_prefill_ws",
     "mla_attn_prefill_workspace_bytes",
     "mla_attn_decode_paged",
@@ -497,7 +551,10 @@ __all__ = [
     "mla_attn_decode_latent",
     "mla_attn_decode_latent_workspace_bytes",
     "mla_attn_prefill",
+    "mla_attn_prefill_varlen",
+    "mla_attn_prefill_masked",
     "mla_attn_decode",
+    "mla_attn_decode_masked",
     "mla_attn_decode_workspace_bytes",
     "MLAError",
     "LIB_PATH",

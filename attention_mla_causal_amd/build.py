@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libmla_attn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["mla_attn_abi.hip", "mla_prefill.hip", "mla_decode.hip", "mla_latent.hip"]
+SOURCES = ["mla_attn_abi.hip", "mla_prefill.hip", "mla_decode.hip", "mla_latent.hip", "mla_rope.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",

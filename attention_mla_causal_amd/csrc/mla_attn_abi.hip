@@ -385,6 +385,48 @@ mla_status mla_attn_decode_latent(const void* q_nope, const void* q_pe, const vo
   return MLA_OK;
 }
 
+size_t mla_rope_table_bytes(int32_t max_pos) { return mla::rope_table_bytes(max_pos); }
+
+mla_status mla_rope_table(void* table, int32_t max_pos, double theta, double factor,
+                          int32_t original_max_position, double beta_fast, double beta_slow,
+                          void* stream) {
+  const mla::CheckResult r = mla::check_rope_table(table, max_pos, theta, factor,
+                                                   original_max_position, beta_fast, beta_slow);
+  if (r.status != MLA_OK) return report("mla_rope_table", r);
+  if (r.empty) return MLA_OK;
+  mla::RopeTableArgs a;
+  a.table = static_cast<float*>(table);
+  a.max_pos = max_pos;
+  a.original_max_position = original_max_position;
+  a.theta = theta;
+  a.factor = factor;
+  a.beta_fast = beta_fast;
+  a.beta_slow = beta_slow;
+  const hipError_t e = mla::launch_rope_table(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error("mla_rope_table", e);
+  return MLA_OK;
+}
+
+mla_status mla_rope_apply(void* x, const int32_t* past_lens, const void* table, int32_t max_pos,
+                          int32_t B, int32_t R, int32_t T, int32_t past_len, void* stream) {
+  const mla::CheckResult r =
+      mla::check_rope_apply(x, past_lens, table, max_pos, B, R, T, past_len);
+  if (r.status != MLA_OK) return report("mla_rope_apply", r);
+  if (r.empty) return MLA_OK;
+  mla::RopeApplyArgs a;
+  a.x = static_cast<uint16_t*>(x);
+  a.table = static_cast<const float*>(table);
+  a.past_lens = past_lens;
+  a.rows = (int64_t)B * R * T;
+  a.R = R;
+  a.T = T;
+  a.past_len = past_len;
+  a.max_pos = max_pos;
+  const hipError_t e = mla::launch_rope_apply(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error("mla_rope_apply", e);
+  return MLA_OK;
+}
+
 const char* mla_status_string(mla_status s) {
   switch (s) {
     case MLA_OK: return "MLA_OK";

@@ -606,6 +606,89 @@ inline CheckResult check_latent_decode(const void* q_nope, const void* q_pe, con
   return r;
 }
 
+// Rotary prologue. The table holds cos and sin (fp32) of every pair at every
+// position 0..max_pos-1: 32 pairs x 2 floats = 256 bytes per position.
+constexpr int64_t kRopePairs = 32;
+constexpr int64_t kRopeTableBytesPerPos = kRopePairs * 2 * 4;
+constexpr int64_t kRopeMaxPositions = int64_t(1) << 24;  // positions exact in fp32 and fp64
+
+inline size_t rope_table_bytes(int64_t max_pos) {
+  return (max_pos <= 0 || max_pos > kRopeMaxPositions) ? 0 : size_t(max_pos) * kRopeTableBytesPerPos;
+}
+
+inline CheckResult check_rope_table(const void* table, int64_t max_pos, double theta, double factor,
+                                    int64_t original_max_position, double beta_fast,
+                                    double beta_slow) {
+  CheckResult r;
+  if (max_pos < 0 || max_pos > kRopeMaxPositions) {
+    std::snprintf(r.msg, sizeof(r.msg), "max_pos %lld outside [0, %lld]", (long long)max_pos,
+                  (long long)kRopeMaxPositions);
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  if (original_max_position <= 0) {
+    std::snprintf(r.msg, sizeof(r.msg), "original_max_position %lld must be positive",
+                  (long long)original_max_position);
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  if (!std::isfinite(theta) || !(theta > 1.0) || !std::isfinite(factor) || !(factor >= 1.0) ||
+      !std::isfinite(beta_fast) || !std::isfinite(beta_slow)) {
+    std::snprintf(r.msg, sizeof(r.msg),
+                  "rope parameters out of range: theta %g (> 1), factor %g (>= 1), betas %g, %g "
+                  "(finite)", theta, factor, beta_fast, beta_slow);
+    r.status = MLA_ERR_SCALE;
+    return r;
+  }
+  if (max_pos == 0) {
+    r.empty = true;
+    return r;
+  }
+  if (table == nullptr) return fail(MLA_ERR_NULL, "table is NULL");
+  if (misaligned(table)) return fail(MLA_ERR_ALIGN, "table is not 16-byte aligned");
+  return r;
+}
+
+// x: [B, R, T, 64] bf16, rotated in place; row t of sequence b at position
+// past_len + t (past_lens NULL) or past_lens[b] + t.
+inline CheckResult check_rope_apply(const void* x, const int32_t* past_lens, const void* table,
+                                    int64_t max_pos, int64_t B, int64_t R, int64_t T,
+                                    int64_t past_len) {
+  CheckResult r;
+  if (B < 0 || R < 0 || T < 0 || past_len < 0 || max_pos < 0) {
+    std::snprintf(r.msg, sizeof(r.msg), "negative size: B=%lld R=%lld T=%lld past_len=%lld max_pos=%lld",
+                  (long long)B, (long long)R, (long long)T, (long long)past_len, (long long)max_pos);
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  if (max_pos > kRopeMaxPositions) {
+    std::snprintf(r.msg, sizeof(r.msg), "max_pos %lld beyond %lld", (long long)max_pos,
+                  (long long)kRopeMaxPositions);
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  if (past_lens == nullptr && past_len + T > max_pos) {
+    std::snprintf(r.msg, sizeof(r.msg), "positions up to past_len %lld + T %lld - 1 need a table of "
+                  "at least %lld positions, not %lld", (long long)past_len, (long long)T,
+                  (long long)(past_len + T), (long long)max_pos);
+    r.status = MLA_ERR_SHAPE;
+    return r;
+  }
+  if (B == 0 || R == 0 || T == 0) {
+    r.empty = true;
+    return r;
+  }
+  if (max_pos == 0) return fail(MLA_ERR_SHAPE, "an empty table cannot rotate any row");
+  if (B * R * T > kMaxGrid) return fail(MLA_ERR_SHAPE, "B * R * T rows beyond the launch limit");
+  if (x == nullptr) return fail(MLA_ERR_NULL, "x is NULL");
+  if (table == nullptr) return fail(MLA_ERR_NULL, "table is NULL");
+  if (misaligned(x)) return fail(MLA_ERR_ALIGN, "x is not 16-byte aligned");
+  if (misaligned(table)) return fail(MLA_ERR_ALIGN, "table is not 16-byte aligned");
+  if (past_lens != nullptr && (reinterpret_cast<uintptr_t>(past_lens) & 3u) != 0)
+    return fail(MLA_ERR_ALIGN, "past_lens is not 4-byte aligned");
+  return r;
+}
+
 }  // namespace mla
 
 #endif  // MLA_HOST_CHECKS_H_

@@ -82,9 +82,26 @@ struct LatentArgs {
 
 // Queries per prefill workgroup.
 int prefill_block_m();
+struct RopeTableArgs {
+  float* table;            // [max_pos, 32] (cos, sin) pairs
+  int32_t max_pos;
+  int32_t original_max_position;
+  double theta, factor, beta_fast, beta_slow;
+};
+
+struct RopeApplyArgs {
+  uint16_t* x;             // [B, R, T, 64] bf16, rotated in place
+  const float* table;      // [max_pos, 32] (cos, sin) pairs
+  const int32_t* past_lens;  // [B] or null: past_len for every sequence
+  int64_t rows;            // B * R * T
+  int32_t R, T, past_len, max_pos;
+};
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_latent_decode(const LatentArgs& a, hipStream_t stream);
+hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t stream);
+hipError_t launch_rope_apply(const RopeApplyArgs& a, hipStream_t stream);
 
 }  // namespace mla
 

@@ -54,7 +54,8 @@ typedef enum mla_status {
   MLA_ERR_NULL = 1,      /* a pointer to a non-empty tensor is NULL */
   MLA_ERR_SHAPE = 2,     /* negative size, S != past_len + T, or size beyond the launch limits */
   MLA_ERR_ALIGN = 3,     /* a tensor pointer is not 16-byte aligned */
-  MLA_ERR_SCALE = 4,     /* softmax_scale is NaN, infinite, zero or negative */
+  MLA_ERR_SCALE = 4,     /* softmax_scale is NaN, infinite, zero or negative (or a RoPE
+                            parameter out of range) */
   MLA_ERR_WORKSPACE = 5, /* decode workspace missing or smaller than required */
   MLA_ERR_DEVICE = 6     /* the HIP runtime reported an error at launch */
 } mla_status;
@@ -353,6 +354,60 @@ mla_status mla_attn_decode_latent(const void* q_nope, const void* q_pe,
                                   void* workspace, size_t workspace_bytes,
                                   int32_t B, int32_t H, int32_t S, int32_t past_len,
                                   float softmax_scale, void* stream);
+
+/*
+ * Rotary prologue (YaRN-scaled RoPE on the 64 rotary dims). The
+ * "Similarities" page ("Query-key similarity") rotates the new tokens' q_pe
+ * and k_pe with a cos/sin table built for kv_seq_len positions and picked by
+ * position, before they join the non-rotary parts; the attention calls above
+ * take q_pe and k_pe after this rotation. The released configuration
+ * ("Embedded state" page, config.json) gives rope_theta 50000 and a "yarn"
+ * rope_scaling: factor 32, original_max_position_embeddings 4096,
+ * beta_fast = beta_slow = 1, mscale = mscale_all_dim = 1. The pages print
+ * neither the rotation nor the YaRN formula; this library takes them as
+ * published: pair i = dims (2i, 2i+1) turns by pos * w_i' (RoPE, Su et al.),
+ * (x, y) -> (x cos - y sin, x sin + y cos), with w_i = theta^(-2i/64) and,
+ * when factor != 1, w_i' = g_i w_i + (1 - g_i) w_i / factor where g_i is
+ * YaRN's ramp (Peng et al.) over the turns r_i = L w_i / (2 pi) that pair i
+ * makes within L = original_max_position: 1 for r_i >= beta_fast, 0 for
+ * r_i < beta_slow, (r_i - beta_slow) / (beta_fast - beta_slow) between.
+ * YaRN's logit temperature (mscale) is not part of the table: it belongs to
+ * softmax_scale.
+ */
+
+/* Bytes of the table for positions 0..max_pos-1 (256 per position); 0 for
+ * max_pos <= 0 or beyond 16,777,216. A pure function of its argument. */
+size_t mla_rope_table_bytes(int32_t max_pos);
+
+/*
+ * Fill table [max_pos, 32, 2] fp32 with (cos, sin) of pos * w_i' for every
+ * position pos < max_pos and pair i < 32 (angle, cosine and sine computed in
+ * fp64, stored rounded to fp32). table: device memory, 16-byte aligned, at
+ * least mla_rope_table_bytes(max_pos) bytes. Errors: MLA_ERR_SHAPE for
+ * max_pos outside [0, 16,777,216] or original_max_position <= 0;
+ * MLA_ERR_SCALE unless theta > 1, factor >= 1 and both betas are finite;
+ * MLA_ERR_NULL / MLA_ERR_ALIGN for the table. max_pos == 0 is a no-op.
+ */
+mla_status mla_rope_table(void* table, int32_t max_pos, double theta, double factor,
+                          int32_t original_max_position, double beta_fast, double beta_slow,
+                          void* stream);
+
+/*
+ * Rotate x [B, R, T, 64] bf16 in place: R = H for the new queries' q_pe, or
+ * R = 1 for the new keys' shared k_pe (before they are appended to a cache).
+ * Row t of sequence b sits at position past_len + t, or past_lens[b] + t when
+ * past_lens ([B] int32, device memory, 4-byte aligned) is given; positions
+ * read from past_lens are clamped on the device into [0, max_pos), so the
+ * table must cover every position. The rotation runs in fp32 on the bf16
+ * inputs and the fp32 table; results are rounded to nearest even bf16.
+ * Errors: MLA_ERR_SHAPE for negative sizes, for past_len + T > max_pos
+ * (without past_lens), max_pos == 0 with rows to rotate, or more than
+ * 2^31 - 1 rows; MLA_ERR_NULL / MLA_ERR_ALIGN for x (16-byte) and the table
+ * (16-byte). B, R or T == 0 is a no-op. The host reads no device memory, so
+ * a graph can capture the call and past_lens can change between replays.
+ */
+mla_status mla_rope_apply(void* x, const int32_t* past_lens, const void* table, int32_t max_pos,
+                          int32_t B, int32_t R, int32_t T, int32_t past_len, void* stream);
 
 /* Static name of a status code ("MLA_OK", ...); "unknown status" otherwise. */
 const char* mla_status_string(mla_status s);

@@ -181,6 +181,40 @@ int main() {
     EXPECT(check_latent_decode(p, p, p, p, p, p, p, size_t(1) << 40, 1, 64, 2097151, 2097150, sc, &lp).status == MLA_OK);
     EXPECT(check_latent_decode(p, p, p, p, p, p, p, size_t(1) << 40, 1, 64, 2097152, 2097151, sc, &lp).status == MLA_ERR_SHAPE);
   }
+  // rotary prologue: table sizes and parameters, rotation sizes and positions
+  {
+    EXPECT(rope_table_bytes(4096) == size_t(4096) * 256);
+    EXPECT(rope_table_bytes(0) == 0 && rope_table_bytes(-1) == 0);
+    EXPECT(rope_table_bytes(int64_t(1) << 24) == (size_t(1) << 24) * 256);
+    EXPECT(rope_table_bytes((int64_t(1) << 24) + 1) == 0);
+    EXPECT(check_rope_table(p, 4096, 50000.0, 32.0, 4096, 1.0, 1.0).status == MLA_OK);
+    EXPECT(check_rope_table(nullptr, 0, 50000.0, 32.0, 4096, 1.0, 1.0).empty);
+    EXPECT(check_rope_table(p, -1, 50000.0, 32.0, 4096, 1.0, 1.0).status == MLA_ERR_SHAPE);
+    EXPECT(check_rope_table(p, 16, 50000.0, 32.0, 0, 1.0, 1.0).status == MLA_ERR_SHAPE);
+    EXPECT(check_rope_table(p, 16, 1.0, 32.0, 4096, 1.0, 1.0).status == MLA_ERR_SCALE);
+    EXPECT(check_rope_table(p, 16, NAN, 32.0, 4096, 1.0, 1.0).status == MLA_ERR_SCALE);
+    EXPECT(check_rope_table(p, 16, 50000.0, 0.5, 4096, 1.0, 1.0).status == MLA_ERR_SCALE);
+    EXPECT(check_rope_table(p, 16, 50000.0, 32.0, 4096, INFINITY, 1.0).status == MLA_ERR_SCALE);
+    EXPECT(check_rope_table(nullptr, 16, 50000.0, 32.0, 4096, 1.0, 1.0).status == MLA_ERR_NULL);
+    EXPECT(check_rope_table(bad, 16, 50000.0, 32.0, 4096, 1.0, 1.0).status == MLA_ERR_ALIGN);
+
+    const int32_t* lens = reinterpret_cast<const int32_t*>(p);
+    EXPECT(check_rope_apply(p, nullptr, p, 4096, 1, 64, 2048, 2048).status == MLA_OK);
+    EXPECT(check_rope_apply(p, nullptr, p, 4096, 1, 64, 2048, 2049).status == MLA_ERR_SHAPE);  // position 4096
+    EXPECT(check_rope_apply(p, lens, p, 4096, 1, 64, 2048, 2049).status == MLA_OK);  // positions from past_lens
+    EXPECT(check_rope_apply(p, nullptr, p, 4096, -1, 64, 1, 0).status == MLA_ERR_SHAPE);
+    EXPECT(check_rope_apply(nullptr, nullptr, nullptr, 4096, 0, 64, 5, 0).empty);
+    EXPECT(check_rope_apply(p, lens, p, 0, 1, 1, 1, 0).status == MLA_ERR_SHAPE);     // empty table
+    EXPECT(check_rope_apply(nullptr, nullptr, p, 16, 1, 1, 1, 0).status == MLA_ERR_NULL);
+    EXPECT(check_rope_apply(p, nullptr, nullptr, 16, 1, 1, 1, 0).status == MLA_ERR_NULL);
+    EXPECT(check_rope_apply(bad, nullptr, p, 16, 1, 1, 1, 0).status == MLA_ERR_ALIGN);
+    EXPECT(check_rope_apply(p, nullptr, bad, 16, 1, 1, 1, 0).status == MLA_ERR_ALIGN);
+    EXPECT(check_rope_apply(p, reinterpret_cast<const int32_t*>(reinterpret_cast<uintptr_t>(p) + 4), p,
+                            16, 1, 1, 1, 0).status == MLA_OK);                          // lengths: 4-byte alignment
+    EXPECT(check_rope_apply(p, reinterpret_cast<const int32_t*>(reinterpret_cast<uintptr_t>(p) + 2), p,
+                            16, 1, 1, 1, 0).status == MLA_ERR_ALIGN);
+    EXPECT(check_rope_apply(p, lens, p, 1 << 20, 65536, 64, 1024, 0).status == MLA_ERR_SHAPE);  // 2^32 rows
+  }
   if (failures) {
     std::printf("%d failures\n", failures);
     return 1;

@@ -38,6 +38,7 @@ def test_header_declares_the_boundary():
         "mla_attn_prefill_ws", "mla_attn_prefill_workspace_bytes",
         "mla_attn_prefill_varlen",
         "mla_attn_prefill_masked", "mla_attn_decode_masked",
+        "mla_rope_table", "mla_rope_table_bytes", "mla_rope_apply",
         "mla_last_error", "mla_status_string"])
 
 
@@ -293,6 +294,24 @@ def test_masked_errors(lib):
     assert dec(odd, ALIGNED, need, 1, 64, 1001, 1000, float("inf")) == 4
     assert "mla_attn_decode_masked" in lib.mla_last_error().decode()
     assert dec([None] * 7, None, 0, 1, 0, 1001, 1000) == 0
+
+
+def test_rope_errors(lib):
+    AL, MIS = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x100008)
+    assert lib.mla_rope_table_bytes(4096) == 4096 * 256
+    assert lib.mla_rope_table_bytes(0) == 0 and lib.mla_rope_table_bytes(-3) == 0
+    assert lib.mla_rope_table(None, 0, 50000.0, 32.0, 4096, 1.0, 1.0, None) == 0      # empty
+    assert lib.mla_rope_table(AL, -1, 50000.0, 32.0, 4096, 1.0, 1.0, None) == 2
+    assert lib.mla_rope_table(AL, 16, 50000.0, float("nan"), 4096, 1.0, 1.0, None) == 4
+    assert lib.mla_rope_table(None, 16, 50000.0, 32.0, 4096, 1.0, 1.0, None) == 1
+    assert lib.mla_rope_table(MIS, 16, 50000.0, 32.0, 4096, 1.0, 1.0, None) == 3
+    assert "mla_rope_table" in lib.mla_last_error().decode()
+    assert lib.mla_rope_apply(AL, None, AL, 4096, 1, 64, 2048, 2049, None) == 2        # past the table
+    assert "table" in lib.mla_last_error().decode()
+    assert lib.mla_rope_apply(None, None, None, 0, 1, 64, 0, 0, None) == 0            # empty
+    assert lib.mla_rope_apply(None, None, AL, 16, 1, 1, 1, 0, None) == 1
+    assert lib.mla_rope_apply(MIS, None, AL, 16, 1, 1, 1, 0, None) == 3
+    assert lib.mla_rope_apply(AL, ctypes.c_void_p(0x100002), AL, 16, 1, 1, 1, 0, None) == 3
 
 
 def test_product_path_never_touches_the_oracle():
