@@ -53,6 +53,10 @@ SIGNATURES = {
     "mla_rope_table": (ctypes.c_int, [_VP, _I32, ctypes.c_double, ctypes.c_double, _I32, ctypes.c_double,
                                       ctypes.c_double, _VP]),
     "mla_rope_apply": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP]),
+    "mla_attn_decode_rope": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _SZ, _I32, _I32, _I32,
+                                            _I32, _F32, _VP]),
+    "mla_attn_decode_paged_rope": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32,
+                                                  _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_last_error": (ctypes.c_char_p, []),
 }
@@ -284,13 +288,22 @@ def mla_attn_decode_workspace_bytes(B: int, H: int, S: int) -> int:
     return int(_lib.mla_attn_decode_workspace_bytes(int(B), int(H), int(S)))
 
 
+def _check_rope_table(table, device):
+    import torch
+    if not (isinstance(table, torch.Tensor) and table.dtype == torch.float32 and table.is_contiguous()
+            and table.dim() == 3 and tuple(table.shape[1:]) == (32, 2) and table.device == device):
+        raise ValueError(f"rope_table must be a contiguous float32 [max_pos, 32, 2] tensor on {device}")
+
+
 def mla_attn_decode(q_nope, q_pe, k_nope, k_pe, v, past_len: int, softmax_scale: float,
-                    out=None, workspace=None):
+                    out=None, workspace=None, rope_table=None):
     """One new query per sequence (T = 1) against S = past_len + 1 keys.
 
     workspace: a GPU tensor of at least mla_attn_decode_workspace_bytes(B, H, S)
     bytes of scratch (contents irrelevant, reusable by non-overlapping calls);
-    allocated here when omitted.
+    allocated here when omitted. rope_table (from mla_rope_table): q_pe is
+    taken before rotation and turned at position past_len in the kernel
+    (mla_attn_decode_rope).
     """
     import torch
 
@@ -309,6 +322,14 @@ def mla_attn_decode(q_nope, q_pe, k_nope, k_pe, v, past_len: int, softmax_scale:
     if not (workspace.is_cuda and workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous GPU tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
+    if rope_table is not None:
+        _check_rope_table(rope_table, q_nope.device)
+        st = _lib.mla_attn_decode_rope(
+            q_nope.data_ptr(), q_pe.data_ptr(), k_nope.data_ptr(), k_pe.data_ptr(), v.data_ptr(),
+            rope_table.data_ptr(), int(rope_table.shape[0]), out.data_ptr(), workspace.data_ptr(),
+            ws_bytes, B, H, S, int(past_len), float(softmax_scale), _stream_handle(q_nope.device))
+        _raise_for(st, "mla_attn_decode_rope")
+        return out
     st = _lib.mla_attn_decode(
         q_nope.data_ptr(), q_pe.data_ptr(), k_nope.data_ptr(), k_pe.data_ptr(), v.data_ptr(),
         out.data_ptr(), workspace.data_ptr(), ws_bytes, B, H, S, int(past_len),
@@ -374,7 +395,8 @@ def _check_int32(t, name, shape, device):
 
 
 def mla_attn_decode_paged(q_nope, q_pe, k_nope_pages, k_pe_pages, v_pages, block_table, seq_lens,
-                          max_seq_len: int, softmax_scale: float, new=None, out=None, workspace=None):
+                          max_seq_len: int, softmax_scale: float, new=None, out=None, workspace=None,
+                          rope_table=None):
     """Decode over a paged cache, optionally appending the new token.
 
     k_nope_pages / v_pages [N, H, bs, 128], k_pe_pages [N, bs, 64] (bs a
@@ -382,6 +404,9 @@ def mla_attn_decode_paged(q_nope, q_pe, k_nope_pages, k_pe_pages, v_pages, block
     the call, clamped on the device to [0, max_seq_len]). new: None or
     (k_nope_new [B,H,1,128], k_pe_new [B,1,1,64], v_new [B,H,1,128]), attended
     to as key seq_lens[b]-1 and written into that slot of the pages.
+    rope_table (from mla_rope_table): q_pe and k_pe_new are taken before
+    rotation and turned at position seq_lens[b]-1 in the kernel, the new key
+    stored rotated (mla_attn_decode_paged_rope).
     Returns out [B,H,1,128] bf16 on the current stream.
     """
     import torch
@@ -427,6 +452,16 @@ def mla_attn_decode_paged(q_nope, q_pe, k_nope_pages, k_pe_pages, v_pages, block
     if not (workspace.is_cuda and workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous GPU tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
+    if rope_table is not None:
+        _check_rope_table(rope_table, q_nope.device)
+        st = _lib.mla_attn_decode_paged_rope(
+            q_nope.data_ptr(), q_pe.data_ptr(), k_nope_pages.data_ptr(), k_pe_pages.data_ptr(),
+            v_pages.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), *ptr_new,
+            rope_table.data_ptr(), int(rope_table.shape[0]), out.data_ptr(), workspace.data_ptr(),
+            ws_bytes, B, H, N, bs, M, int(max_seq_len), float(softmax_scale),
+            _stream_handle(q_nope.device))
+        _raise_for(st, "mla_attn_decode_paged_rope")
+        return out
     st = _lib.mla_attn_decode_paged(
         q_nope.data_ptr(), q_pe.data_ptr(), k_nope_pages.data_ptr(), k_pe_pages.data_ptr(),
         v_pages.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), *ptr_new, out.data_ptr(),

@@ -47,7 +47,23 @@ struct DecodeExtras {
   const void* kp_new = nullptr;
   const void* v_new = nullptr;
   const uint8_t* key_mask = nullptr;  // [B, S] 2D padding mask
+  const float* rope_table = nullptr;  // fused rotary prologue: (cos, sin) [>= S positions, 32]
 };
+
+// The rotary table a fused-prologue decode reads: present, aligned, and
+// holding every position up to need - 1.
+mla::CheckResult check_rope_arg(const void* table, int64_t max_pos, int64_t need) {
+  if (table == nullptr) return mla::fail(MLA_ERR_NULL, "rope_table is NULL");
+  if (mla::misaligned(table)) return mla::fail(MLA_ERR_ALIGN, "rope_table is not 16-byte aligned");
+  if (max_pos < need || max_pos > mla::kRopeMaxPositions) {
+    mla::CheckResult r;
+    r.status = MLA_ERR_SHAPE;
+    std::snprintf(r.msg, sizeof(r.msg), "rope_max_pos %lld must cover positions 0..%lld (at most %lld)",
+                  (long long)max_pos, (long long)(need - 1), (long long)mla::kRopeMaxPositions);
+    return r;
+  }
+  return mla::CheckResult{};
+}
 
 // Every decode entry point: fill the arguments from a checked plan and launch.
 mla_status launch_decode_call(const char* where, const void* q_nope, const void* q_pe,
@@ -65,7 +81,14 @@ mla_status launch_decode_call(const char* where, const void* q_nope, const void*
   a.kn_new = static_cast<const uint16_t*>(x.kn_new);
   a.kp_new = static_cast<const uint16_t*>(x.kp_new);
   a.v_new = static_cast<const uint16_t*>(x.v_new);
-  a.key_mask = x.key_mask;
+  mla::DecodeKind kind = mla::kDecodePlain;
+  if (x.key_mask != nullptr) {
+    a.key_mask = x.key_mask;
+    kind = mla::kDecodeMasked;
+  } else if (x.rope_table != nullptr) {
+    a.rope_table = x.rope_table;
+    kind = mla::kDecodeRope;
+  }
   a.cap = cap;
   a.q_nope = static_cast<const uint16_t*>(q_nope);
   a.q_pe = static_cast<const uint16_t*>(q_pe);
@@ -104,7 +127,7 @@ mla_status launch_decode_call(const char* where, const void* q_nope, const void*
   a.nsplit = (int32_t)plan.nsplit;
   a.keys_per_split = (int32_t)plan.keys_per_split;
   a.scale_log2 = softmax_scale * kLog2e;
-  const hipError_t e = mla::launch_decode(a, static_cast<hipStream_t>(stream));
+  const hipError_t e = mla::launch_decode(a, kind, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error(where, e);
   return MLA_OK;
 }
@@ -261,6 +284,23 @@ mla_status mla_attn_decode(const void* q_nope, const void* q_pe, const void* k_n
                             out, workspace, plan, B, H, S, S, softmax_scale, stream);
 }
 
+mla_status mla_attn_decode_rope(const void* q_nope, const void* q_pe, const void* k_nope,
+                                const void* k_pe, const void* v, const void* rope_table,
+                                int32_t rope_max_pos, void* out, void* workspace,
+                                size_t workspace_bytes, int32_t B, int32_t H, int32_t S,
+                                int32_t past_len, float softmax_scale, void* stream) {
+  mla::DecodePlan plan;
+  mla::CheckResult r = mla::check_decode(q_nope, q_pe, k_nope, k_pe, v, out, workspace,
+                                         workspace_bytes, B, H, S, past_len, softmax_scale, &plan);
+  if (r.status == MLA_OK && !r.empty) r = check_rope_arg(rope_table, rope_max_pos, (int64_t)past_len + 1);
+  if (r.status != MLA_OK) return report("mla_attn_decode_rope", r);
+  if (r.empty) return MLA_OK;
+  DecodeExtras x;
+  x.rope_table = static_cast<const float*>(rope_table);
+  return launch_decode_call("mla_attn_decode_rope", q_nope, q_pe, k_nope, k_pe, v, x, out,
+                            workspace, plan, B, H, S, S, softmax_scale, stream);
+}
+
 mla_status mla_attn_decode_masked(const void* q_nope, const void* q_pe, const void* k_nope,
                                   const void* k_pe, const void* v, const uint8_t* attn_mask,
                                   void* out, void* workspace, size_t workspace_bytes, int32_t B,
@@ -320,21 +360,28 @@ size_t mla_attn_decode_paged_workspace_bytes(int32_t B, int32_t H, int32_t max_s
   return mla::plan_decode_varlen(B, H, max_seq_len).workspace_bytes;
 }
 
-mla_status mla_attn_decode_paged(const void* q_nope, const void* q_pe, void* k_nope_pages,
-                                 void* k_pe_pages, void* v_pages, const int32_t* block_table,
-                                 const int32_t* seq_lens, const void* k_nope_new,
-                                 const void* k_pe_new, const void* v_new, void* out,
-                                 void* workspace, size_t workspace_bytes, int32_t B, int32_t H,
-                                 int32_t num_blocks, int32_t block_size, int32_t max_blocks,
-                                 int32_t max_seq_len, float softmax_scale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+mla_status decode_paged_call(const char* where, const void* q_nope, const void* q_pe,
+                             void* k_nope_pages, void* k_pe_pages, void* v_pages,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const void* k_nope_new, const void* k_pe_new, const void* v_new,
+                             bool rope, const void* rope_table, int32_t rope_max_pos, void* out,
+                             void* workspace, size_t workspace_bytes, int32_t B, int32_t H,
+                             int32_t num_blocks, int32_t block_size, int32_t max_blocks,
+                             int32_t max_seq_len, float softmax_scale, void* stream) {
   mla::DecodePlan plan;
-  const mla::CheckResult r = mla::check_decode_paged(
+  mla::CheckResult r = mla::check_decode_paged(
       q_nope, q_pe, k_nope_pages, k_pe_pages, v_pages, block_table, seq_lens, k_nope_new,
       k_pe_new, v_new, out, workspace, workspace_bytes, B, H, num_blocks, block_size, max_blocks,
       max_seq_len, softmax_scale, &plan);
-  if (r.status != MLA_OK) return report("mla_attn_decode_paged", r);
+  if (r.status == MLA_OK && !r.empty && rope) r = check_rope_arg(rope_table, rope_max_pos, max_seq_len);
+  if (r.status != MLA_OK) return report(where, r);
   if (r.empty) return MLA_OK;
   DecodeExtras x;
+  x.rope_table = rope ? static_cast<const float*>(rope_table) : nullptr;
   x.seq_lens = seq_lens;
   x.block_table = block_table;
   x.max_blocks = max_blocks;
@@ -343,9 +390,40 @@ mla_status mla_attn_decode_paged(const void* q_nope, const void* q_pe, void* k_n
   x.kn_new = k_nope_new;
   x.kp_new = k_pe_new;
   x.v_new = v_new;
-  return launch_decode_call("mla_attn_decode_paged", q_nope, q_pe, k_nope_pages, k_pe_pages,
-                            v_pages, x, out, workspace, plan, B, H, max_seq_len, 0,
-                            softmax_scale, stream);
+  return launch_decode_call(where, q_nope, q_pe, k_nope_pages, k_pe_pages, v_pages, x, out,
+                            workspace, plan, B, H, max_seq_len, 0, softmax_scale, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_attn_decode_paged(const void* q_nope, const void* q_pe, void* k_nope_pages,
+                                 void* k_pe_pages, void* v_pages, const int32_t* block_table,
+                                 const int32_t* seq_lens, const void* k_nope_new,
+                                 const void* k_pe_new, const void* v_new, void* out,
+                                 void* workspace, size_t workspace_bytes, int32_t B, int32_t H,
+                                 int32_t num_blocks, int32_t block_size, int32_t max_blocks,
+                                 int32_t max_seq_len, float softmax_scale, void* stream) {
+  return decode_paged_call("mla_attn_decode_paged", q_nope, q_pe, k_nope_pages, k_pe_pages,
+                           v_pages, block_table, seq_lens, k_nope_new, k_pe_new, v_new, false,
+                           nullptr, 0, out, workspace, workspace_bytes, B, H, num_blocks, block_size,
+                           max_blocks, max_seq_len, softmax_scale, stream);
+}
+
+mla_status mla_attn_decode_paged_rope(const void* q_nope, const void* q_pe, void* k_nope_pages,
+                                      void* k_pe_pages, void* v_pages, const int32_t* block_table,
+                                      const int32_t* seq_lens, const void* k_nope_new,
+                                      const void* k_pe_new, const void* v_new,
+                                      const void* rope_table, int32_t rope_max_pos, void* out,
+                                      void* workspace, size_t workspace_bytes, int32_t B,
+                                      int32_t H, int32_t num_blocks, int32_t block_size,
+                                      int32_t max_blocks, int32_t max_seq_len,
+                                      float softmax_scale, void* stream) {
+  return decode_paged_call("mla_attn_decode_paged_rope", q_nope, q_pe, k_nope_pages, k_pe_pages,
+                           v_pages, block_table, seq_lens, k_nope_new, k_pe_new, v_new, true, rope_table,
+                           rope_max_pos, out, workspace, workspace_bytes, B, H, num_blocks,
+                           block_size, max_blocks, max_seq_len, softmax_scale, stream);
 }
 
 size_t mla_attn_decode_latent_workspace_bytes(int32_t B, int32_t H, int32_t S) {

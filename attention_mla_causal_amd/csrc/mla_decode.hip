@@ -7,7 +7,9 @@
 // token's key and value may be appended by the call itself (the cache update
 // the "Similarities" page runs before attending). A second instantiation
 // takes the caller's general 2D padding mask ([B, S] bytes, nonzero keeps):
-// it fetches each trip's mask bytes a trip ahead and loads only kept rows.
+// it fetches each trip's mask bytes a trip ahead and loads only kept rows. A
+// third fuses the rotary prologue: the new token's query (and appended key)
+// turns at its position in registers, from a cos/sin table, before scoring.
 //
 // The same computation as prefill with T = 1 (the Kimi K2 "Similarities"
 // page shows it in decode mode with p = 1000: scores [B, 64, 1, 1001]); the
@@ -109,7 +111,7 @@ __device__ __forceinline__ void merge_xor(float& m, float& l, float (&o)[8], int
 // MASKED: the caller's 2D padding mask hides keys (a.key_mask, [B, S] bytes,
 // nonzero keeps); one instantiation each, so the unmasked kernel carries none
 // of its code.
-template <bool MASKED>
+template <bool MASKED, bool ROPE>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   __shared__ float red_o[NW][DV];
   __shared__ float red_ml[NW][2];
@@ -188,6 +190,23 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     for (int e = 0; e < 2; ++e) {
       qp[2 * e] = lo_bf16(wp[e]);
       qp[2 * e + 1] = hi_bf16(wp[e]);
+    }
+  }
+  // Fused rotary prologue (the rotary instantiation): the new token's query, and its
+  // key when the call appends it, turn at position S-1, the last key of the
+  // sequence. Lane cl holds rotary dims 4cl..4cl+3, i.e. whole pairs 2cl and
+  // 2cl+1, so it reads their (cos, sin) and rotates in its own registers.
+  f32x4 rope_cs = {1.0f, 0.0f, 1.0f, 0.0f};
+  if (ROPE) {
+    // S <= a.S and the host checked that the table holds a.S positions
+    const int64_t pos = S > 0 ? S - 1 : 0;
+    rope_cs = *reinterpret_cast<const f32x4*>(a.rope_table + pos * 64 + 4 * cl);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float x = qp[2 * e], y = qp[2 * e + 1];
+      const float c = rope_cs[2 * e], sn = rope_cs[2 * e + 1];
+      qp[2 * e] = x * c - y * sn;
+      qp[2 * e + 1] = x * sn + y * c;
     }
   }
 
@@ -337,7 +356,17 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   // every head reads key S-1 from the new rows, so no one reads that slot).
   if (owns_new && wave == 0 && qq == 0) {
     const u32x4 kw = *reinterpret_cast<const u32x4*>(a.kn_new + (int64_t)bh * DN + 8 * cl);
-    const u32x2 pw = *reinterpret_cast<const u32x2*>(a.kp_new + (int64_t)b * DR + 4 * cl);
+    u32x2 pw = *reinterpret_cast<const u32x2*>(a.kp_new + (int64_t)b * DR + 4 * cl);
+    if (ROPE) {
+      // the new key's rotary part, rotated and rounded as it is stored: this
+      // call and every later one attend to the same bf16 values
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float x = lo_bf16(pw[e]), y = hi_bf16(pw[e]);
+        const float c = rope_cs[2 * e], sn = rope_cs[2 * e + 1];
+        pw[e] = (uint32_t)to_bf16_rne(x * c - y * sn) | ((uint32_t)to_bf16_rne(x * sn + y * c) << 16);
+      }
+    }
     const u32x4 vw = *reinterpret_cast<const u32x4*>(a.v_new + (int64_t)bh * DV + 8 * cl);
     float d = 0.0f;
 #pragma unroll
@@ -495,8 +524,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   }
 }
 
-__global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) { decode_body<false>(a); }
-__global__ __launch_bounds__(NT) void mla_decode_masked_kernel(DecodeArgs a) { decode_body<true>(a); }
+__global__ __launch_bounds__(NT) void mla_decode_kernel(DecodeArgs a) { decode_body<false, false>(a); }
+__global__ __launch_bounds__(NT) void mla_decode_masked_kernel(DecodeArgs a) { decode_body<true, false>(a); }
+__global__ __launch_bounds__(NT) void mla_decode_rope_kernel(DecodeArgs a) { decode_body<false, true>(a); }
 
 // Log-sum-exp merge of the nsplit partials of each (b, h): one wave per (b, h);
 // quarter-wave qq merges splits qq, qq+4, ..., then the quarters merge.
@@ -537,10 +567,12 @@ __global__ __launch_bounds__(64) void mla_decode_combine_kernel(DecodeArgs a) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, DecodeKind kind, hipStream_t stream) {
   const int grid = a.B * a.H * a.nsplit;
-  if (a.key_mask != nullptr)
+  if (kind == kDecodeMasked)
     hipLaunchKernelGGL(mla_decode_masked_kernel, dim3(grid), dim3(NT), 0, stream, a);
+  else if (kind == kDecodeRope)
+    hipLaunchKernelGGL(mla_decode_rope_kernel, dim3(grid), dim3(NT), 0, stream, a);
   else
     hipLaunchKernelGGL(mla_decode_kernel, dim3(grid), dim3(NT), 0, stream, a);
   if (a.nsplit > 1 && !a.fused)

@@ -409,6 +409,43 @@ mla_status mla_rope_table(void* table, int32_t max_pos, double theta, double fac
 mla_status mla_rope_apply(void* x, const int32_t* past_lens, const void* table, int32_t max_pos,
                           int32_t B, int32_t R, int32_t T, int32_t past_len, void* stream);
 
+/*
+ * mla_attn_decode with the rotary prologue fused in: q_pe is the new query's
+ * rotary part before rotation, and the kernel turns it at position past_len
+ * (the new token's, the last key) with rope_table [rope_max_pos, 32, 2]
+ * (filled by mla_rope_table; device memory, 16-byte aligned) before scoring;
+ * the rotated query stays in fp32. k_pe holds cached keys already rotated at
+ * their positions, as the pages' cache stores them. Errors as for
+ * mla_attn_decode, plus MLA_ERR_NULL / MLA_ERR_ALIGN for rope_table and
+ * MLA_ERR_SHAPE when rope_max_pos <= past_len (or beyond 16,777,216).
+ */
+mla_status mla_attn_decode_rope(const void* q_nope, const void* q_pe, const void* k_nope,
+                                const void* k_pe, const void* v, const void* rope_table,
+                                int32_t rope_max_pos, void* out, void* workspace,
+                                size_t workspace_bytes, int32_t B, int32_t H, int32_t S,
+                                int32_t past_len, float softmax_scale, void* stream);
+
+/*
+ * mla_attn_decode_paged with the rotary prologue fused in: q_pe and, when the
+ * call appends the new token, k_pe_new are rotary parts before rotation.
+ * Sequence b's new token sits at position seq_lens[b] - 1 (clamped into the
+ * table on the device); the kernel turns the query there, and turns the new
+ * key there, rounds it to bf16 and both attends to it and stores it in its
+ * slot, so later calls read the same rotated key. rope_table as for
+ * mla_attn_decode_rope, covering positions up to max_seq_len - 1
+ * (rope_max_pos >= max_seq_len, else MLA_ERR_SHAPE). Other errors as for
+ * mla_attn_decode_paged.
+ */
+mla_status mla_attn_decode_paged_rope(const void* q_nope, const void* q_pe, void* k_nope_pages,
+                                      void* k_pe_pages, void* v_pages, const int32_t* block_table,
+                                      const int32_t* seq_lens, const void* k_nope_new,
+                                      const void* k_pe_new, const void* v_new,
+                                      const void* rope_table, int32_t rope_max_pos, void* out,
+                                      void* workspace, size_t workspace_bytes, int32_t B,
+                                      int32_t H, int32_t num_blocks, int32_t block_size,
+                                      int32_t max_blocks, int32_t max_seq_len,
+                                      float softmax_scale, void* stream);
+
 /* Static name of a status code ("MLA_OK", ...); "unknown status" otherwise. */
 const char* mla_status_string(mla_status s);
 

@@ -39,6 +39,7 @@ def test_header_declares_the_boundary():
         "mla_attn_prefill_varlen",
         "mla_attn_prefill_masked", "mla_attn_decode_masked",
         "mla_rope_table", "mla_rope_table_bytes", "mla_rope_apply",
+        "mla_attn_decode_rope", "mla_attn_decode_paged_rope",
         "mla_last_error", "mla_status_string"])
 
 
@@ -312,6 +313,20 @@ def test_rope_errors(lib):
     assert lib.mla_rope_apply(None, None, AL, 16, 1, 1, 1, 0, None) == 1
     assert lib.mla_rope_apply(MIS, None, AL, 16, 1, 1, 1, 0, None) == 3
     assert lib.mla_rope_apply(AL, ctypes.c_void_p(0x100002), AL, 16, 1, 1, 1, 0, None) == 3
+    # fused prologue in decode: the table must cover the new token's position
+    ok = [AL] * 5
+    need = lib.mla_attn_decode_workspace_bytes(1, 64, 1001)
+    assert lib.mla_attn_decode_rope(*ok, AL, 1000, AL, AL, need, 1, 64, 1001, 1000, SC, None) == 2
+    assert "rope_max_pos" in lib.mla_last_error().decode()
+    assert lib.mla_attn_decode_rope(*ok, None, 1001, AL, AL, need, 1, 64, 1001, 1000, SC, None) == 1
+    assert lib.mla_attn_decode_rope(*ok, MIS, 1001, AL, AL, need, 1, 64, 1001, 1000, SC, None) == 3
+    assert lib.mla_attn_decode_rope(*ok, None, 0, AL, AL, need, 1, 64, 1001, 999, SC, None) == 2  # shape first
+    assert lib.mla_attn_decode_rope(*ok, None, 0, None, None, 0, 0, 64, 1001, 1000, SC, None) == 0  # empty
+    pw = lib.mla_attn_decode_paged_workspace_bytes(2, 8, 4096)
+    args = [AL, AL, AL, AL, AL, AL, AL, None, None, None]
+    assert lib.mla_attn_decode_paged_rope(*args, None, 4096, AL, AL, pw, 2, 8, 64, 64, 64, 4096, SC, None) == 1
+    assert lib.mla_attn_decode_paged_rope(*args, AL, 4095, AL, AL, pw, 2, 8, 64, 64, 64, 4096, SC, None) == 2
+    assert "mla_attn_decode_paged_rope" in lib.mla_last_error().decode()
 
 
 def test_product_path_never_touches_the_oracle():

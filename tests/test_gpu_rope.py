@@ -184,3 +184,68 @@ def test_empty_and_errors_through_the_binding():
         m.mla_rope_apply(y, tab, past_len=13)                             # position 16 is past the table
     assert tuple(m.mla_rope_table(0).shape) == (0, 32, 2)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("B,H,P", [(1, 64, 1000), (4, 16, 300), (32, 8, 4095)])
+def test_fused_prologue_decode(B, H, P):
+    """mla_attn_decode with rope_table: the raw q_pe turns at position past_len
+    inside the kernel; the cache's k_pe was rotated at its positions (here by
+    mla_rope_apply). Against the oracle's rotation of the query and its
+    attention over the same cached keys; and close to the unfused path
+    (rotation kernel, then the plain decode), which rounds the rotated query
+    to bf16 first."""
+    import torch
+    S = P + 1
+    log(f"case rope fused decode B={B} H={H} P={P}")
+    x = random_inputs(B, H, 1, P, seed=50 + H)
+    tab = _gpu_table(S, KIMI_K2_ROPE)
+    d = {k: to_device(v) for k, v in x.items()}
+    m = _lib()
+    m.mla_rope_apply(d["k_pe"], tab, past_len=0)                  # the cache holds rotated keys
+    k_rot_bits = to_host_bits(d["k_pe"])
+    out = m.mla_attn_decode(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], P, ALPHA, rope_table=tab)
+    cos, sin = rope_cos_sin(S, **KIMI_K2_ROPE)
+    q_rot = apply_rope(to_f64(x["q_pe"]), rope_positions(B, 1, past_len=P), cos, sin)
+    ref = mla_attention(to_f64(x["q_nope"]), q_rot, to_f64(x["k_nope"]), to_f64(k_rot_bits), to_f64(x["v"]),
+                        P, ALPHA)
+    got = to_host_f64(out)
+    assert_parity(got, ref, f"fused rope decode B={B} H={H} P={P}")
+    q2 = d["q_pe"].clone()
+    m.mla_rope_apply(q2, tab, past_len=P)
+    unfused = to_host_f64(m.mla_attn_decode(d["q_nope"], q2, d["k_nope"], d["k_pe"], d["v"], P, ALPHA))
+    torch.cuda.synchronize()
+    assert_parity(unfused, ref, "unfused")
+
+
+def test_fused_prologue_paged_append():
+    """mla_attn_decode_paged with rope_table and an appended token: the query
+    and the new key turn at position seq_lens[b] - 1; the slot receives the
+    rotated key rounded to bf16 (within half a bf16 ulp of the exact
+    rotation), and the output is the oracle's attention with the rotated query
+    over the cache holding that key."""
+    import torch
+    from oracle import mla_decode_paged
+    from seeded_inputs import paged_host_inputs, paged_layout
+    lens, H, bs = [1001, 1, 64, 300], 16, 32
+    table, N = paged_layout(lens, bs, seed=3, spare=1)
+    x = paged_host_inputs(len(lens), H, N, bs, seed=3)
+    max_len = max(lens)
+    log(f"case rope fused paged append lens={lens} H={H} bs={bs}")
+    tab = _gpu_table(max_len, KIMI_K2_ROPE)
+    d = {k: to_device(v) for k, v in x.items()}
+    tb = torch.as_tensor(table, device="cuda")
+    sl = torch.as_tensor(np.asarray(lens, dtype=np.int32), device="cuda")
+    m = _lib()
+    out = m.mla_attn_decode_paged(d["q_nope"], d["q_pe"], d["k_nope_pages"], d["k_pe_pages"], d["v_pages"],
+                                  tb, sl, max_len, ALPHA, new=(d["k_nope_new"], d["k_pe_new"], d["v_new"]),
+                                  rope_table=tab)
+    torch.cuda.synchronize()
+    cos, sin = rope_cos_sin(max_len, **KIMI_K2_ROPE)
+    pos = np.asarray(lens, dtype=np.int64)[:, None] - 1
+    pages_kp = to_host_bits(d["k_pe_pages"])
+    stored = np.stack([pages_kp[table[b, (L - 1) // bs], (L - 1) % bs] for b, L in enumerate(lens)])[:, None, None]
+    _check_rotation(to_f64(stored), x["k_pe_new"], apply_rope(to_f64(x["k_pe_new"]), pos, cos, sin), "new key")
+    q_rot = apply_rope(to_f64(x["q_pe"]), pos, cos, sin)
+    ref, _ = mla_decode_paged(x["q_nope"], q_rot, x["k_nope_pages"], x["k_pe_pages"], x["v_pages"], table,
+                              np.asarray(lens), ALPHA, new=(x["k_nope_new"], stored, x["v_new"]))
+    assert_parity(to_host_f64(out), ref, "fused rope paged append")
