@@ -118,19 +118,17 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 
   const int nwg = gridDim.x;
   const int wg = blockIdx.x;
-  int bh, split;
-  if (a.interleave) {
-    // Variable lengths: (b, h) pairs go round-robin over the XCDs, so every
-    // XCD gets H/8 heads of every sequence and the same share of keys; the
-    // splits of one (b, h) still share an XCD.
-    const int k = wg >> 3;
-    bh = (wg & 7) + 8 * (k / a.nsplit);
-    split = k % a.nsplit;
-  } else {
-    const int logical = (nwg % 8 == 0) ? (wg % 8) * (nwg / 8) + wg / 8 : wg;
-    bh = logical / a.nsplit;
-    split = logical % a.nsplit;
-  }
+  // Variable lengths (a.interleave): (b, h) pairs go round-robin over the
+  // XCDs, so every XCD gets H/8 heads of every sequence and the same share of
+  // keys; the splits of one (b, h) still share an XCD. Otherwise each XCD
+  // takes a contiguous run of (b, h, split). Both mappings are formed and one
+  // selected, without a branch, so the argument loads issue as one batch.
+  const int k8 = wg >> 3;
+  const int logical = (nwg % 8 == 0) ? (wg % 8) * (nwg / 8) + wg / 8 : wg;
+  const int src = a.interleave ? k8 : logical;
+  const int q = src / a.nsplit;
+  const int bh = a.interleave ? (wg & 7) + 8 * q : q;
+  const int split = src - q * a.nsplit;
   const int b = bh / a.H;
   const int h = bh - b * a.H;
 
@@ -177,10 +175,16 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     return table ? a.k_pe + (block_of(key) * bsz + key % bsz) * DR + 4 * cl : kp_g + key * DR;
   };
 
+  // The query: 8 non-rotary dims and 4 rotary dims per lane, as bf16 words.
+  // The plain kernels widen them to fp32 inside the loop, after each trip's
+  // key loads are issued (an empty asm keeps the compiler from hoisting the
+  // widening, and with it the wait for the query, in front of the first key
+  // loads); the query's latency then overlaps the keys' instead of preceding
+  // it. The rotary kernel widens and rotates them here.
+  const u32x4 qw = *reinterpret_cast<const u32x4*>(a.q_nope + (int64_t)bh * DN + 8 * cl);
+  const u32x2 qpw = *reinterpret_cast<const u32x2*>(a.q_pe + (int64_t)bh * DR + 4 * cl);
   float qn[8], qp[4];
-  {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(a.q_nope + (int64_t)bh * DN + 8 * cl);
-    const u32x2 wp = *reinterpret_cast<const u32x2*>(a.q_pe + (int64_t)bh * DR + 4 * cl);
+  auto widen_q = [&](const u32x4& w, const u32x2& wp) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       qn[2 * e] = lo_bf16(w[e]);
@@ -191,7 +195,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
       qp[2 * e] = lo_bf16(wp[e]);
       qp[2 * e + 1] = hi_bf16(wp[e]);
     }
-  }
+  };
+  if (ROPE) widen_q(qw, qpw);
   // Fused rotary prologue (the rotary instantiation): the new token's query, and its
   // key when the call appends it, turn at position S-1, the last key of the
   // sequence. Lane cl holds rotary dims 4cl..4cl+3, i.e. whole pairs 2cl and
@@ -311,6 +316,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
         if (!ok[u]) vv[u] = u32x4{0, 0, 0, 0};
       }
     }
+    if (!ROPE) {
+      u32x4 w = qw;
+      u32x2 wp = qpw;
+      asm volatile("" : "+v"(w), "+v"(wp));
+      widen_q(w, wp);
+    }
     float t[KEYS_PER_LANE];
 #pragma unroll
     for (int u = 0; u < KEYS_PER_LANE; ++u) {
@@ -354,6 +365,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   // the new rows in quarter-wave 0 of wave 0, which also writes the rows into
   // the cache (the rotary row by head 0 only: it is shared by the heads, and
   // every head reads key S-1 from the new rows, so no one reads that slot).
+  if (!ROPE) widen_q(qw, qpw);  // the loop may have run no trip
   if (owns_new && wave == 0 && qq == 0) {
     const u32x4 kw = *reinterpret_cast<const u32x4*>(a.kn_new + (int64_t)bh * DN + 8 * cl);
     u32x2 pw = *reinterpret_cast<const u32x2*>(a.kp_new + (int64_t)b * DR + 4 * cl);
