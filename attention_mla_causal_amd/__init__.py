@@ -53,6 +53,7 @@ SIGNATURES = {
     "mla_rope_table": (ctypes.c_int, [_VP, _I32, ctypes.c_double, ctypes.c_double, _I32, ctypes.c_double,
                                       ctypes.c_double, _VP]),
     "mla_rope_apply": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP]),
+    "mla_rope_apply_qk": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP]),
     "mla_attn_decode_rope": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _SZ, _I32, _I32, _I32,
                                             _I32, _F32, _VP]),
     "mla_attn_decode_paged_rope": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32,
@@ -573,10 +574,34 @@ def mla_rope_apply(x, table, past_len: int = 0, past_lens=None):
     return x
 
 
+def mla_rope_apply_qk(q_pe, k_pe, table, past_len: int = 0, past_lens=None):
+    """Rotate q_pe [B, H, T, 64] and the new keys' k_pe [B, 1, T, 64] in place,
+    in one launch (positions as mla_rope_apply). Returns (q_pe, k_pe)."""
+    import torch
+
+    _check_tensor(q_pe, "q_pe")
+    _check_tensor(k_pe, "k_pe")
+    B, H, T, D = q_pe.shape
+    if D != QK_ROPE_HEAD_DIM or tuple(k_pe.shape) != (B, 1, T, QK_ROPE_HEAD_DIM) or k_pe.device != q_pe.device:
+        raise ValueError(f"q_pe {tuple(q_pe.shape)} and k_pe {tuple(k_pe.shape)} must be [B, H, T, 64] and "
+                         "[B, 1, T, 64] on one device")
+    if not (isinstance(table, torch.Tensor) and table.dtype == torch.float32 and table.is_contiguous()
+            and table.dim() == 3 and tuple(table.shape[1:]) == (32, 2) and table.device == q_pe.device):
+        raise ValueError(f"table must be a contiguous float32 [max_pos, 32, 2] tensor on {q_pe.device}")
+    if past_lens is not None:
+        _check_int32(past_lens, "past_lens", (B,), q_pe.device)
+    st = _lib.mla_rope_apply_qk(q_pe.data_ptr(), k_pe.data_ptr(),
+                                past_lens.data_ptr() if past_lens is not None else None, table.data_ptr(),
+                                int(table.shape[0]), B, H, T, int(past_len), _stream_handle(q_pe.device))
+    _raise_for(st, "mla_rope_apply_qk")
+    return q_pe, k_pe
+
+
 __all__ = [
     "mla_rope_table",
     "mla_rope_table_bytes",
     "mla_rope_apply",
+    "mla_rope_apply_qk",
     "mla_attn_prefill_ws",
     "mla_attn_prefill_workspace_bytes",
     "mla_attn_decode_paged",

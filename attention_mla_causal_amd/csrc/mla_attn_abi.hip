@@ -493,15 +493,45 @@ mla_status mla_rope_apply(void* x, const int32_t* past_lens, const void* table, 
   if (r.empty) return MLA_OK;
   mla::RopeApplyArgs a;
   a.x = static_cast<uint16_t*>(x);
+  a.x2 = nullptr;
   a.table = static_cast<const float*>(table);
   a.past_lens = past_lens;
   a.rows = (int64_t)B * R * T;
+  a.rows1 = a.rows;
   a.R = R;
   a.T = T;
   a.past_len = past_len;
   a.max_pos = max_pos;
   const hipError_t e = mla::launch_rope_apply(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error("mla_rope_apply", e);
+  return MLA_OK;
+}
+
+mla_status mla_rope_apply_qk(void* q_pe, void* k_pe, const int32_t* past_lens, const void* table,
+                             int32_t max_pos, int32_t B, int32_t H, int32_t T, int32_t past_len,
+                             void* stream) {
+  // the limits of one tensor of B * (H + 1) * T rows; then the key rows' own pointer
+  mla::CheckResult r =
+      mla::check_rope_apply(q_pe, past_lens, table, max_pos, B, (int64_t)H + 1, T, past_len);
+  if (r.status == MLA_OK && !r.empty) {
+    if (k_pe == nullptr) r = mla::fail(MLA_ERR_NULL, "k_pe is NULL");
+    else if (mla::misaligned(k_pe)) r = mla::fail(MLA_ERR_ALIGN, "k_pe is not 16-byte aligned");
+  }
+  if (r.status != MLA_OK) return report("mla_rope_apply_qk", r);
+  if (r.empty) return MLA_OK;
+  mla::RopeApplyArgs a;
+  a.x = static_cast<uint16_t*>(q_pe);
+  a.x2 = static_cast<uint16_t*>(k_pe);
+  a.table = static_cast<const float*>(table);
+  a.past_lens = past_lens;
+  a.rows1 = (int64_t)B * H * T;
+  a.rows = a.rows1 + (int64_t)B * T;
+  a.R = H;
+  a.T = T;
+  a.past_len = past_len;
+  a.max_pos = max_pos;
+  const hipError_t e = mla::launch_rope_apply(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error("mla_rope_apply_qk", e);
   return MLA_OK;
 }
 

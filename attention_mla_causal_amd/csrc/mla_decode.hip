@@ -176,11 +176,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   };
 
   // The query: 8 non-rotary dims and 4 rotary dims per lane, as bf16 words.
-  // The plain kernels widen them to fp32 inside the loop, after each trip's
+  // The plain kernel widens them to fp32 inside the loop, after each trip's
   // key loads are issued (an empty asm keeps the compiler from hoisting the
   // widening, and with it the wait for the query, in front of the first key
   // loads); the query's latency then overlaps the keys' instead of preceding
-  // it. The rotary kernel widens and rotates them here.
+  // it. The masked kernel widens them here (in its loop the wait would also
+  // cover the next trip's mask bytes, fetched ahead), and so does the rotary
+  // kernel, which rotates them here too.
+  constexpr bool kLateQuery = !MASKED && !ROPE;
   const u32x4 qw = *reinterpret_cast<const u32x4*>(a.q_nope + (int64_t)bh * DN + 8 * cl);
   const u32x2 qpw = *reinterpret_cast<const u32x2*>(a.q_pe + (int64_t)bh * DR + 4 * cl);
   float qn[8], qp[4];
@@ -196,7 +199,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
       qp[2 * e + 1] = hi_bf16(wp[e]);
     }
   };
-  if (ROPE) widen_q(qw, qpw);
+  if (!kLateQuery) widen_q(qw, qpw);
   // Fused rotary prologue (the rotary instantiation): the new token's query, and its
   // key when the call appends it, turn at position S-1, the last key of the
   // sequence. Lane cl holds rotary dims 4cl..4cl+3, i.e. whole pairs 2cl and
@@ -316,7 +319,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
         if (!ok[u]) vv[u] = u32x4{0, 0, 0, 0};
       }
     }
-    if (!ROPE) {
+    if (kLateQuery) {
       u32x4 w = qw;
       u32x2 wp = qpw;
       asm volatile("" : "+v"(w), "+v"(wp));
@@ -365,7 +368,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   // the new rows in quarter-wave 0 of wave 0, which also writes the rows into
   // the cache (the rotary row by head 0 only: it is shared by the heads, and
   // every head reads key S-1 from the new rows, so no one reads that slot).
-  if (!ROPE) widen_q(qw, qpw);  // the loop may have run no trip
+  if (kLateQuery) widen_q(qw, qpw);  // the loop may have run no trip
   if (owns_new && wave == 0 && qq == 0) {
     const u32x4 kw = *reinterpret_cast<const u32x4*>(a.kn_new + (int64_t)bh * DN + 8 * cl);
     u32x2 pw = *reinterpret_cast<const u32x2*>(a.kp_new + (int64_t)b * DR + 4 * cl);

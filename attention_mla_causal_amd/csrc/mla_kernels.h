@@ -99,9 +99,11 @@ struct RopeTableArgs {
 
 struct RopeApplyArgs {
   uint16_t* x;             // [B, R, T, 64] bf16, rotated in place
+  uint16_t* x2;            // [B, 1, T, 64] bf16 rotated in the same launch (rows past rows1), or null
   const float* table;      // [max_pos, 32] (cos, sin) pairs
   const int32_t* past_lens;  // [B] or null: past_len for every sequence
-  int64_t rows;            // B * R * T
+  int64_t rows;            // B * R * T, plus B * T with x2
+  int64_t rows1;           // B * R * T: rows of x
   int32_t R, T, past_len, max_pos;
 };
 

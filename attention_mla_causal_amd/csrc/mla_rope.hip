@@ -13,7 +13,9 @@
 //    the angle and its cosine and sine are computed in fp64 and stored as
 //    fp32, 256 bytes per position. Built once per model and context length.
 //  * mla_rope_apply_kernel: rotates bf16 rows [B, R, T, 64] in place (R = H for
-//    q_pe, 1 for the shared k_pe). A quarter-wave covers one 128-byte row:
+//    q_pe, 1 for the shared k_pe), optionally followed in the same launch by
+//    the new keys' rows [B, 1, T, 64] (the pages rotate the query and the key
+//    in one call). A quarter-wave covers one 128-byte row:
 //    lane l holds dims 4l..4l+3 (pairs 2l and 2l+1) and loads the matching
 //    16 bytes of the table row, so every pair turns inside one lane's
 //    registers (fp32 arithmetic, round-to-nearest-even bf16 result). Each
@@ -68,15 +70,20 @@ __global__ __launch_bounds__(kThreads) void mla_rope_apply_kernel(RopeApplyArgs 
   const int64_t row0 = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
   u32x2 xv[kRowsPerThread];
   f32x4 cs[kRowsPerThread];
+  uint16_t* ptr[kRowsPerThread];
 #pragma unroll
   for (int u = 0; u < kRowsPerThread; ++u) {
     const int64_t row = row0 + (int64_t)u * (kThreads / 16);
     if (row >= a.rows) continue;
-    const int64_t t = row % a.T;
-    const int64_t b = row / ((int64_t)a.R * a.T);
+    // rows of x first ([B, R, T]), then those of x2 ([B, 1, T])
+    const bool second = row >= a.rows1;
+    const int64_t r = second ? row - a.rows1 : row;
+    const int64_t t = r % a.T;
+    const int64_t b = r / ((second ? 1 : (int64_t)a.R) * a.T);
     int64_t pos = (a.past_lens != nullptr ? (int64_t)a.past_lens[b] : (int64_t)a.past_len) + t;
     pos = pos < 0 ? 0 : (pos >= a.max_pos ? a.max_pos - 1 : pos);  // never leave the table
-    xv[u] = *reinterpret_cast<const u32x2*>(a.x + row * 64 + 4 * lane16);
+    ptr[u] = (second ? a.x2 : a.x) + r * 64 + 4 * lane16;
+    xv[u] = *reinterpret_cast<const u32x2*>(ptr[u]);
     cs[u] = *reinterpret_cast<const f32x4*>(a.table + pos * (2 * kPairs) + 4 * lane16);
   }
 #pragma unroll
@@ -89,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void mla_rope_apply_kernel(RopeApplyArgs 
     u32x2 w;
     w[0] = to_bf16(x0 * c0 - y0 * s0) | (to_bf16(x0 * s0 + y0 * c0) << 16);
     w[1] = to_bf16(x1 * c1 - y1 * s1) | (to_bf16(x1 * s1 + y1 * c1) << 16);
-    *reinterpret_cast<u32x2*>(a.x + row * 64 + 4 * lane16) = w;
+    *reinterpret_cast<u32x2*>(ptr[u]) = w;
   }
 }
 

@@ -48,6 +48,7 @@ KERNEL_SOURCES = {
     "mla_decode_kernel": "attention_mla_causal_amd/csrc/mla_decode.hip",
     "mla_prefill_kernel": "attention_mla_causal_amd/csrc/mla_prefill.hip",
     "mla_attn_decode_latent": "attention_mla_causal_amd/csrc/mla_latent.hip",  # its four launches
+    "mla_rope_apply_kernel": "attention_mla_causal_amd/csrc/mla_rope.hip",
 }
 
 
@@ -213,11 +214,14 @@ def time_eager(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
 
 
-def run_decode(wl, steps, warmup, seed=0, graph=True, copies=None):
+def run_decode(wl, steps, warmup, seed=0, graph=True, copies=None, rope=False):
+    """rope: the query's rotary part is rotated inside the kernel
+    (mla_attn_decode_rope, the released configuration's YaRN table); the
+    algorithmic bytes add one 256-byte table row per sequence."""
     import torch
     import attention_mla_causal_amd as mla
     dev = torch.device("cuda:0")
-    nbytes = decode_bytes(wl)
+    nbytes = decode_bytes(wl) + (wl.B * 256 if rope else 0)
     if copies is None:
         # enough distinct inputs that the rotation cannot live in the Infinity Cache
         copies = 1 if nbytes >= 2 * CACHE_BYTES else min(64, -(-2 * CACHE_BYTES // nbytes) + 1)
@@ -231,31 +235,95 @@ def run_decode(wl, steps, warmup, seed=0, graph=True, copies=None):
     out = torch.empty((wl.B, wl.H, 1, 128), dtype=torch.bfloat16, device=dev)
     need = mla.mla_attn_decode_workspace_bytes(wl.B, wl.H, wl.S)
     ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+    table = mla.mla_rope_table(wl.S, device=dev) if rope else None
 
     def step(i):
         d = sets[i % copies]
         mla.mla_attn_decode(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], wl.past_len,
-                            wl.softmax_scale, out=out, workspace=ws)
+                            wl.softmax_scale, out=out, workspace=ws, rope_table=table)
 
     if graph:
         ms, wall_ms = time_graph(step, steps, warmup)
     else:
         ms, wall_ms = time_eager(step, steps, warmup)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    kernel = "mla_decode_kernel"
+    kernel = "mla_decode_rope_kernel" if rope else "mla_decode_kernel"
+    name = wl.name + ("_rope" if rope else "")
     res = {
-        "workload": wl.name, "B": wl.B, "H": wl.H, "T": 1, "past_len": wl.past_len, "S": wl.S,
+        "workload": name, "B": wl.B, "H": wl.H, "T": 1, "past_len": wl.past_len, "S": wl.S,
         "std": wl.std, "inputs": recipe, "input_copies": copies, "steps": steps,
         "timing": "hip_graph" if graph else "eager",
         "ms_per_step": ms, "wall_ms_per_step": wall_ms, "value": gbs, "unit": "GB/s",
         "algorithmic_bytes": nbytes,
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(kernel, wl.name)},
+                     "traffic": measured_traffic("mla_decode_kernel", name)},
     }
     del sets
     torch.cuda.empty_cache()
     return res
+
+
+def rope_apply_bytes(wl) -> int:
+    """Rows of the new tokens' q_pe (H per position) and k_pe (one per
+    position), each read and written once (128 bytes each way), plus one
+    256-byte table row per position."""
+    return (wl.H + 1) * wl.B * wl.T * 256 + wl.T * 256
+
+
+def run_rope_apply(wl, steps, warmup, seed=0, graph=True):
+    """The rotary prologue of a prefill step: q_pe [B, H, T, 64] and the new
+    keys' k_pe [B, 1, T, 64] rotated in place at past_len + t, in one launch."""
+    import torch
+    import attention_mla_causal_amd as mla
+    dev = torch.device("cuda:0")
+    nbytes = rope_apply_bytes(wl)
+    copies = min(64, -(-2 * CACHE_BYTES // nbytes) + 1)
+    log(f"[bench] rope prologue of {wl.name}: B={wl.B} H={wl.H} T={wl.T} P={wl.past_len} copies={copies}")
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    sets = [(torch.randn((wl.B, wl.H, wl.T, 64), generator=g, device=dev).to(torch.bfloat16),
+             torch.randn((wl.B, 1, wl.T, 64), generator=g, device=dev).to(torch.bfloat16)) for _ in range(copies)]
+    table = mla.mla_rope_table(wl.S, device=dev)
+
+    def step(i):
+        q, k = sets[i % copies]
+        mla.mla_rope_apply_qk(q, k, table, past_len=wl.past_len)
+
+    ms, wall_ms = (time_graph if graph else time_eager)(step, steps, warmup)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    name = "rope_" + wl.name
+    res = {"workload": name, "B": wl.B, "H": wl.H, "T": wl.T, "past_len": wl.past_len, "S": wl.S,
+           "inputs": "device", "input_copies": copies, "steps": steps,
+           "timing": "hip_graph" if graph else "eager", "ms_per_step": ms, "wall_ms_per_step": wall_ms,
+           "value": gbs, "unit": "GB/s", "algorithmic_bytes": nbytes, "launches_per_step": 1,
+           "roofline": {"bound": "hbm", "kernel": "mla_rope_apply_kernel", "achieved": gbs,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                        "traffic": measured_traffic("mla_rope_apply_kernel", name)}}
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline_rope_apply(wl, seconds, seed=0):
+    """The fp64 rotation oracle over the same rows (table built once, not timed)."""
+    from oracle import KIMI_K2_ROPE, apply_rope, rope_cos_sin, rope_positions
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((wl.B, wl.H, wl.T, 64))
+    k = rng.standard_normal((wl.B, 1, wl.T, 64))
+    cos, sin = rope_cos_sin(wl.S, **KIMI_K2_ROPE)
+    pos = rope_positions(wl.B, wl.T, past_len=wl.past_len)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        apply_rope(q, pos, cos, sin)
+        apply_rope(k, pos, cos, sin)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": rope_apply_bytes(wl) * n / el / 1e9, "unit": "GB/s", "cores": blas_threads(),
+            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"the whole workload {n} times, {el:.1f} s"}
 
 
 def run_varlen(wl, steps, warmup, seed=0, graph=True):
@@ -645,7 +713,8 @@ def main():
     ap.add_argument("--workload", default="decode_p1000",
                     choices=sorted(WORKLOADS) + sorted(SHARD_WORKLOADS) + sorted(LATENT_WORKLOADS)
                     + sorted(VARLEN_WORKLOADS)
-                    + sorted(PAGED_WORKLOADS) + sorted(VARLEN_PREFILL_WORKLOADS) + sorted(MASKED_WORKLOADS))
+                    + sorted(PAGED_WORKLOADS) + sorted(VARLEN_PREFILL_WORKLOADS) + sorted(MASKED_WORKLOADS)
+                    + ["decode_p1000_rope", "rope_chunked_prefill"])
     ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -680,7 +749,15 @@ def main():
         sys.exit(2)
 
     torch.cuda.synchronize()
-    if args.workload in MASKED_WORKLOADS:
+    if args.workload == "decode_p1000_rope":
+        wl = WORKLOADS["decode_p1000"]
+        head = run_decode(wl, args.steps, args.warmup, graph=not args.eager, rope=True)
+        cpu = None
+    elif args.workload == "rope_chunked_prefill":
+        wl = WORKLOADS["chunked_prefill"]
+        head = run_rope_apply(wl, args.steps, args.warmup, graph=not args.eager)
+        cpu = None
+    elif args.workload in MASKED_WORKLOADS:
         wl = MASKED_WORKLOADS[args.workload]
         head = run_masked(wl, args.steps, args.warmup, graph=not args.eager)
         cpu = None
@@ -746,6 +823,13 @@ def main():
                 workloads[name] = run_masked(w, args.extra_steps, 2)
                 if not args.no_cpu:
                     workloads[name]["cpu_baseline"] = cpu_baseline_masked(w, min(args.cpu_seconds, 5.0))
+        # the rotary prologue: fused into the short decode, and on its own over
+        # the chunked prefill's new tokens
+        workloads["decode_p1000_rope"] = run_decode(WORKLOADS["decode_p1000"], 200, 20, rope=True)
+        workloads["rope_chunked_prefill"] = run_rope_apply(WORKLOADS["chunked_prefill"], 200, 20)
+        if not args.no_cpu:
+            workloads["rope_chunked_prefill"]["cpu_baseline"] = cpu_baseline_rope_apply(
+                WORKLOADS["chunked_prefill"], min(args.cpu_seconds, 3.0))
         for name, w in LATENT_WORKLOADS.items():
             if name == wl.name:
                 continue

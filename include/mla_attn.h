@@ -410,6 +410,17 @@ mla_status mla_rope_apply(void* x, const int32_t* past_lens, const void* table, 
                           int32_t B, int32_t R, int32_t T, int32_t past_len, void* stream);
 
 /*
+ * The pages' one call for both rotary parts: q_pe [B, H, T, 64] and the new
+ * keys' k_pe [B, 1, T, 64] (both bf16, 16-byte aligned) rotated in place, in
+ * one launch, at the positions mla_rope_apply uses. Errors as for
+ * mla_rope_apply (the row limit counts B * (H + 1) * T rows); B == 0 or
+ * T == 0 is a no-op (with H == 0 only the key rows turn).
+ */
+mla_status mla_rope_apply_qk(void* q_pe, void* k_pe, const int32_t* past_lens, const void* table,
+                             int32_t max_pos, int32_t B, int32_t H, int32_t T, int32_t past_len,
+                             void* stream);
+
+/*
  * mla_attn_decode with the rotary prologue fused in: q_pe is the new query's
  * rotary part before rotation, and the kernel turns it at position past_len
  * (the new token's, the last key) with rope_table [rope_max_pos, 32, 2]

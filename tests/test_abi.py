@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
         "mla_attn_prefill_ws", "mla_attn_prefill_workspace_bytes",
         "mla_attn_prefill_varlen",
         "mla_attn_prefill_masked", "mla_attn_decode_masked",
-        "mla_rope_table", "mla_rope_table_bytes", "mla_rope_apply",
+        "mla_rope_table", "mla_rope_table_bytes", "mla_rope_apply", "mla_rope_apply_qk",
         "mla_attn_decode_rope", "mla_attn_decode_paged_rope",
         "mla_last_error", "mla_status_string"])
 
@@ -313,6 +313,11 @@ def test_rope_errors(lib):
     assert lib.mla_rope_apply(None, None, AL, 16, 1, 1, 1, 0, None) == 1
     assert lib.mla_rope_apply(MIS, None, AL, 16, 1, 1, 1, 0, None) == 3
     assert lib.mla_rope_apply(AL, ctypes.c_void_p(0x100002), AL, 16, 1, 1, 1, 0, None) == 3
+    assert lib.mla_rope_apply_qk(AL, None, None, AL, 4096, 1, 64, 8, 0, None) == 1           # k_pe NULL
+    assert lib.mla_rope_apply_qk(AL, MIS, None, AL, 4096, 1, 64, 8, 0, None) == 3
+    assert lib.mla_rope_apply_qk(AL, AL, None, AL, 4096, 1, 64, 8, 4089, None) == 2         # past the table
+    assert lib.mla_rope_apply_qk(None, None, None, None, 0, 1, 64, 0, 0, None) == 0         # T == 0: no-op
+    assert lib.mla_rope_apply_qk(None, None, None, AL, 16, 1, 0, 8, 0, None) == 1           # H == 0: keys still turn
     # fused prologue in decode: the table must cover the new token's position
     ok = [AL] * 5
     need = lib.mla_attn_decode_workspace_bytes(1, 64, 1001)

@@ -249,3 +249,26 @@ def test_fused_prologue_paged_append():
     ref, _ = mla_decode_paged(x["q_nope"], q_rot, x["k_nope_pages"], x["k_pe_pages"], x["v_pages"], table,
                               np.asarray(lens), ALPHA, new=(x["k_nope_new"], stored, x["v_new"]))
     assert_parity(to_host_f64(out), ref, "fused rope paged append")
+
+
+@pytest.mark.parametrize("per_seq", [False, True])
+def test_apply_qk_in_one_launch_equals_two_calls(per_seq):
+    """mla_rope_apply_qk (the query's and the new keys' rotary parts in one
+    launch) gives the same bits as two mla_rope_apply calls."""
+    import torch
+    B, H, T, P = 3, 16, 45, 70
+    log(f"case rope apply qk B={B} H={H} T={T} P={P} per_seq={per_seq}")
+    x = random_inputs(B, H, T, P, seed=60)
+    kp_new = np.ascontiguousarray(x["k_pe"][:, :, P:])
+    tab = _gpu_table(400, KIMI_K2_ROPE)
+    lens = torch.as_tensor(np.array([0, 200, 33], dtype=np.int32), device="cuda") if per_seq else None
+    m = _lib()
+    q1, k1 = to_device(x["q_pe"]), to_device(kp_new)
+    m.mla_rope_apply_qk(q1, k1, tab, past_len=P, past_lens=lens)
+    q2, k2 = to_device(x["q_pe"]), to_device(kp_new)
+    m.mla_rope_apply(q2, tab, past_len=P, past_lens=lens)
+    m.mla_rope_apply(k2, tab, past_len=P, past_lens=lens)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(q1), to_host_bits(q2))
+    assert np.array_equal(to_host_bits(k1), to_host_bits(k2))
+    assert not np.array_equal(to_host_bits(k1), kp_new)                 # the keys did turn
