@@ -511,8 +511,9 @@ mla_status mla_rope_apply_qk(void* q_pe, void* k_pe, const int32_t* past_lens, c
                              int32_t max_pos, int32_t B, int32_t H, int32_t T, int32_t past_len,
                              void* stream) {
   // the limits of one tensor of B * (H + 1) * T rows; then the key rows' own pointer
-  mla::CheckResult r =
-      mla::check_rope_apply(q_pe, past_lens, table, max_pos, B, (int64_t)H + 1, T, past_len);
+  // (with H == 0 the query has no rows and may be NULL)
+  mla::CheckResult r = mla::check_rope_apply(H > 0 ? q_pe : k_pe, past_lens, table, max_pos, B,
+                                             (int64_t)H + 1, T, past_len);
   if (r.status == MLA_OK && !r.empty) {
     if (k_pe == nullptr) r = mla::fail(MLA_ERR_NULL, "k_pe is NULL");
     else if (mla::misaligned(k_pe)) r = mla::fail(MLA_ERR_ALIGN, "k_pe is not 16-byte aligned");

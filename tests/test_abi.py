@@ -318,6 +318,8 @@ def test_rope_errors(lib):
     assert lib.mla_rope_apply_qk(AL, AL, None, AL, 4096, 1, 64, 8, 4089, None) == 2         # past the table
     assert lib.mla_rope_apply_qk(None, None, None, None, 0, 1, 64, 0, 0, None) == 0         # T == 0: no-op
     assert lib.mla_rope_apply_qk(None, None, None, AL, 16, 1, 0, 8, 0, None) == 1           # H == 0: keys still turn
+    assert "x is NULL" in lib.mla_last_error().decode()
+    assert lib.mla_rope_apply_qk(None, MIS, None, AL, 16, 1, 0, 8, 0, None) == 3            # ... and are checked
     # fused prologue in decode: the table must cover the new token's position
     ok = [AL] * 5
     need = lib.mla_attn_decode_workspace_bytes(1, 64, 1001)
