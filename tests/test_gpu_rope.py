@@ -272,3 +272,58 @@ def test_apply_qk_in_one_launch_equals_two_calls(per_seq):
     assert np.array_equal(to_host_bits(q1), to_host_bits(q2))
     assert np.array_equal(to_host_bits(k1), to_host_bits(k2))
     assert not np.array_equal(to_host_bits(k1), kp_new)                 # the keys did turn
+
+
+def test_fused_prologue_paged_append_graph_loop():
+    """A serving loop: one paged decode step with the rotary prologue fused and
+    the new token appended, captured once and replayed with the lengths
+    growing by one and new token rows each time. Every replay gives the same
+    bits (output and pages) as eager calls on a twin cache."""
+    import torch
+    from seeded_inputs import paged_host_inputs, paged_layout
+    lens0, H, bs, steps = [300, 45, 1000], 16, 32, 4
+    cap = [L + steps for L in lens0]
+    table_np, N = paged_layout(cap, bs, seed=9, spare=1)
+    x = paged_host_inputs(len(lens0), H, N, bs, seed=9)
+    max_len = max(cap)
+    log(f"case rope fused paged graph loop lens0={lens0} H={H} bs={bs} steps={steps}")
+    m = _lib()
+    tab = _gpu_table(max_len, KIMI_K2_ROPE)
+    tb = torch.as_tensor(table_np, device="cuda")
+    pages_g = {k: to_device(x[k]) for k in ("k_nope_pages", "k_pe_pages", "v_pages")}
+    pages_e = {k: v.clone() for k, v in pages_g.items()}
+    inp = {k: to_device(x[k]) for k in ("q_nope", "q_pe", "k_nope_new", "k_pe_new", "v_new")}
+    sl = torch.as_tensor(np.asarray(lens0, dtype=np.int32), device="cuda")
+    out_g = torch.empty((len(lens0), H, 1, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(m.mla_attn_decode_paged_workspace_bytes(len(lens0), H, max_len), 16),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(pages, out):
+        return m.mla_attn_decode_paged(inp["q_nope"], inp["q_pe"], pages["k_nope_pages"], pages["k_pe_pages"],
+                                       pages["v_pages"], tb, sl, max_len, ALPHA,
+                                       new=(inp["k_nope_new"], inp["k_pe_new"], inp["v_new"]), out=out,
+                                       workspace=ws, rope_table=tab)
+
+    scratch = {k: v.clone() for k, v in pages_g.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(scratch, out_g)                         # warm-up outside the capture, on a scratch cache
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(pages_g, out_g)
+    rng = np.random.default_rng(10)
+    for r in range(steps):
+        sl.copy_(torch.as_tensor(np.asarray(lens0, dtype=np.int32) + r + 1, device="cuda"))
+        for k in inp:
+            inp[k].copy_(torch.as_tensor(rng.standard_normal(tuple(inp[k].shape)), device="cuda").to(torch.bfloat16))
+        g.replay()
+        torch.cuda.synchronize()
+        out_e = step(pages_e, None)
+        torch.cuda.synchronize()
+        log(f"  replay {r}: lens={sl.tolist()}")
+        assert np.array_equal(to_host_bits(out_g), to_host_bits(out_e)), f"output, replay {r}"
+        for k in pages_g:
+            assert np.array_equal(to_host_bits(pages_g[k]), to_host_bits(pages_e[k])), f"{k}, replay {r}"
