@@ -2,8 +2,9 @@
 
 A thin ctypes binding over libmla_attn.so (the C ABI in include/mla_attn.h).
 The functions below only check and marshal arguments: torch supplies device
-memory and the current HIP stream; every step of the attention runs in the
-library's HIP kernels. There is no fallback path: if the library has not been
+memory and the current HIP stream; every step of the attention, and of the
+rotary prologue (the YaRN table, the rotation of new rows, or the rotation
+fused into the decode), runs in the library's HIP kernels. There is no fallback path: if the library has not been
 built (``python attention_mla_causal_amd/build.py``) importing this package
 raises.
 """

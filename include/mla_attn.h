@@ -24,6 +24,8 @@
  *  - All tensors are bf16, contiguous, row-major, in device memory owned by
  *    the caller. Shapes: q_nope [B,H,T,128], q_pe [B,H,T,64],
  *    k_nope [B,H,S,128], k_pe [B,1,S,64], v [B,H,S,128], out [B,H,T,128].
+ *    (Exceptions, stated where they apply: lengths and block tables are
+ *    int32, masks are bytes, the rotary table is fp32.)
  *  - Every non-empty tensor pointer must be 16-byte aligned.
  *  - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
  *    work on it and return without synchronising; ordering against other
@@ -31,7 +33,8 @@
  *  - All argument checks run on the host before any HIP call; a failing
  *    call returns a status and enqueues nothing. No exceptions cross the ABI.
  *    mla_last_error() gives a thread-local description of the last failure.
- *  - B == 0, H == 0 or T == 0 is a valid empty call: it returns MLA_OK.
+ *  - B == 0, H == 0 or T == 0 is a valid empty call: it returns MLA_OK
+ *    (the rotary calls state their own empty cases).
  *  - softmax_scale is taken as a 32-bit float and must be finite and > 0
  *    (the model's scale is an inverse square root, always positive).
  */
