@@ -57,6 +57,8 @@ SIGNATURES = {
     "mla_rope_apply_qk": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP]),
     "mla_attn_decode_rope": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _SZ, _I32, _I32, _I32,
                                             _I32, _F32, _VP]),
+    "mla_attn_decode_varlen_rope": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _SZ, _I32,
+                                                   _I32, _I32, _I32, _F32, _VP]),
     "mla_attn_decode_paged_rope": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32,
                                                   _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -346,14 +348,17 @@ def mla_attn_decode_varlen_workspace_bytes(B: int, H: int, max_seq_len: int) -> 
 
 
 def mla_attn_decode_varlen(q_nope, q_pe, k_nope_cache, k_pe_cache, v_cache, seq_lens,
-                           max_seq_len: int, softmax_scale: float, out=None, workspace=None):
+                           max_seq_len: int, softmax_scale: float, out=None, workspace=None,
+                           rope_table=None):
     """Decode over a preallocated, right-padded cache with a length per sequence.
 
     q_nope [B,H,1,128], q_pe [B,H,1,64]; k_nope_cache [B,H,L,128], k_pe_cache
     [B,1,L,64], v_cache [B,H,L,128] with L the cache length; seq_lens an int32
     GPU tensor [B]: sequence b attends over cache rows [0, seq_lens[b]),
     each length clamped on the device to [0, max_seq_len] (max_seq_len <= L).
-    A sequence of length 0 gives a zero row. Returns out [B,H,1,128] bf16.
+    A sequence of length 0 gives a zero row. rope_table (from mla_rope_table):
+    q_pe is taken before rotation and turned at position seq_lens[b]-1 in the
+    kernel (mla_attn_decode_varlen_rope). Returns out [B,H,1,128] bf16.
     """
     import torch
 
@@ -376,6 +381,15 @@ def mla_attn_decode_varlen(q_nope, q_pe, k_nope_cache, k_pe_cache, v_cache, seq_
     if not (workspace.is_cuda and workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous GPU tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
+    if rope_table is not None:
+        _check_rope_table(rope_table, q_nope.device)
+        st = _lib.mla_attn_decode_varlen_rope(
+            q_nope.data_ptr(), q_pe.data_ptr(), k_nope_cache.data_ptr(), k_pe_cache.data_ptr(),
+            v_cache.data_ptr(), seq_lens.data_ptr(), rope_table.data_ptr(), int(rope_table.shape[0]),
+            out.data_ptr(), workspace.data_ptr(), ws_bytes, B, H, L, int(max_seq_len), float(softmax_scale),
+            _stream_handle(q_nope.device))
+        _raise_for(st, "mla_attn_decode_varlen_rope")
+        return out
     st = _lib.mla_attn_decode_varlen(
         q_nope.data_ptr(), q_pe.data_ptr(), k_nope_cache.data_ptr(), k_pe_cache.data_ptr(),
         v_cache.data_ptr(), seq_lens.data_ptr(), out.data_ptr(), workspace.data_ptr(), ws_bytes,

@@ -356,6 +356,28 @@ mla_status mla_attn_decode_varlen(const void* q_nope, const void* q_pe, const vo
                             softmax_scale, stream);
 }
 
+mla_status mla_attn_decode_varlen_rope(const void* q_nope, const void* q_pe,
+                                       const void* k_nope_cache, const void* k_pe_cache,
+                                       const void* v_cache, const int32_t* seq_lens,
+                                       const void* rope_table, int32_t rope_max_pos, void* out,
+                                       void* workspace, size_t workspace_bytes, int32_t B,
+                                       int32_t H, int32_t cache_len, int32_t max_seq_len,
+                                       float softmax_scale, void* stream) {
+  mla::DecodePlan plan;
+  mla::CheckResult r = mla::check_decode_varlen(
+      q_nope, q_pe, k_nope_cache, k_pe_cache, v_cache, seq_lens, out, workspace, workspace_bytes,
+      B, H, cache_len, max_seq_len, softmax_scale, &plan);
+  if (r.status == MLA_OK && !r.empty) r = check_rope_arg(rope_table, rope_max_pos, max_seq_len);
+  if (r.status != MLA_OK) return report("mla_attn_decode_varlen_rope", r);
+  if (r.empty) return MLA_OK;
+  DecodeExtras x;
+  x.seq_lens = seq_lens;
+  x.rope_table = static_cast<const float*>(rope_table);
+  return launch_decode_call("mla_attn_decode_varlen_rope", q_nope, q_pe, k_nope_cache, k_pe_cache,
+                            v_cache, x, out, workspace, plan, B, H, max_seq_len, cache_len,
+                            softmax_scale, stream);
+}
+
 size_t mla_attn_decode_paged_workspace_bytes(int32_t B, int32_t H, int32_t max_seq_len) {
   return mla::plan_decode_varlen(B, H, max_seq_len).workspace_bytes;
 }

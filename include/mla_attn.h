@@ -440,6 +440,23 @@ mla_status mla_attn_decode_rope(const void* q_nope, const void* q_pe, const void
                                 int32_t past_len, float softmax_scale, void* stream);
 
 /*
+ * mla_attn_decode_varlen with the rotary prologue fused in: q_pe is the new
+ * query's rotary part before rotation; sequence b's query turns at position
+ * seq_lens[b] - 1 (its last key; lengths clamped on the device as for
+ * mla_attn_decode_varlen). The cache holds keys already rotated at their
+ * positions. rope_table as for mla_attn_decode_rope, covering positions up
+ * to max_seq_len - 1 (rope_max_pos >= max_seq_len, else MLA_ERR_SHAPE).
+ * Other errors as for mla_attn_decode_varlen.
+ */
+mla_status mla_attn_decode_varlen_rope(const void* q_nope, const void* q_pe,
+                                       const void* k_nope_cache, const void* k_pe_cache,
+                                       const void* v_cache, const int32_t* seq_lens,
+                                       const void* rope_table, int32_t rope_max_pos, void* out,
+                                       void* workspace, size_t workspace_bytes, int32_t B,
+                                       int32_t H, int32_t cache_len, int32_t max_seq_len,
+                                       float softmax_scale, void* stream);
+
+/*
  * mla_attn_decode_paged with the rotary prologue fused in: q_pe and, when the
  * call appends the new token, k_pe_new are rotary parts before rotation.
  * Sequence b's new token sits at position seq_lens[b] - 1 (clamped into the

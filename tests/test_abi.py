@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
         "mla_attn_prefill_varlen",
         "mla_attn_prefill_masked", "mla_attn_decode_masked",
         "mla_rope_table", "mla_rope_table_bytes", "mla_rope_apply", "mla_rope_apply_qk",
-        "mla_attn_decode_rope", "mla_attn_decode_paged_rope",
+        "mla_attn_decode_rope", "mla_attn_decode_paged_rope", "mla_attn_decode_varlen_rope",
         "mla_last_error", "mla_status_string"])
 
 
@@ -329,6 +329,10 @@ def test_rope_errors(lib):
     assert lib.mla_attn_decode_rope(*ok, MIS, 1001, AL, AL, need, 1, 64, 1001, 1000, SC, None) == 3
     assert lib.mla_attn_decode_rope(*ok, None, 0, AL, AL, need, 1, 64, 1001, 999, SC, None) == 2  # shape first
     assert lib.mla_attn_decode_rope(*ok, None, 0, None, None, 0, 0, 64, 1001, 1000, SC, None) == 0  # empty
+    vw = lib.mla_attn_decode_varlen_workspace_bytes(2, 8, 4096)
+    assert lib.mla_attn_decode_varlen_rope(*ok, AL, None, 4096, AL, AL, vw, 2, 8, 4096, 4096, SC, None) == 1
+    assert lib.mla_attn_decode_varlen_rope(*ok, AL, AL, 4000, AL, AL, vw, 2, 8, 4096, 4096, SC, None) == 2
+    assert "mla_attn_decode_varlen_rope" in lib.mla_last_error().decode()
     pw = lib.mla_attn_decode_paged_workspace_bytes(2, 8, 4096)
     args = [AL, AL, AL, AL, AL, AL, AL, None, None, None]
     assert lib.mla_attn_decode_paged_rope(*args, None, 4096, AL, AL, pw, 2, 8, 64, 64, 64, 4096, SC, None) == 1

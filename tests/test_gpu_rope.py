@@ -327,3 +327,31 @@ def test_fused_prologue_paged_append_graph_loop():
         assert np.array_equal(to_host_bits(out_g), to_host_bits(out_e)), f"output, replay {r}"
         for k in pages_g:
             assert np.array_equal(to_host_bits(pages_g[k]), to_host_bits(pages_e[k])), f"{k}, replay {r}"
+
+
+def test_fused_prologue_varlen_decode():
+    """mla_attn_decode_varlen with rope_table: sequence b's query turns at
+    position seq_lens[b] - 1 inside the kernel, over a right-padded cache of
+    keys rotated at their positions; lengths include 0 and 1."""
+    import torch
+    from oracle import mla_decode_varlen
+    B, H, cap = 5, 16, 700
+    lens = np.array([700, 1, 0, 333, 129], dtype=np.int32)
+    log(f"case rope fused varlen decode lens={lens.tolist()} H={H} cap={cap}")
+    x = random_inputs(B, H, 1, cap - 1, seed=70)
+    tab = _gpu_table(cap, KIMI_K2_ROPE)
+    d = {k: to_device(v) for k, v in x.items()}
+    m = _lib()
+    m.mla_rope_apply(d["k_pe"], tab, past_len=0)                  # cache rows rotated at their positions
+    k_rot_bits = to_host_bits(d["k_pe"])
+    out = m.mla_attn_decode_varlen(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"],
+                                   torch.as_tensor(lens, device="cuda"), cap, ALPHA, rope_table=tab)
+    torch.cuda.synchronize()
+    cos, sin = rope_cos_sin(cap, **KIMI_K2_ROPE)
+    pos = np.maximum(lens.astype(np.int64) - 1, 0)[:, None]
+    q_rot = apply_rope(to_f64(x["q_pe"]), pos, cos, sin)
+    ref = mla_decode_varlen(to_f64(x["q_nope"]), q_rot, to_f64(x["k_nope"]), to_f64(k_rot_bits), to_f64(x["v"]),
+                            lens, ALPHA)
+    got = to_host_f64(out)
+    assert not np.any(got[2])                                           # empty sequence: zero row
+    assert_parity(got, ref, "fused rope varlen decode")
