@@ -7,17 +7,12 @@ tests/test_oracle_masked.py, and runs every pin there: at least one must fail.
 The unchanged copy must pass them all.
 """
 
-import inspect
-import os
-import types
-
 import pytest
 
 import test_oracle_masked as pins
+from _mutants import load_copy, oracle_source, pin_failures, plant
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SOURCE = open(os.path.join(ROOT, "oracle", "mla_masked.py")).read().replace(
-    "from .mla_oracle import", "from oracle.mla_oracle import")
+SOURCE = oracle_source("mla_masked")
 NAMES = ("mla_attention_masked", "visible_keys")
 
 MUTANTS = {
@@ -34,50 +29,10 @@ MUTANTS = {
 }
 
 
-def _load(source: str) -> types.ModuleType:
-    mod = types.ModuleType("mla_masked_copy")
-    exec(compile(source, "mla_masked_copy", "exec"), mod.__dict__)
-    return mod
-
-
-def _failures(mod) -> list:
-    saved = {n: getattr(pins, n) for n in NAMES}
-    failed = []
-    try:
-        for n in NAMES:
-            setattr(pins, n, getattr(mod, n))
-        for name in sorted(dir(pins)):
-            fn = getattr(pins, name)
-            if not name.startswith("test_") or not callable(fn):
-                continue
-            marks = getattr(fn, "pytestmark", [])
-            cases = [()]
-            for mk in marks:
-                if mk.name == "parametrize":
-                    cases = [c if isinstance(c, tuple) else (c,) for c in mk.args[1]]
-            for args in cases:
-                if len(inspect.signature(fn).parameters) != len(args):
-                    continue
-                try:
-                    fn(*args)
-                except pytest.skip.Exception:
-                    pass
-                except Exception:  # noqa: BLE001 - any failure of a pin counts
-                    failed.append(name)
-    finally:
-        for n, v in saved.items():
-            setattr(pins, n, v)
-    return failed
-
-
 def test_unchanged_copy_passes_every_pin():
-    assert _failures(_load(SOURCE)) == []
+    assert pin_failures(pins, NAMES, load_copy(SOURCE)) == []
 
 
 @pytest.mark.parametrize("what", sorted(MUTANTS))
 def test_planted_mistake_fails_a_pin(what):
-    src = SOURCE
-    for old, new in MUTANTS[what]:
-        assert old in src, (what, old)
-        src = src.replace(old, new)
-    assert _failures(_load(src)), f"no pin caught: {what}"
+    assert pin_failures(pins, NAMES, load_copy(plant(SOURCE, MUTANTS[what]))), f"no pin caught: {what}"

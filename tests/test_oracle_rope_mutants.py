@@ -7,15 +7,12 @@ every pin there: at least one must fail. The unchanged copy must pass them all,
 so the harness itself is checked too.
 """
 
-import os
-import types
-
 import pytest
 
 import test_oracle_rope as pins
+from _mutants import load_copy, oracle_source, pin_failures, plant
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SOURCE = open(os.path.join(ROOT, "oracle", "mla_rope.py")).read()
+SOURCE = oracle_source("mla_rope")
 NAMES = ("apply_rope", "rope_cos_sin", "rope_positions", "yarn_inv_freq", "KIMI_K2_ROPE")
 
 MUTANTS = {
@@ -36,38 +33,10 @@ MUTANTS = {
 }
 
 
-def _load(source: str) -> types.ModuleType:
-    mod = types.ModuleType("mla_rope_copy")
-    exec(compile(source, "mla_rope_copy", "exec"), mod.__dict__)
-    return mod
-
-
-def _failures(mod) -> list:
-    saved = {n: getattr(pins, n) for n in NAMES}
-    failed = []
-    try:
-        for n in NAMES:
-            setattr(pins, n, getattr(mod, n))
-        for name in sorted(dir(pins)):
-            if name.startswith("test_"):
-                try:
-                    getattr(pins, name)()
-                except Exception:  # noqa: BLE001 - any failure of a pin counts
-                    failed.append(name)
-    finally:
-        for n, v in saved.items():
-            setattr(pins, n, v)
-    return failed
-
-
 def test_unchanged_copy_passes_every_pin():
-    assert _failures(_load(SOURCE)) == []
+    assert pin_failures(pins, NAMES, load_copy(SOURCE)) == []
 
 
 @pytest.mark.parametrize("what", sorted(MUTANTS))
 def test_planted_mistake_fails_a_pin(what):
-    src = SOURCE
-    for old, new in MUTANTS[what]:
-        assert old in src, (what, old)
-        src = src.replace(old, new)
-    assert _failures(_load(src)), f"no pin caught: {what}"
+    assert pin_failures(pins, NAMES, load_copy(plant(SOURCE, MUTANTS[what]))), f"no pin caught: {what}"
