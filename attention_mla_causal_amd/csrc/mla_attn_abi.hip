@@ -33,6 +33,25 @@ mla_status device_error(const char* where, hipError_t e) {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// XCDs of the current device (hipDeviceAttributeNumberOfXccs), looked up once
+// per device; -1 when the runtime cannot tell. The decode's in-kernel merge
+// relies on workgroup w running on XCD w % 8, the dispatch order of an
+// 8-XCD part; on any other count the combine kernel merges instead.
+constexpr int kMaxDevices = 64;
+int device_xcds() {
+  static std::atomic<int> cache[kMaxDevices];  // 0: not looked up yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int x = 0;
+    if (hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || x <= 0) x = -1;
+    cache[dev].store(x, std::memory_order_relaxed);
+    n = x;
+  }
+  return n;
+}
+
 }  // namespace
 
 namespace {
@@ -49,21 +68,6 @@ struct DecodeExtras {
   const uint8_t* key_mask = nullptr;  // [B, S] 2D padding mask
   const float* rope_table = nullptr;  // fused rotary prologue: (cos, sin) [>= S positions, 32]
 };
-
-// The rotary table a fused-prologue decode reads: present, aligned, and
-// holding every position up to need - 1.
-mla::CheckResult check_rope_arg(const void* table, int64_t max_pos, int64_t need) {
-  if (table == nullptr) return mla::fail(MLA_ERR_NULL, "rope_table is NULL");
-  if (mla::misaligned(table)) return mla::fail(MLA_ERR_ALIGN, "rope_table is not 16-byte aligned");
-  if (max_pos < need || max_pos > mla::kRopeMaxPositions) {
-    mla::CheckResult r;
-    r.status = MLA_ERR_SHAPE;
-    std::snprintf(r.msg, sizeof(r.msg), "rope_max_pos %lld must cover positions 0..%lld (at most %lld)",
-                  (long long)max_pos, (long long)(need - 1), (long long)mla::kRopeMaxPositions);
-    return r;
-  }
-  return mla::CheckResult{};
-}
 
 // Every decode entry point: fill the arguments from a checked plan and launch.
 mla_status launch_decode_call(const char* where, const void* q_nope, const void* q_pe,
@@ -110,8 +114,9 @@ mla_status launch_decode_call(const char* where, const void* q_nope, const void*
   }
   {
     // The split kernel merges the partials itself when every split of a
-    // (b, h) runs on one XCD (workgroup w runs on XCD w % 8, and the kernel
-    // hands each XCD whole (b, h) groups); otherwise a second kernel merges.
+    // (b, h) runs on one XCD (on an 8-XCD part workgroup w runs on XCD w % 8,
+    // and the kernel hands each XCD whole (b, h) groups); otherwise, or on a
+    // part with another XCD count, a second kernel merges.
     // With a length per sequence, (b, h) pairs are dealt round-robin over
     // the XCDs when B*H is a multiple of 8, which keeps each one's splits
     // together by construction.
@@ -119,7 +124,7 @@ mla_status launch_decode_call(const char* where, const void* q_nope, const void*
     const int64_t grid = bh * plan.nsplit;
     a.interleave = ((seq_lens != nullptr || x.key_mask != nullptr) && bh % 8 == 0) ? 1 : 0;
     const bool together = a.interleave || (grid % 8 == 0 && (grid / 8) % plan.nsplit == 0);
-    a.fused = (plan.nsplit > 1 && plan.nsplit <= 64 && together) ? 1 : 0;
+    a.fused = (plan.nsplit > 1 && plan.nsplit <= 64 && together && device_xcds() == 8) ? 1 : 0;
   }
   a.B = B;
   a.H = H;
@@ -292,7 +297,8 @@ mla_status mla_attn_decode_rope(const void* q_nope, const void* q_pe, const void
   mla::DecodePlan plan;
   mla::CheckResult r = mla::check_decode(q_nope, q_pe, k_nope, k_pe, v, out, workspace,
                                          workspace_bytes, B, H, S, past_len, softmax_scale, &plan);
-  if (r.status == MLA_OK && !r.empty) r = check_rope_arg(rope_table, rope_max_pos, (int64_t)past_len + 1);
+  if (r.status == MLA_OK && !r.empty)
+    r = mla::check_rope_decode_table(rope_table, rope_max_pos, (int64_t)past_len + 1);
   if (r.status != MLA_OK) return report("mla_attn_decode_rope", r);
   if (r.empty) return MLA_OK;
   DecodeExtras x;
@@ -367,7 +373,8 @@ mla_status mla_attn_decode_varlen_rope(const void* q_nope, const void* q_pe,
   mla::CheckResult r = mla::check_decode_varlen(
       q_nope, q_pe, k_nope_cache, k_pe_cache, v_cache, seq_lens, out, workspace, workspace_bytes,
       B, H, cache_len, max_seq_len, softmax_scale, &plan);
-  if (r.status == MLA_OK && !r.empty) r = check_rope_arg(rope_table, rope_max_pos, max_seq_len);
+  if (r.status == MLA_OK && !r.empty)
+    r = mla::check_rope_decode_table(rope_table, rope_max_pos, max_seq_len);
   if (r.status != MLA_OK) return report("mla_attn_decode_varlen_rope", r);
   if (r.empty) return MLA_OK;
   DecodeExtras x;
@@ -399,7 +406,8 @@ mla_status decode_paged_call(const char* where, const void* q_nope, const void* 
       q_nope, q_pe, k_nope_pages, k_pe_pages, v_pages, block_table, seq_lens, k_nope_new,
       k_pe_new, v_new, out, workspace, workspace_bytes, B, H, num_blocks, block_size, max_blocks,
       max_seq_len, softmax_scale, &plan);
-  if (r.status == MLA_OK && !r.empty && rope) r = check_rope_arg(rope_table, rope_max_pos, max_seq_len);
+  if (r.status == MLA_OK && !r.empty && rope)
+    r = mla::check_rope_decode_table(rope_table, rope_max_pos, max_seq_len);
   if (r.status != MLA_OK) return report(where, r);
   if (r.empty) return MLA_OK;
   DecodeExtras x;

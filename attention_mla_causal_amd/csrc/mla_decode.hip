@@ -32,9 +32,9 @@
 //    workspace. If all splits of a (b, h) run on one XCD, they share that
 //    XCD's L2, and the split kernel merges them itself: each workgroup stores
 //    its partial, then a flag holding the call's tag, waits for both stores,
-//    and reads all flags of its (b, h) past L1; whichever sees every flag set
-//    merges (the last to finish always does; two that finish together both
-//    write the same bytes), then clears the flags of its (b, h), so a replayed
+//    and reads all flags of its (b, h) with device-scope loads (past L1);
+//    whichever sees every flag set merges (the last to finish always does;
+//    two that finish together both write the same bytes), then clears the flags of its (b, h), so a replayed
 //    graph, which repeats the captured tag, starts from cleared flags. No
 //    atomics or device-scope fences are needed: on
 //    this chip a device-scope release or acquire writes back or invalidates
@@ -63,6 +63,15 @@ constexpr int NT = NW * 64;
 constexpr int KEYS_PER_LANE = 8; // keys each quarter-wave takes per trip (loads in flight)
 constexpr int KEYS_PER_WAVE = 4 * KEYS_PER_LANE;   // 32
 constexpr int KEYS_PER_TRIP = NW * KEYS_PER_WAVE;  // 128
+
+// Cache-policy operand of the buffer loads that read what other workgroups
+// stored (completion flags, partials): the SC1 bit alone, device scope in the
+// CDNA3/CDNA4 scope encoding (SC1:SC0 = 0 wave, 1 workgroup, 2 device,
+// 3 system). A device-scope load misses in the CU's L1, so it cannot return
+// a line an earlier workgroup on the same CU cached before the store landed;
+// it is served by the XCD's L2, which every split of a (b, h) shares. (SC0
+// alone is workgroup scope, which the L1 may serve.)
+constexpr int kDeviceScope = 16;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -468,8 +477,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   if (!a.fused) return;
   // Completion without atomics: each workgroup publishes its partial, then a
   // flag holding this call's tag, waiting for each store to reach the XCD's
-  // L2; then it reads every flag of its (b, h) past L1. Of the workgroups that
-  // finish last, at least one sees all flags (a store that has completed is
+  // L2; then it reads every flag of its (b, h) with device-scope loads (past
+  // L1). Of the workgroups that finish last, at least one sees all flags (a store that has completed is
   // seen by every later load); any that do merge the same partials the same
   // way and write identical bytes.
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -483,8 +492,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
       (void*)(a.ws_flag + (int64_t)bh * a.nsplit), (short)0, a.nsplit * 8, 0x00020000);
   bool done = true;
   for (int sp = lane; sp < nact; sp += 64) {
-    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(rf, sp * 8, 0, 1);      // sc0: past L1
-    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(rf, sp * 8 + 4, 0, 1);
+    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(rf, sp * 8, 0, kDeviceScope);
+    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(rf, sp * 8 + 4, 0, kDeviceScope);
     done = done && (((unsigned long long)hi << 32 | lo) == a.tag);
   }
   if (__any(!done)) return;
@@ -506,9 +515,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) oo[e] = 0.0f;
   for (int sp = qq; sp < nact; sp += 4) {
-    const u32x4 mlw = __builtin_amdgcn_raw_buffer_load_b128(rm, sp * 16, 0, 1);
-    const u32x4 w0 = __builtin_amdgcn_raw_buffer_load_b128(ro, (sp * DV + 8 * cl) * 4, 0, 1);
-    const u32x4 w1 = __builtin_amdgcn_raw_buffer_load_b128(ro, (sp * DV + 8 * cl + 4) * 4, 0, 1);
+    const u32x4 mlw = __builtin_amdgcn_raw_buffer_load_b128(rm, sp * 16, 0, kDeviceScope);
+    const u32x4 w0 = __builtin_amdgcn_raw_buffer_load_b128(ro, (sp * DV + 8 * cl) * 4, 0, kDeviceScope);
+    const u32x4 w1 = __builtin_amdgcn_raw_buffer_load_b128(ro, (sp * DV + 8 * cl + 4) * 4, 0, kDeviceScope);
     const uint32_t m_bits = mlw[0], l_bits = mlw[1], x_bits = mlw[2];
     same_xcd = same_xcd && (x_bits == my_xcc);
     const float m_sp = __builtin_bit_cast(float, m_bits), l_sp = __builtin_bit_cast(float, l_bits);
@@ -527,8 +536,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   merge_xor(mm, ll, oo, 32);
   same_xcd = !__any(!same_xcd);
   if (qq == 0) {
-    // A partial written on another XCD may not be visible here: poison the
-    // output rather than return a silently wrong row.
+    // A partial written on another XCD may not be visible here. The host
+    // takes this path only on a part that reports 8 XCDs, whose dispatcher
+    // places workgroup w on XCD w % 8; should placement ever differ, the row
+    // is poisoned (NaN) rather than silently wrong.
     const float inv = !same_xcd ? __builtin_nanf("") : (ll > 0.0f ? 1.0f / ll : 0.0f);
     uint16_t* dst = a.out + (int64_t)bh * DV + 8 * cl;
     u32x4 w;

@@ -109,6 +109,20 @@ inline CheckResult fail(mla_status s, const char* what) {
 
 inline bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
+// softmax_scale: any finite value, of either sign or zero, whose product with
+// log2(e) (the factor the kernels fold into their exponent) is a finite fp32
+// (|scale| <= FLT_MAX / log2(e), about 2.36e38). Returns true, with r filled
+// in, when the scale is refused.
+inline bool check_scale(float scale, CheckResult* r) {
+  const float c = scale * 1.4426950408889634f;
+  if (std::isfinite(scale) && std::isfinite(c)) return false;
+  std::snprintf(r->msg, sizeof(r->msg),
+                "softmax_scale %g must be finite, with softmax_scale * log2(e) finite in fp32",
+                (double)scale);
+  r->status = MLA_ERR_SCALE;
+  return true;
+}
+
 // Common part of both entry points. T is the number of new queries.
 inline CheckResult check_common(const void* q_nope, const void* q_pe, const void* k_nope,
                                 const void* k_pe, const void* v, const void* out, int64_t B,
@@ -151,13 +165,7 @@ inline CheckResult check_common(const void* q_nope, const void* q_pe, const void
       return r;
     }
   }
-  const float c = scale * 1.4426950408889634f;
-  if (!std::isfinite(scale) || !(scale > 0.0f) || !std::isfinite(c)) {
-    std::snprintf(r.msg, sizeof(r.msg), "softmax_scale %g must be finite and positive",
-                  (double)scale);
-    r.status = MLA_ERR_SCALE;
-    return r;
-  }
+  if (check_scale(scale, &r)) return r;
   return r;
 }
 
@@ -304,13 +312,7 @@ inline CheckResult check_prefill_varlen(const void* q_nope, const void* q_pe, co
       return r;
     }
   }
-  const float c = scale * 1.4426950408889634f;
-  if (!std::isfinite(scale) || !(scale > 0.0f) || !std::isfinite(c)) {
-    std::snprintf(r.msg, sizeof(r.msg), "softmax_scale %g must be finite and positive",
-                  (double)scale);
-    r.status = MLA_ERR_SCALE;
-    return r;
-  }
+  if (check_scale(scale, &r)) return r;
   if (max_kv > kMaxPrefillKeys) {
     std::snprintf(r.msg, sizeof(r.msg), "max_kv_len=%lld keys exceeds the prefill limit of %lld",
                   (long long)max_kv, (long long)kMaxPrefillKeys);
@@ -398,13 +400,7 @@ inline CheckResult check_decode_varlen(const void* q_nope, const void* q_pe, con
       return r;
     }
   }
-  const float c = scale * 1.4426950408889634f;
-  if (!std::isfinite(scale) || !(scale > 0.0f) || !std::isfinite(c)) {
-    std::snprintf(r.msg, sizeof(r.msg), "softmax_scale %g must be finite and positive",
-                  (double)scale);
-    r.status = MLA_ERR_SCALE;
-    return r;
-  }
+  if (check_scale(scale, &r)) return r;
   const DecodePlan plan = plan_decode_varlen(B, H, max_len);
   if (B * H > kMaxGrid / plan.nsplit) {
     std::snprintf(r.msg, sizeof(r.msg), "B*H*nsplit exceeds the grid limit");
@@ -494,13 +490,7 @@ inline CheckResult check_decode_paged(const void* q_nope, const void* q_pe, cons
       return r;
     }
   }
-  const float c = scale * 1.4426950408889634f;
-  if (!std::isfinite(scale) || !(scale > 0.0f) || !std::isfinite(c)) {
-    std::snprintf(r.msg, sizeof(r.msg), "softmax_scale %g must be finite and positive",
-                  (double)scale);
-    r.status = MLA_ERR_SCALE;
-    return r;
-  }
+  if (check_scale(scale, &r)) return r;
   const DecodePlan plan = plan_decode_varlen(B, H, max_len);
   if (B * H > kMaxGrid / plan.nsplit) {
     std::snprintf(r.msg, sizeof(r.msg), "B*H*nsplit exceeds the grid limit");
@@ -647,6 +637,24 @@ inline CheckResult check_rope_table(const void* table, int64_t max_pos, double t
   if (table == nullptr) return fail(MLA_ERR_NULL, "table is NULL");
   if (misaligned(table)) return fail(MLA_ERR_ALIGN, "table is not 16-byte aligned");
   return r;
+}
+
+// The rotary table a fused-prologue decode reads: present, 16-byte aligned,
+// and holding every position up to need - 1, and at least one row (the
+// kernel reads the row of position S - 1, or row 0 for an empty sequence).
+inline CheckResult check_rope_decode_table(const void* table, int64_t max_pos, int64_t need) {
+  if (table == nullptr) return fail(MLA_ERR_NULL, "rope_table is NULL");
+  if (misaligned(table)) return fail(MLA_ERR_ALIGN, "rope_table is not 16-byte aligned");
+  const int64_t rows = need > 1 ? need : 1;
+  if (max_pos < rows || max_pos > kRopeMaxPositions) {
+    CheckResult r;
+    r.status = MLA_ERR_SHAPE;
+    std::snprintf(r.msg, sizeof(r.msg),
+                  "rope_max_pos %lld must cover positions 0..%lld (at least one row, at most %lld)",
+                  (long long)max_pos, (long long)(rows - 1), (long long)kRopeMaxPositions);
+    return r;
+  }
+  return CheckResult{};
 }
 
 // x: [B, R, T, 64] bf16, rotated in place; row t of sequence b at position

@@ -102,11 +102,18 @@ __global__ __launch_bounds__(256) void latent_absorb_kernel(LatentArgs a) {
     *reinterpret_cast<u32x4*>(wt + row * ABS_ROW + col * 16) =
         *reinterpret_cast<const u32x4*>(wk + (int64_t)row * R + col * 8);
   }
-  if (chunk == 0) {  // the rotary query goes through unchanged
+  // The sign of softmax_scale travels with the joined query (see
+  // positive_cl2): negated for a negative scale (exact in bf16), cleared for a
+  // zero one.
+  const float cl2_in = a.scale_log2;
+  const uint32_t q_and = cl2_in == 0.0f ? 0u : 0xffffffffu;
+  const uint32_t q_xor = cl2_in < 0.0f ? 0x80008000u : 0u;
+  const float q_mul = cl2_in == 0.0f ? 0.0f : (cl2_in < 0.0f ? -1.0f : 1.0f);
+  if (chunk == 0) {  // the rotary query goes through unchanged (but for that sign)
     for (int c = tid; c < a.B * 8; c += 256) {
       const int64_t bh = (int64_t)(c >> 3) * a.H + h;
       *reinterpret_cast<u32x4*>(a.qt + bh * KW + R + (c & 7) * 8) =
-          *reinterpret_cast<const u32x4*>(a.q_pe + bh * DR + (c & 7) * 8);
+          (*reinterpret_cast<const u32x4*>(a.q_pe + bh * DR + (c & 7) * 8) & q_and) ^ q_xor;
     }
   }
   // query fragments of the first 16 batches load while W lands in LDS
@@ -139,7 +146,10 @@ __global__ __launch_bounds__(256) void latent_absorb_kernel(LatentArgs a) {
 #pragma unroll
     for (int ks = 0; ks < DN / 32; ++ks) acc = mfma16(wf[ks], __builtin_bit_cast(bf16x8, qv[ks]), acc);
     if (b0 + 16 < a.B) load_q(b0 + 16, qv);
-    // acc[r] = q~[b][e0 + 16w + 4g + r]
+    // acc[r] = q~[b][e0 + 16w + 4g + r]; RNE rounding is symmetric, so
+    // bf16(-x) = -bf16(x) and the sign can be applied before rounding
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] *= q_mul;
     const int b = b0 + j;
     if (b < a.B) {
       const uint32_t p0 = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
@@ -168,6 +178,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* seq,
   const int records = left > 0 ? (int)(left * rowbytes) : 0;
   return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)seq + kb * rowbytes), (short)0,
                                            records, 0x00020000);
+}
+
+// The softmax takes the running max of the unscaled scores and scales it by
+// cl2 = softmax_scale * log2(e), which needs cl2 > 0. Any finite scale is
+// served: the absorb kernel stores the joined query negated for a negative
+// scale (scale * q.k = |scale| * (-q).k) and cleared for a zero scale (every
+// key then scores 0, as with scale 0), and the attention runs with |cl2|, or
+// with 1 when the scale is zero.
+__device__ __forceinline__ float positive_cl2(float cl2_in) {
+  return cl2_in == 0.0f ? 1.0f : __builtin_fabsf(cl2_in);
 }
 
 // ---- 2. attention over the latent keys of one key split
@@ -269,7 +289,7 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
   const int vA0 = vrow * 64 + (((j & 3) >> 1) ^ tile_swz(vrow)) * 16 + 8 * (j & 1);        // even dt
   const int vA1 = vrow * 64 + ((2 + ((j & 3) >> 1)) ^ tile_swz(vrow)) * 16 + 8 * (j & 1);  // odd dt
 
-  const float cl2 = a.scale_log2;
+  const float cl2 = positive_cl2(a.scale_log2);
   // o[hg * NDTW + d]: dims 128w + 16d + 4g + r, head 16 hg + j
   f32x4 o[NWAVE * NDTW];
 #pragma unroll

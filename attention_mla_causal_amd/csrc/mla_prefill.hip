@@ -235,7 +235,7 @@ __device__ __forceinline__ void smx_slot(Smx& st, f32x16& c, bf16x8 (&pc)[2], Ac
   if constexpr (SLOT < 4) {  // running max of the raw scores, 4 per slot
 #pragma unroll
     for (int r = 4 * SLOT; r < 4 * SLOT + 4; ++r) st.mx = fmaxf(st.mx, c[r]);
-  } else if constexpr (SLOT == 4) {  // new running max (scale > 0) and rescale factor
+  } else if constexpr (SLOT == 4) {  // new running max (cl2 > 0) and rescale factor
     const float mx = max_pair32(st.mx);
     const float m_new = fmaxf(acc.m_run, mx * cl2);
     st.m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
@@ -645,6 +645,18 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
     km1 = load_km(1);
   }
 
+  // ---- any finite softmax_scale. The softmax below takes the running max of
+  // the unscaled scores and scales it by cl2 = scale * log2(e), which needs
+  // cl2 > 0. A negative scale gives the same scaled scores as |scale| with the
+  // query negated (scale * q.k = |scale| * (-q).k; flipping bf16 sign bits is
+  // exact); a zero scale gives every visible key the same score 0, as a zero
+  // query with cl2 = 1 does. So the query fragments are sign-flipped or
+  // cleared once here and the loop always runs with a positive cl2.
+  const float cl2_in = a.scale_log2;
+  const uint32_t q_and = cl2_in == 0.0f ? 0u : 0xffffffffu;
+  const uint32_t q_xor = cl2_in < 0.0f ? 0x80008000u : 0u;
+  const float cl2 = cl2_in == 0.0f ? 1.0f : __builtin_fabsf(cl2_in);
+
   // ---- query fragments (B operand): 8 dims of the lane's query per K-step
   bf16x8 qf[12];
   {
@@ -652,10 +664,11 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
     const bool ok = myq < T;
     const uint16_t* qn = a.q_nope + ((int64_t)bh * Tst + myq) * DN + 8 * hi;
     const uint16_t* qp = a.q_pe + ((int64_t)bh * Tst + myq) * DR + 8 * hi;
+    auto signed_q = [&](u32x4 w) { return as_bf16x8((w & q_and) ^ q_xor); };
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qf[kk] = as_bf16x8(ok ? ldg16(qn + 16 * kk) : u32x4{0, 0, 0, 0});
+    for (int kk = 0; kk < 8; ++kk) qf[kk] = signed_q(ok ? ldg16(qn + 16 * kk) : u32x4{0, 0, 0, 0});
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qf[8 + kk] = as_bf16x8(ok ? ldg16(qp + 16 * kk) : u32x4{0, 0, 0, 0});
+    for (int kk = 0; kk < 4; ++kk) qf[8 + kk] = signed_q(ok ? ldg16(qp + 16 * kk) : u32x4{0, 0, 0, 0});
   }
 
   Lane ln;
@@ -670,7 +683,6 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
     ln.va1 = (vrow + 8) * 64 + ((vc4 ^ (hi + 2)) * 16) + 8 * (sl & 1);
   }
 
-  const float cl2 = a.scale_log2;
   Acc acc;
 #pragma unroll
   for (int n = 0; n < 4; ++n)

@@ -37,7 +37,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kPairs = 32;
 constexpr int kRowsPerThread = 5;   // measured: 4 → 10.97 µs, 5 → 9.60, 6 → 10.02, 8 → 11.09 on 2048 new tokens
 constexpr int kThreads = 256;
-constexpr int kRowsPerBlock = kThreads / 16 * kRowsPerThread;  // 64
+constexpr int kRowsPerBlock = kThreads / 16 * kRowsPerThread;  // 80
 
 __global__ __launch_bounds__(kThreads) void mla_rope_table_kernel(RopeTableArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;

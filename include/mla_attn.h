@@ -35,8 +35,12 @@
  *    mla_last_error() gives a thread-local description of the last failure.
  *  - B == 0, H == 0 or T == 0 is a valid empty call: it returns MLA_OK
  *    (the rotary calls state their own empty cases).
- *  - softmax_scale is taken as a 32-bit float and must be finite and > 0
- *    (the model's scale is an inverse square root, always positive).
+ *  - softmax_scale is taken as a 32-bit float and may be any finite value,
+ *    zero and negative included (the pages multiply the scores by it without
+ *    stating its value); the kernels fold softmax_scale * log2(e) into their
+ *    exponent, so |softmax_scale| must stay at most FLT_MAX / log2(e)
+ *    (about 2.36e38). NaN, infinities and larger magnitudes are
+ *    MLA_ERR_SCALE. A zero scale weights every visible key equally.
  */
 #ifndef MLA_ATTN_H_
 #define MLA_ATTN_H_
@@ -57,8 +61,8 @@ typedef enum mla_status {
   MLA_ERR_NULL = 1,      /* a pointer to a non-empty tensor is NULL */
   MLA_ERR_SHAPE = 2,     /* negative size, S != past_len + T, or size beyond the launch limits */
   MLA_ERR_ALIGN = 3,     /* a tensor pointer is not 16-byte aligned */
-  MLA_ERR_SCALE = 4,     /* softmax_scale is NaN, infinite, zero or negative (or a RoPE
-                            parameter out of range) */
+  MLA_ERR_SCALE = 4,     /* softmax_scale is NaN or infinite, or softmax_scale * log2(e)
+                            overflows fp32 (or a RoPE parameter is out of range) */
   MLA_ERR_WORKSPACE = 5, /* decode workspace missing or smaller than required */
   MLA_ERR_DEVICE = 6     /* the HIP runtime reported an error at launch */
 } mla_status;
@@ -445,8 +449,9 @@ mla_status mla_attn_decode_rope(const void* q_nope, const void* q_pe, const void
  * seq_lens[b] - 1 (its last key; lengths clamped on the device as for
  * mla_attn_decode_varlen). The cache holds keys already rotated at their
  * positions. rope_table as for mla_attn_decode_rope, covering positions up
- * to max_seq_len - 1 (rope_max_pos >= max_seq_len, else MLA_ERR_SHAPE).
- * Other errors as for mla_attn_decode_varlen.
+ * to max_seq_len - 1 and holding at least one row (rope_max_pos >=
+ * max(max_seq_len, 1), else MLA_ERR_SHAPE). Other errors as for
+ * mla_attn_decode_varlen.
  */
 mla_status mla_attn_decode_varlen_rope(const void* q_nope, const void* q_pe,
                                        const void* k_nope_cache, const void* k_pe_cache,
@@ -463,9 +468,9 @@ mla_status mla_attn_decode_varlen_rope(const void* q_nope, const void* q_pe,
  * table on the device); the kernel turns the query there, and turns the new
  * key there, rounds it to bf16 and both attends to it and stores it in its
  * slot, so later calls read the same rotated key. rope_table as for
- * mla_attn_decode_rope, covering positions up to max_seq_len - 1
- * (rope_max_pos >= max_seq_len, else MLA_ERR_SHAPE). Other errors as for
- * mla_attn_decode_paged.
+ * mla_attn_decode_rope, covering positions up to max_seq_len - 1 and
+ * holding at least one row (rope_max_pos >= max(max_seq_len, 1), else
+ * MLA_ERR_SHAPE). Other errors as for mla_attn_decode_paged.
  */
 mla_status mla_attn_decode_paged_rope(const void* q_nope, const void* q_pe, void* k_nope_pages,
                                       void* k_pe_pages, void* v_pages, const int32_t* block_table,

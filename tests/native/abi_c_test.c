@@ -37,8 +37,8 @@ int main(void) {
          "masked prefill without a mask");
   expect(mla_attn_decode(p, p, p, p, p, p, NULL, 0, 1, 64, 1001, 1000, sc, NULL) ==
              MLA_ERR_WORKSPACE, "decode without its workspace");
-  expect(mla_attn_decode_masked(p, p, p, p, p, mask, p, p, 1 << 20, 1, 64, 1001, 1000, -1.0f, NULL) ==
-             MLA_ERR_SCALE, "masked decode with a negative scale");
+  expect(mla_attn_decode_masked(p, p, p, p, p, mask, p, p, 1 << 20, 1, 64, 1001, 1000, 1.0f / 0.0f, NULL) ==
+             MLA_ERR_SCALE, "masked decode with an infinite scale");
   expect(mla_attn_decode_varlen(p, p, p, p, p, lens, p, p, 1 << 20, 1, 64, 1000, 1001, sc, NULL) ==
              MLA_ERR_SHAPE, "varlen decode max_seq_len > cache_len");
   expect(mla_attn_decode_paged(p, p, p, p, p, lens, lens, NULL, NULL, NULL, p, p, 1 << 20, 4, 64, 100,

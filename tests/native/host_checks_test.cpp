@@ -56,8 +56,14 @@ int main() {
   // scale
   EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, NAN, 128).status == MLA_ERR_SCALE);
   EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, INFINITY, 128).status == MLA_ERR_SCALE);
-  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, 0.0f, 128).status == MLA_ERR_SCALE);
-  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, -0.5f, 128).status == MLA_ERR_SCALE);
+  // any finite scale is valid (zero and negative included) while scale * log2(e) stays finite
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, 0.0f, 128).status == MLA_OK);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, -0.0f, 128).status == MLA_OK);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, -0.5f, 128).status == MLA_OK);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, 2.3e38f, 128).status == MLA_OK);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, -2.3e38f, 128).status == MLA_OK);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, -3.0e38f, 128).status == MLA_ERR_SCALE);
+  EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, -INFINITY, 128).status == MLA_ERR_SCALE);
   EXPECT(check_prefill(p, p, p, p, p, p, 1, 2, 3, 3, 0, 3.0e38f, 128).status == MLA_ERR_SCALE);
 
   // decode planning
@@ -163,7 +169,9 @@ int main() {
     EXPECT(check_prefill_varlen(p, p, p, p, p, p, p, p, -1, 64, 16, 16, sc, 128).status == MLA_ERR_SHAPE);
     EXPECT(check_prefill_varlen(p, p, p, p, p, p, p, p, 1, 64, 16, 8388608, sc, 128).status == MLA_ERR_SHAPE);
     EXPECT(check_prefill_varlen(p, p, p, p, p, p, p, p, 1, 64, 16, 8388607, sc, 128).status == MLA_OK);
-    EXPECT(check_prefill_varlen(p, p, p, p, p, p, p, p, 1, 64, 16, 16, 0.0f, 128).status == MLA_ERR_SCALE);
+    EXPECT(check_prefill_varlen(p, p, p, p, p, p, p, p, 1, 64, 16, 16, 0.0f, 128).status == MLA_OK);
+    EXPECT(check_prefill_varlen(p, p, p, p, p, p, p, p, 1, 64, 16, 16, -1.0f, 128).status == MLA_OK);
+    EXPECT(check_prefill_varlen(p, p, p, p, p, p, p, p, 1, 64, 16, 16, NAN, 128).status == MLA_ERR_SCALE);
     const CheckResult e = check_prefill_varlen(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                                nullptr, nullptr, 4, 64, 0, 100, sc, 128);
     EXPECT(e.status == MLA_OK && e.empty);
@@ -214,6 +222,32 @@ int main() {
     EXPECT(check_rope_apply(p, reinterpret_cast<const int32_t*>(reinterpret_cast<uintptr_t>(p) + 2), p,
                             16, 1, 1, 1, 0).status == MLA_ERR_ALIGN);
     EXPECT(check_rope_apply(p, lens, p, 1 << 20, 65536, 64, 1024, 0).status == MLA_ERR_SHAPE);  // 2^32 rows
+
+    // the table of a fused-prologue decode: every position below `need`, and
+    // at least one row even when no sequence has a key (the kernel reads row 0)
+    EXPECT(check_rope_decode_table(p, 1001, 1001).status == MLA_OK);
+    EXPECT(check_rope_decode_table(p, 1000, 1001).status == MLA_ERR_SHAPE);
+    EXPECT(check_rope_decode_table(p, 0, 0).status == MLA_ERR_SHAPE);
+    EXPECT(check_rope_decode_table(p, 1, 0).status == MLA_OK);
+    EXPECT(check_rope_decode_table(p, (int64_t(1) << 24) + 1, 16).status == MLA_ERR_SHAPE);
+    EXPECT(check_rope_decode_table(nullptr, 16, 16).status == MLA_ERR_NULL);
+    EXPECT(check_rope_decode_table(bad, 16, 16).status == MLA_ERR_ALIGN);
+  }
+  // every decode check accepts zero and negative scales and refuses non-finite ones
+  {
+    DecodePlan dp;
+    EXPECT(check_decode(p, p, p, p, p, p, p, size_t(1) << 30, 1, 64, 1001, 1000, 0.0f, &dp).status == MLA_OK);
+    EXPECT(check_decode(p, p, p, p, p, p, p, size_t(1) << 30, 1, 64, 1001, 1000, -0.07f, &dp).status == MLA_OK);
+    EXPECT(check_decode(p, p, p, p, p, p, p, size_t(1) << 30, 1, 64, 1001, 1000, NAN, &dp).status == MLA_ERR_SCALE);
+    EXPECT(check_decode_varlen(p, p, p, p, p, p, p, p, size_t(1) << 30, 2, 8, 64, 64, -3.0f, &dp).status == MLA_OK);
+    EXPECT(check_decode_varlen(p, p, p, p, p, p, p, p, size_t(1) << 30, 2, 8, 64, 64, INFINITY, &dp).status == MLA_ERR_SCALE);
+    EXPECT(check_decode_paged(p, p, p, p, p, p, p, nullptr, nullptr, nullptr, p, p, size_t(1) << 30, 2, 8, 4, 32,
+                              2, 64, 0.0f, &dp).status == MLA_OK);
+    EXPECT(check_decode_paged(p, p, p, p, p, p, p, nullptr, nullptr, nullptr, p, p, size_t(1) << 30, 2, 8, 4, 32,
+                              2, 64, NAN, &dp).status == MLA_ERR_SCALE);
+    LatentPlan lp;
+    EXPECT(check_latent_decode(p, p, p, p, p, p, p, size_t(1) << 30, 1, 64, 1001, 1000, -0.07f, &lp).status == MLA_OK);
+    EXPECT(check_latent_decode(p, p, p, p, p, p, p, size_t(1) << 30, 1, 64, 1001, 1000, 0.0f, &lp).status == MLA_OK);
   }
   if (failures) {
     std::printf("%d failures\n", failures);

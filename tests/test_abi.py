@@ -80,7 +80,7 @@ def test_prefill_null_align_scale_errors(lib):
         assert _prefill(lib, ptrs, 1, 2, 3, 3, 0) == 1
         ptrs[i] = MISALIGNED
         assert _prefill(lib, ptrs, 1, 2, 3, 3, 0) == 3
-    for bad in (float("nan"), float("inf"), 0.0, -1.0):
+    for bad in (float("nan"), float("inf"), float("-inf"), 3.0e38, -3.0e38):
         assert _prefill(lib, [ALIGNED] * 6, 1, 2, 3, 3, 0, bad) == 4
     assert "softmax_scale" in lib.mla_last_error().decode()
 
@@ -175,7 +175,7 @@ def test_varlen_decode_errors(lib):
     assert _varlen(lib, [None] * 7, None, 0, 0, 64, 2048, 1001) == 0      # empty batch: no-op
     assert _varlen(lib, ok, None, need, 1, 64, 2048, 1001) == 5
     assert _varlen(lib, ok, ALIGNED, need - 1, 1, 64, 2048, 1001) == 5
-    assert _varlen(lib, ok, ALIGNED, need, 1, 64, 2048, 1001, 0.0) == 4
+    assert _varlen(lib, ok, ALIGNED, need, 1, 64, 2048, 1001, float("nan")) == 4
     assert "mla_attn_decode_varlen" in lib.mla_last_error().decode()
 
 
@@ -259,7 +259,7 @@ def test_prefill_varlen_errors(lib):
     ptrs = list(ok)
     ptrs[5] = ptrs[6] = ctypes.c_void_p(0x10004)
     assert call(ptrs, 2, 4, 16, 32, float("nan")) == 4
-    assert call(ok, 2, 4, 16, 32, -1.0) == 4
+    assert call(ok, 2, 4, 16, 32, float("-inf")) == 4
     assert "mla_attn_prefill_varlen" in lib.mla_last_error().decode()
     assert call([None] * 8, 2, 4, 0, 32) == 0               # no query rows: empty call
     assert call([None] * 8, 0, 4, 16, 32) == 0
@@ -281,7 +281,7 @@ def test_masked_errors(lib):
     assert "attn_mask is NULL" in lib.mla_last_error().decode()
     odd = list(ok)
     odd[5] = ctypes.c_void_p(0x10003)                           # the mask needs no alignment: stops at the scale
-    assert pre(odd, 1, 4, 16, 20, 4, 0.0) == 4
+    assert pre(odd, 1, 4, 16, 20, 4, float("inf")) == 4
     assert pre([None] * 7, 0, 4, 16, 20, 4) == 0               # empty call
     need = lib.mla_attn_decode_varlen_workspace_bytes(1, 64, 1001)
     assert dec(ok, ALIGNED, need, 1, 64, 1001, 999) == 2

@@ -38,6 +38,9 @@ def _setup(lens, H, bs, seed, spare=2, nan_unowned=True):
 
 def _call(d, table, lens, max_len, append, out=None, workspace=None):
     import torch
+    if out is None:  # NaN first, so a row the kernel never writes fails the parity check
+        B, H = d["q_nope"].shape[:2]
+        out = torch.full((B, H, 1, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
     tb = torch.as_tensor(table, device="cuda")
     sl = torch.as_tensor(np.asarray(lens, dtype=np.int32), device="cuda")
     new = (d["k_nope_new"], d["k_pe_new"], d["v_new"]) if append else None
@@ -149,6 +152,7 @@ def test_graph_decode_loop_appends_one_token_per_replay():
         for k in ("k_nope_new", "k_pe_new", "v_new", "q_nope"):
             host[k] = rng.integers(0x3C00, 0x4000, size=host[k].shape).astype(np.uint16)
             d[k].copy_(upload({k: host[k]})[k])
+        out.fill_(float("nan"))  # a (b, h) the replay does not merge keeps its NaN
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()

@@ -319,9 +319,11 @@ def test_fused_prologue_paged_append_graph_loop():
         sl.copy_(torch.as_tensor(np.asarray(lens0, dtype=np.int32) + r + 1, device="cuda"))
         for k in inp:
             inp[k].copy_(torch.as_tensor(rng.standard_normal(tuple(inp[k].shape)), device="cuda").to(torch.bfloat16))
+        out_g.fill_(float("nan"))  # a (b, h) the replay does not merge keeps its NaN
         g.replay()
         torch.cuda.synchronize()
-        out_e = step(pages_e, None)
+        assert torch.isfinite(out_g).all().item(), f"replay {r} left rows unwritten"
+        out_e = step(pages_e, torch.full_like(out_g, float("nan")))
         torch.cuda.synchronize()
         log(f"  replay {r}: lens={sl.tolist()}")
         assert np.array_equal(to_host_bits(out_g), to_host_bits(out_e)), f"output, replay {r}"

@@ -34,6 +34,9 @@ def _cache(B, H, cap, seed, lens=None):
 
 def _gpu(d, lens, max_len, out=None, workspace=None):
     import torch
+    if out is None:  # NaN first, so a row the kernel never writes fails the parity check
+        B, H = d["q_nope"].shape[:2]
+        out = torch.full((B, H, 1, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
     sl = torch.as_tensor(np.asarray(lens, dtype=np.int32), device="cuda")
     o = _lib().mla_attn_decode_varlen(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], sl,
                                       max_len, ALPHA, out=out, workspace=workspace)
@@ -127,11 +130,13 @@ def test_graph_replays_follow_the_device_lengths():
     torch.cuda.synchronize()
     for i, lens in enumerate(([cap, 7, 1000], [1, 2048, 0], [513, 3, 2047], [cap, 7, 1000])):
         sl.copy_(torch.tensor(lens, dtype=torch.int32))
+        out.fill_(float("nan"))  # a (b, h) the replay does not merge keeps its NaN
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         replayed = to_host_bits(out).copy()
-        eager = to_host_bits(_gpu(d, lens, cap))
+        assert np.isfinite(to_host_f64(out)).all(), f"replay {i} left rows unwritten"
+        eager = to_host_bits(_gpu(d, lens, cap, out=torch.full_like(out, float("nan"))))
         assert np.array_equal(replayed, eager), f"replay {i} with lengths {lens}"
         if i == 1:
             assert_parity(to_host_f64(out), _oracle(x, lens), "varlen graph replay")
