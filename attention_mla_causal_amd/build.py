@@ -1,10 +1,11 @@
-"""Build libmla_attn.so in-tree with hipcc for gfx950.
+"""Build the HIP libraries in-tree with hipcc for gfx950.
 
     python attention_mla_causal_amd/build.py
 
-Compiles every HIP source under csrc/ into one shared library next to this
-file. Always recompiles (it is the "does it build" step); loading the
-library never builds it.
+Compiles the attention core's HIP sources under csrc/ into libmla_attn.so
+next to this file, and the benchmark's measurement probes (csrc/mla_probe.hip,
+outside the attention ABI) into libmla_probe.so. Always recompiles (it is the
+"does it build" step); loading a library never builds it.
 """
 
 from __future__ import annotations
@@ -20,6 +21,8 @@ LIB_NAME = "libmla_attn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = ["mla_attn_abi.hip", "mla_prefill.hip", "mla_decode.hip", "mla_latent.hip", "mla_rope.hip"]
+PROBE_SOURCES = ["mla_probe.hip"]
+PROBE_LIB_PATH = os.path.join(HERE, "libmla_probe.so")
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",
@@ -41,8 +44,15 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra_flags=None) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
+    """Build libmla_attn.so and libmla_probe.so; returns the first's path."""
+    _build_one(SOURCES, LIB_PATH, verbose, extra_flags)
+    _build_one(PROBE_SOURCES, PROBE_LIB_PATH, verbose, extra_flags)
+    return LIB_PATH
+
+
+def _build_one(sources, lib_path, verbose, extra_flags) -> str:
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS, *(extra_flags or []), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -53,8 +63,8 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out.strip():
         print(out, flush=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

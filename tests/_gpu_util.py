@@ -57,3 +57,26 @@ def assert_parity(gpu: np.ndarray, ref: np.ndarray, what: str = ""):
     assert ok, (f"{what}: elementwise bound violated at {worst}: gpu={gpu[worst]} "
                 f"oracle={ref[worst]} err={err[worst]:.3e}")
     assert rel_fro <= REL_FRO_MAX, f"{what}: relative Frobenius error {rel_fro:.3e} > {REL_FRO_MAX}"
+
+
+def spread_pairs(B: int, H: int, n: int, seed: int = 0) -> list:
+    """Up to n (b, h) pairs: both ends, one in each eighth of the b*H + h range
+    and one of each residue of b*H + h mod 8 (the two ways the decode kernels
+    deal (b, h) pairs to the XCDs), then random ones."""
+    import numpy as np
+
+    rng = np.random.default_rng(seed)
+    BH = B * H
+    eighth = max(BH // 8, 1)
+    flat = [0, BH - 1]
+    for r in range(8):
+        flat.append(min(BH - 1, r * BH // 8 + int(rng.integers(eighth))))
+        flat.append(min(BH - 1, 8 * int(rng.integers(eighth)) + r))
+    while len(set(flat)) < min(n, BH):
+        flat.append(int(rng.integers(BH)))
+    return [divmod(f, H) for f in list(dict.fromkeys(flat))[:n]]
+
+
+def spread_heads(H: int) -> list:
+    """Four heads spread over [0, H): first, last and two between."""
+    return sorted({0, H // 3, 2 * H // 3, H - 1})

@@ -6,7 +6,7 @@ import pytest
 from oracle import mla_attention
 from seeded_inputs import SHARD_WORKLOADS, WORKLOADS, device_inputs, host_inputs, random_inputs
 
-from _gpu_util import assert_parity, log, to_host_bits, to_host_f64, upload
+from _gpu_util import assert_parity, log, spread_pairs, to_host_bits, to_host_f64, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -190,19 +190,15 @@ def test_decode_determinism():
 def test_batched_decode_full_size_sampled(name):
     """The full batched decode (B=32, H=64, S=8192; 8.6 GB of keys and values;
     and one GPU's 8-head share of it), inputs drawn on the device; the oracle
-    checks sampled (b, h) rows."""
+    checks 64 (b, h) rows spread over both XCD placements of the pairs."""
     import torch
     wl = WORKLOADS[name] if name in WORKLOADS else SHARD_WORKLOADS[name]
     log(f"case batched_decode B={wl.B} H={wl.H} P={wl.past_len}")
     d = device_inputs(wl, "cuda", seed=0)
     out = _gpu_decode(d, wl.past_len, wl.softmax_scale)
     assert torch.isfinite(out).all().item()
-    rng = np.random.default_rng(0)
-    picks = {(0, 0), (wl.B - 1, wl.H - 1)}
-    while len(picks) < 12:
-        picks.add((int(rng.integers(wl.B)), int(rng.integers(wl.H))))
     got, ref = [], []
-    for b, h in sorted(picks):
+    for b, h in spread_pairs(wl.B, wl.H, 64):
         xs = {
             "q_nope": to_host_bits(d["q_nope"][b:b + 1, h:h + 1]),
             "q_pe": to_host_bits(d["q_pe"][b:b + 1, h:h + 1]),

@@ -7,7 +7,7 @@ import pytest
 from oracle import mla_decode_latent, mla_decode_latent_rows
 from seeded_inputs import LATENT_WORKLOADS, latent_device_inputs, latent_host_inputs, latent_random_inputs
 
-from _gpu_util import assert_parity, log, to_host_bits, to_host_f64, upload
+from _gpu_util import assert_parity, log, spread_pairs, to_host_bits, to_host_f64, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -77,19 +77,16 @@ def test_latent_workspace_garbage_and_determinism():
 
 
 def test_latent_batched_decode_full_size_sampled():
-    """B=32, H=64, S=8192 with inputs drawn on the device; sampled (b, h) rows
-    against the oracle (which decompresses one head at a time)."""
+    """B=32, H=64, S=8192 with inputs drawn on the device; 64 (b, h) rows
+    spread over the batch and heads against the oracle (which decompresses one
+    head at a time)."""
     import torch
     wl = LATENT_WORKLOADS["latent_batched_decode"]
     log(f"case latent_batched_decode B={wl.B} H={wl.H} S={wl.S}")
     d = latent_device_inputs(wl, "cuda", seed=0)
     out = _gpu(d, wl.past_len)
     assert torch.isfinite(out).all().item()
-    rng = np.random.default_rng(1)
-    picks = {(0, 0), (wl.B - 1, wl.H - 1)}
-    while len(picks) < 10:
-        picks.add((int(rng.integers(wl.B)), int(rng.integers(wl.H))))
-    picks = sorted(picks)
+    picks = sorted(spread_pairs(wl.B, wl.H, 64, seed=1))
     w = to_host_bits(d["w_kv_b"])
     got, ref = [], []
     for b, h in picks:

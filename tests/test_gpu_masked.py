@@ -178,7 +178,8 @@ def test_bool_mask_is_accepted():
 def test_full_size_workloads_sampled():
     """The benchmarked launches (left padding): a batched decode of 32
     sequences over 8192 positions and a prefill of 4 left-padded 4096-token
-    prompts, 64 heads; the oracle checks sampled rows, each on its own keys."""
+    prompts, 64 heads; the oracle checks sampled rows, each on its own keys,
+    and for the prefill every query row of one head of each sequence."""
     import torch
     from seeded_inputs import MASKED_WORKLOADS, device_inputs, left_pad_mask, left_pads
     for name, wl in MASKED_WORKLOADS.items():
@@ -212,6 +213,14 @@ def test_full_size_workloads_sampled():
             got.append(to_host_f64(out[b, h, i]))
         assert_parity(np.stack(got), np.stack(ref), f"{name} sampled")
         assert torch.isfinite(out).all().item()
+        if wl.T > 1:  # every query row of one head per sequence, heads spread over the range
+            for b in range(wl.B):
+                h = (b * 21 + 5) % wl.H
+                sl = {k: to_host_bits(d[k][b:b + 1, h:h + 1]) for k in ("q_nope", "q_pe", "k_nope", "v")}
+                sl["k_pe"] = to_host_bits(d["k_pe"][b:b + 1])
+                ref_h = mla_attention_masked(sl["q_nope"], sl["q_pe"], sl["k_nope"], sl["k_pe"], sl["v"],
+                                             mask[b:b + 1], wl.past_len, wl.softmax_scale)
+                assert_parity(to_host_f64(out[b:b + 1, h:h + 1]), ref_h, f"{name} sequence {b} whole head {h}")
         del d, out
         torch.cuda.empty_cache()
 

@@ -6,7 +6,7 @@ import pytest
 from oracle import mla_attention, mla_attention_rows
 from seeded_inputs import SHARD_WORKLOADS, WORKLOADS, host_inputs, random_inputs
 
-from _gpu_util import assert_parity, log, to_host_bits, to_host_f64, upload
+from _gpu_util import assert_parity, log, spread_heads, to_host_bits, to_host_f64, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -193,7 +193,9 @@ def _sample_rows(B, H, T, n, seed):
                                       ("chunked_prefill", 2.0), ("chunked_prefill_h8", None)])
 def test_full_size_workloads_sampled(name, std):
     """Full-size launch as benchmarked (and one GPU's 8-head share of the
-    chunked prefill); the oracle checks sampled rows."""
+    chunked prefill); the oracle checks sampled rows, then every query row of
+    four heads spread over the head range (a head's tiles run on one XCD, in
+    the order the kernel deals them)."""
     import torch
     wl = WORKLOADS[name] if name in WORKLOADS else SHARD_WORKLOADS[name]
     log(f"case full {name} std={std or wl.std} B={wl.B} H={wl.H} T={wl.T} P={wl.past_len}")
@@ -206,6 +208,10 @@ def test_full_size_workloads_sampled(name, std):
                              wl.softmax_scale, rows)
     assert_parity(got, ref, f"{name} sampled")
     assert torch.isfinite(out).all().item()
+    for h in spread_heads(wl.H):
+        ref = mla_attention(x["q_nope"][:, h:h + 1], x["q_pe"][:, h:h + 1], x["k_nope"][:, h:h + 1], x["k_pe"],
+                            x["v"][:, h:h + 1], wl.past_len, wl.softmax_scale)
+        assert_parity(to_host_f64(out[:, h:h + 1]), ref, f"{name} whole head {h}")
 
 
 def test_split_prefill_graph_replays():

@@ -177,7 +177,8 @@ def _sample_rows(tq, H, n, seed):
 def test_full_size_workload_sampled():
     """The benchmarked launch (8 chunked prefills of mixed lengths, 64 heads,
     2048 x 16384 slices); the oracle checks sampled rows of each sequence on
-    its own keys only, and every padded row must be zero."""
+    its own keys only and every query row of one head per sequence, and every
+    padded row must be zero."""
     import torch
     wl = VARLEN_PREFILL_WORKLOADS["varlen_prefill"]
     tq, pp = varlen_prefill_lens(wl.B, wl.max_q, wl.max_kv, seed=0)
@@ -203,6 +204,16 @@ def test_full_size_workload_sampled():
         for k, (n, _) in enumerate(items):
             ref[n] = r[k]
     assert_parity(got, ref, "varlen_prefill sampled")
+    # every query row of one head of each sequence, heads spread over the range
+    for b in range(wl.B):
+        h = (b * 21 + 5) % wl.H
+        T_b, P_b = int(tq[b]), int(pp[b])
+        sl = {k: to_host_bits(d[k][b:b + 1, h:h + 1, :T_b]) for k in ("q_nope", "q_pe")}
+        sl.update({k: to_host_bits(d[k][b:b + 1, h:h + 1, :T_b + P_b]) for k in ("k_nope", "v")})
+        sl["k_pe"] = to_host_bits(d["k_pe"][b:b + 1, :, :T_b + P_b])
+        ref_h = mla_prefill_varlen(sl["q_nope"], sl["q_pe"], sl["k_nope"], sl["k_pe"], sl["v"], np.array([T_b]),
+                                   np.array([P_b]), wl.softmax_scale)
+        assert_parity(to_host_f64(out[b:b + 1, h:h + 1, :T_b]), ref_h, f"varlen_prefill sequence {b} head {h}")
     for b in range(wl.B):
         assert not torch.any(out[b, :, int(tq[b]):] != 0).item(), b
     assert torch.isfinite(out).all().item()
