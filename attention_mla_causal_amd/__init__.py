@@ -43,6 +43,7 @@ SIGNATURES = {
     "mla_attn_decode_masked": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "mla_attn_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _F32, _VP]),
+    "mla_attn_decode_noalloc": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_attn_decode_varlen_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "mla_attn_decode_varlen": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32, _I32, _I32, _I32, _F32, _VP]),
     "mla_attn_decode_paged_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
@@ -339,6 +340,29 @@ def mla_attn_decode(q_nope, q_pe, k_nope, k_pe, v, past_len: int, softmax_scale:
         out.data_ptr(), workspace.data_ptr(), ws_bytes, B, H, S, int(past_len),
         float(softmax_scale), _stream_handle(q_nope.device))
     _raise_for(st, "mla_attn_decode")
+    return out
+
+
+def mla_attn_decode_noalloc(q_nope, q_pe, k_nope, k_pe, v, past_len: int, softmax_scale: float, out=None):
+    """mla_attn_decode without a workspace: the library keeps the split
+    partials in its own per-device scratch array, so the C call allocates
+    nothing (pass `out` to keep this wrapper from allocating it). Calls that
+    may overlap on one device share that array and must be ordered."""
+    import torch
+
+    B, H, T, S = _shapes(q_nope, q_pe, k_nope, k_pe, v)
+    if T != 1:
+        raise ValueError(f"decode takes one query per sequence, got T={T}")
+    if out is None:
+        out = torch.empty((B, H, 1, V_HEAD_DIM), dtype=torch.bfloat16, device=q_nope.device)
+    else:
+        _check_tensor(out, "out")
+        if tuple(out.shape) != (B, H, 1, V_HEAD_DIM) or out.device != q_nope.device:
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, 1, V_HEAD_DIM)}")
+    st = _lib.mla_attn_decode_noalloc(
+        q_nope.data_ptr(), q_pe.data_ptr(), k_nope.data_ptr(), k_pe.data_ptr(), v.data_ptr(), out.data_ptr(),
+        B, H, S, int(past_len), float(softmax_scale), _stream_handle(q_nope.device))
+    _raise_for(st, "mla_attn_decode_noalloc")
     return out
 
 

@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/mla_attn.h"
 #include "mla_host_checks.h"
@@ -50,6 +51,43 @@ int device_xcds() {
     n = x;
   }
   return n;
+}
+
+// ---- allocation-free decode: its scratch lives in the library
+//
+// mla_attn_decode_noalloc keeps the split partials and completion flags of
+// mla_attn_decode in this file-scope array instead of a caller's workspace.
+// Each device that loads the library holds its own copy until the process
+// ends. In host code `scratch` names a host-side stand-in, not device memory:
+// its device address is looked up once per device (with that device current)
+// by hipGetSymbolAddress and only that address is ever passed to a kernel.
+// Every plan_decode workspace fits: B*H*nsplit stays below 768 when the keys
+// are split (nsplit <= ceil(512 / (B*H)) for B*H < 256, no split above), i.e.
+// at most 410,112 bytes.
+constexpr size_t kScratchBytes = MLA_DECODE_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes >= 410112, "the largest plan_decode workspace must fit");
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device, or nullptr (with the
+// HIP error in *err) when it cannot be looked up.
+void* scratch_on_current_device(hipError_t* err) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
 }
 
 }  // namespace
@@ -287,6 +325,39 @@ mla_status mla_attn_decode(const void* q_nope, const void* q_pe, const void* k_n
   if (r.empty) return MLA_OK;
   return launch_decode_call("mla_attn_decode", q_nope, q_pe, k_nope, k_pe, v, DecodeExtras{},
                             out, workspace, plan, B, H, S, S, softmax_scale, stream);
+}
+
+mla_status mla_attn_decode_noalloc(const void* q_nope, const void* q_pe, const void* k_nope,
+                                   const void* k_pe, const void* v, void* out, int32_t B, int32_t H,
+                                   int32_t S, int32_t past_len, float softmax_scale, void* stream) {
+  const char* where = "mla_attn_decode_noalloc";
+  mla::DecodePlan plan;
+  // Every check runs before any HIP call, the scratch's device address
+  // included: the checks see a stand-in workspace of the scratch's size (a
+  // non-null, aligned value that is never dereferenced), so a plan larger
+  // than the scratch is MLA_ERR_WORKSPACE.
+  void* const stand_in = reinterpret_cast<void*>(uintptr_t(1) << 20);
+  const mla::CheckResult r = mla::check_decode(q_nope, q_pe, k_nope, k_pe, v, out, stand_in, kScratchBytes,
+                                               B, H, S, past_len, softmax_scale, &plan);
+  if (r.status != MLA_OK) {
+    if (r.status == MLA_ERR_WORKSPACE) {
+      char msg[200];
+      std::snprintf(msg, sizeof(msg), "needs %zu bytes of scratch, more than the library's %zu",
+                    mla::plan_decode(B, H, S).workspace_bytes, kScratchBytes);
+      set_error(where, msg);
+      return MLA_ERR_WORKSPACE;
+    }
+    return report(where, r);
+  }
+  if (r.empty) return MLA_OK;
+  void* ws = nullptr;
+  if (plan.workspace_bytes > 0) {
+    hipError_t e = hipSuccess;
+    ws = scratch_on_current_device(&e);
+    if (ws == nullptr) return device_error(where, e);
+  }
+  return launch_decode_call(where, q_nope, q_pe, k_nope, k_pe, v, DecodeExtras{}, out, ws, plan, B, H, S, S,
+                            softmax_scale, stream);
 }
 
 mla_status mla_attn_decode_rope(const void* q_nope, const void* q_pe, const void* k_nope,

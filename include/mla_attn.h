@@ -203,6 +203,29 @@ mla_status mla_attn_decode(const void* q_nope, const void* q_pe,
                            float softmax_scale, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * mla_attn_decode without a workspace argument. The split partials and
+ * completion flags live in a library-owned array of
+ * MLA_DECODE_NOALLOC_SCRATCH_BYTES bytes on each device (reserved with the
+ * library's code on that device, kept until the process ends); the call
+ * allocates nothing. Every shape mla_attn_decode accepts fits (its workspace
+ * never exceeds 410,112 bytes); a plan larger than the array would be
+ * MLA_ERR_WORKSPACE. All calls on one device share that array: calls that
+ * can overlap on one device (on different streams, or graphs replayed
+ * concurrently) race, and the caller must order them. The array's contents
+ * on entry do not matter (each call's completion flags carry the call's tag
+ * and the merging workgroup clears them). Arguments, result and other errors
+ * as for mla_attn_decode.
+ */
+#define MLA_DECODE_NOALLOC_SCRATCH_BYTES (512u * 1024u)
+mla_status mla_attn_decode_noalloc(const void* q_nope, const void* q_pe,
+                                   const void* k_nope, const void* k_pe,
+                                   const void* v, void* out,
+                                   int32_t B, int32_t H, int32_t S, int32_t past_len,
+                                   float softmax_scale, void* stream);
+
+/*
  * mla_attn_decode under the caller's 2D padding mask ("Causal mask" page,
  * "Construct causal mask"): the new query of sequence b sees key j iff
  * attn_mask[b * S + j] != 0 (the causal mask hides no key from the last

@@ -37,6 +37,12 @@ int main(void) {
          "masked prefill without a mask");
   expect(mla_attn_decode(p, p, p, p, p, p, NULL, 0, 1, 64, 1001, 1000, sc, NULL) ==
              MLA_ERR_WORKSPACE, "decode without its workspace");
+  expect(mla_attn_decode_noalloc(p, p, p, p, p, NULL, 1, 64, 1001, 1000, sc, NULL) == MLA_ERR_NULL,
+         "allocation-free decode without out");
+  expect(mla_attn_decode_noalloc(p, p, p, p, p, p, 1, 64, 1001, 999, sc, NULL) == MLA_ERR_SHAPE,
+         "allocation-free decode S != past_len + 1");
+  expect(MLA_DECODE_NOALLOC_SCRATCH_BYTES >= mla_attn_decode_workspace_bytes(1, 255, 257),
+         "the allocation-free scratch holds the largest decode workspace");
   expect(mla_attn_decode_masked(p, p, p, p, p, mask, p, p, 1 << 20, 1, 64, 1001, 1000, 1.0f / 0.0f, NULL) ==
              MLA_ERR_SCALE, "masked decode with an infinite scale");
   expect(mla_attn_decode_varlen(p, p, p, p, p, lens, p, p, 1 << 20, 1, 64, 1000, 1001, sc, NULL) ==

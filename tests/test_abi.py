@@ -31,7 +31,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert _declared_functions() == sorted([
-        "mla_attn_decode", "mla_attn_decode_workspace_bytes", "mla_attn_prefill",
+        "mla_attn_decode", "mla_attn_decode_workspace_bytes", "mla_attn_prefill", "mla_attn_decode_noalloc",
         "mla_attn_decode_latent", "mla_attn_decode_latent_workspace_bytes",
         "mla_attn_decode_varlen", "mla_attn_decode_varlen_workspace_bytes",
         "mla_attn_decode_paged", "mla_attn_decode_paged_workspace_bytes",
