@@ -7,7 +7,8 @@
 // token's key and value may be appended by the call itself (the cache update
 // the "Similarities" page runs before attending). A second instantiation
 // takes the caller's general 2D padding mask ([B, S] bytes, nonzero keeps):
-// it fetches each trip's mask bytes a trip ahead and loads only kept rows. A
+// it takes the mask bytes of eight trips at a time (one group ahead) as ballot
+// bits and loads only kept rows. A
 // third fuses the rotary prologue: the new token's query (and appended key)
 // turns at its position in registers, from a cos/sin table, before scoring.
 //
@@ -260,24 +261,32 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     const int64_t kb = base0 + (int64_t)KEYS_PER_TRIP * lane;
     if (kb < s1) blk_lane = (int32_t)block_of(kb);
   }
-  // 2D mask: the mask bytes of each trip's keys are fetched one trip ahead
-  // (the first trip's here, before the loop), so the rows of hidden keys are
-  // never fetched and trips whose keys are all hidden are skipped.
-  const uint8_t* mrow = MASKED ? a.key_mask + (int64_t)b * a.S : nullptr;
-  uint8_t pre[KEYS_PER_LANE];
-  if (MASKED) {
+  // 2D mask: each wave takes the mask bytes of its keys eight trips (256
+  // keys) at a time, the next group's one group ahead: lane l holds the four
+  // bytes of trip l / 8 at offset 4 (l % 8) of the wave's 32 keys. Four
+  // ballots (one per byte position) turn them into one bit per key: key
+  // 4u + qq of trip t is bit 8t + u of ballot qq. A trip whose keys are all
+  // hidden then costs a few scalar ops and no memory round trip, and rows of
+  // hidden keys are never fetched. Bytes past this split's keys read as 0
+  // (buffer range check), i.e. hidden.
+  __amdgpu_buffer_rsrc_t mrs;
+  uint32_t mb_cur[4] = {0, 0, 0, 0}, mb_next[4] = {0, 0, 0, 0};
+  uint64_t m_any = 0, m_lane = 0;  // the current group's bits: any key kept per slot, this lane's keys
+  auto load_group = [&](int g, uint32_t (&mb)[4]) {
+    const int off = (int)(base0 + (int64_t)(8 * g + (lane >> 3)) * KEYS_PER_TRIP + 4 * (lane & 7));
 #pragma unroll
-    for (int u = 0; u < KEYS_PER_LANE; ++u) {
-      const int64_t key = base0 + 4 * u + qq;
-      pre[u] = key < s1 ? mrow[key] : 0;
-    }
+    for (int p = 0; p < 4; ++p) mb[p] = __builtin_amdgcn_raw_buffer_load_b8(mrs, off + p, 0, 0);
+  };
+  if (MASKED) {
+    mrs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.key_mask + (int64_t)b * a.S), (short)0,
+                                            s1 > 0 ? (int)s1 : 0, 0x00020000);
+    load_group(0, mb_cur);
   }
   int trip = 0;
   for (int64_t base = base0; base < s1; base += KEYS_PER_TRIP, ++trip) {
     u32x4 kn[KEYS_PER_LANE], vv[KEYS_PER_LANE];
     u32x2 kp[KEYS_PER_LANE];
     bool ok[KEYS_PER_LANE];
-    uint8_t keep[KEYS_PER_LANE];
     const uint16_t* kn_t;  // rows base .. base+31 are consecutive
     const uint16_t* v_t;
     const uint16_t* kp_t;
@@ -293,18 +302,22 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
       kp_t = kp_g + base * DR;
     }
     if (MASKED) {
-      bool any = false;
+      if ((trip & 7) == 0) {  // a new group of eight trips: its bits, and the next group's bytes
+        if (trip > 0) {
 #pragma unroll
-      for (int u = 0; u < KEYS_PER_LANE; ++u) {
-        const int64_t key = base + 4 * u + qq;
-        keep[u] = pre[u];
-        ok[u] = key < s1 && keep[u] != 0;
-        any = any || ok[u];
-        const int64_t next = key + KEYS_PER_TRIP;
-        pre[u] = next < s1 ? mrow[next] : 0;
+          for (int p = 0; p < 4; ++p) mb_cur[p] = mb_next[p];
+        }
+        load_group((trip >> 3) + 1, mb_next);
+        const uint64_t m0 = __ballot(mb_cur[0] != 0), m1 = __ballot(mb_cur[1] != 0);
+        const uint64_t m2 = __ballot(mb_cur[2] != 0), m3 = __ballot(mb_cur[3] != 0);
+        m_any = m0 | m1 | m2 | m3;
+        m_lane = (qq & 2) ? ((qq & 1) ? m3 : m2) : ((qq & 1) ? m1 : m0);
       }
+      const int sh = 8 * (trip & 7);
       // a trip whose keys are all hidden is skipped whole
-      if (!__any(any)) continue;
+      if (((m_any >> sh) & 0xffu) == 0) continue;
+#pragma unroll
+      for (int u = 0; u < KEYS_PER_LANE; ++u) ok[u] = ((m_lane >> (sh + u)) & 1u) != 0;
     }
 #pragma unroll
     for (int u = 0; u < KEYS_PER_LANE; ++u) {
@@ -319,15 +332,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
         vv[u] = u32x4{0, 0, 0, 0};
       }
     }
-    if (MASKED) {
-      // a hidden key scores -inf below; its value row is cleared so that
-      // whatever it holds (NaN included) cannot reach the output
-#pragma unroll
-      for (int u = 0; u < KEYS_PER_LANE; ++u) {
-        ok[u] = ok[u] && keep[u] != 0;
-        if (!ok[u]) vv[u] = u32x4{0, 0, 0, 0};
-      }
-    }
+    // (a hidden key was never loaded: it scores -inf below and its value
+    // registers hold 0, so whatever its rows hold, NaN included, cannot reach
+    // the output)
     if (kLateQuery) {
       u32x4 w = qw;
       u32x2 wp = qpw;
