@@ -71,14 +71,24 @@ inline DecodePlan plan_decode(int64_t B, int64_t H, int64_t S) {
 // Variable-length decode: lengths differ, so a (b, h) with many keys would
 // keep its workgroup running long after the short ones finished. Splitting
 // every (b, h) into pieces of at most this many keys bounds that tail (the
-// pieces past a short sequence's end find no key and finish at once).
+// pieces past a short sequence's end find no key and finish at once). With
+// many (b, h) pairs the GPU is full without splitting and the pieces' fixed
+// costs (partials, completion flags, the merge; for a 2D mask a round trip
+// for the mask bytes per piece) outweigh the tail they even out: at 32 x 64
+// pairs over 8192 keys one workgroup per pair measured 0.633 against 0.648
+// ms (variable lengths), 0.660 against 0.669 (paged) and 0.640 against 0.725
+// (left-padding mask), so from kDecodeVarlenWidePairs pairs on the pieces
+// are kDecodeVarlenWideKeysPerSplit keys long.
 constexpr int64_t kDecodeVarlenKeysPerSplit = 1024;
+constexpr int64_t kDecodeVarlenWidePairs = 2048;  // 8 workgroups per CU on 256 CUs
+constexpr int64_t kDecodeVarlenWideKeysPerSplit = 8192;
 constexpr int64_t kDecodeMaxFusedSplits = 64;
 
 inline DecodePlan plan_decode_varlen(int64_t B, int64_t H, int64_t max_len) {
   DecodePlan p = plan_decode(B, H, max_len);
   if (B <= 0 || H <= 0 || max_len <= 0) return p;
-  int64_t want = (max_len + kDecodeVarlenKeysPerSplit - 1) / kDecodeVarlenKeysPerSplit;
+  const int64_t piece = B * H >= kDecodeVarlenWidePairs ? kDecodeVarlenWideKeysPerSplit : kDecodeVarlenKeysPerSplit;
+  int64_t want = (max_len + piece - 1) / piece;
   if (want > kDecodeMaxFusedSplits) want = kDecodeMaxFusedSplits;
   if (want <= p.nsplit) return p;
   int64_t kps = (max_len + want - 1) / want;

@@ -105,7 +105,8 @@ int main() {
     CheckResult r = check_decode(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 64, 5, 4, sc, &pl);
     EXPECT(r.status == MLA_OK && r.empty);
   }
-  // variable-length decode: pieces of at most 1024 keys, at most 64 per (b, h)
+  // variable-length decode: pieces of at most 1024 keys (8192 from 2048 (b, h)
+  // pairs on), at most 64 per (b, h)
   {
     for (long long M : {0LL, 1LL, 1000LL, 1024LL, 1025LL, 4096LL, 8192LL, 65536LL, 100000LL}) {
       for (long long bh : {1LL, 48LL, 2048LL}) {
@@ -116,19 +117,22 @@ int main() {
           EXPECT(pl.keys_per_split % kDecodeKeysPerTrip == 0);
           EXPECT(pl.keys_per_split * pl.nsplit >= M);
           EXPECT(pl.keys_per_split * (pl.nsplit - 1) < M);
-          EXPECT(pl.keys_per_split <= 1024 || M > 64 * 1024 || pl.nsplit == base.nsplit);
+          const long long piece = bh >= kDecodeVarlenWidePairs ? kDecodeVarlenWideKeysPerSplit : kDecodeVarlenKeysPerSplit;
+          EXPECT(pl.keys_per_split <= piece || M > 64 * piece || pl.nsplit == base.nsplit);
         }
         EXPECT(pl.workspace_bytes == (pl.nsplit > 1 ? pl.ws_o_bytes + pl.ws_ml_bytes + pl.ws_flag_bytes : 0));
       }
     }
-    EXPECT(plan_decode_varlen(32, 64, 8192).nsplit == 8);
+    EXPECT(plan_decode_varlen(32, 64, 8192).nsplit == 1);    // 2048 pairs: one workgroup each
+    EXPECT(plan_decode_varlen(32, 64, 16384).nsplit == 2);
+    EXPECT(plan_decode_varlen(16, 64, 8192).nsplit == 8);    // 1024 pairs: pieces of 1024 keys
     EXPECT(plan_decode_varlen(32, 64, 1024).nsplit == 1);
     DecodePlan pl;
-    const size_t need = plan_decode_varlen(32, 64, 8192).workspace_bytes;
-    EXPECT(check_decode_varlen(p, p, p, p, p, p, p, p, need, 32, 64, 8192, 8192, sc, &pl).status == MLA_OK);
+    const size_t need = plan_decode_varlen(16, 64, 8192).workspace_bytes;
+    EXPECT(check_decode_varlen(p, p, p, p, p, p, p, p, need, 16, 64, 8192, 8192, sc, &pl).status == MLA_OK);
     EXPECT(pl.nsplit == 8);
-    EXPECT(check_decode_varlen(p, p, p, p, p, p, p, p, need, 32, 64, 8192, 8193, sc, &pl).status == MLA_ERR_SHAPE);
-    EXPECT(check_decode_varlen(p, p, p, p, p, p, p, p, need - 1, 32, 64, 8192, 8192, sc, &pl).status == MLA_ERR_WORKSPACE);
+    EXPECT(check_decode_varlen(p, p, p, p, p, p, p, p, need, 16, 64, 8192, 8193, sc, &pl).status == MLA_ERR_SHAPE);
+    EXPECT(check_decode_varlen(p, p, p, p, p, p, p, p, need - 1, 16, 64, 8192, 8192, sc, &pl).status == MLA_ERR_WORKSPACE);
     EXPECT(check_decode_varlen(p, p, nullptr, nullptr, nullptr, p, p, nullptr, 0, 2, 8, 0, 0, sc, &pl).status == MLA_OK);
     EXPECT(check_decode_varlen(p, p, nullptr, p, p, p, p, nullptr, 0, 2, 8, 16, 0, sc, &pl).status == MLA_ERR_NULL);
   }

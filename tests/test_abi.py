@@ -150,9 +150,12 @@ def _varlen(lib, ptrs, ws, ws_bytes, B, H, L, M, scale=SC):
 def test_varlen_decode_errors(lib):
     need = lib.mla_attn_decode_varlen_workspace_bytes(1, 64, 1001)
     assert need > 0 and need == lib.mla_attn_decode_workspace_bytes(1, 64, 1001)
-    # B*H fills the chip, but long sequences still split into pieces of <= 1024 keys
-    assert lib.mla_attn_decode_workspace_bytes(32, 64, 8192) == 0
-    assert lib.mla_attn_decode_varlen_workspace_bytes(32, 64, 8192) >= 32 * 64 * 8 * (128 + 4) * 4
+    # B*H fills the chip, but long sequences still split into pieces of <= 1024
+    # keys; from 2048 (b, h) pairs on, of <= 8192 keys
+    assert lib.mla_attn_decode_workspace_bytes(16, 64, 8192) == 0
+    assert lib.mla_attn_decode_varlen_workspace_bytes(16, 64, 8192) >= 16 * 64 * 8 * (128 + 4) * 4
+    assert lib.mla_attn_decode_varlen_workspace_bytes(32, 64, 8192) == 0
+    assert lib.mla_attn_decode_varlen_workspace_bytes(32, 64, 16384) >= 32 * 64 * 2 * (128 + 4) * 4
     assert lib.mla_attn_decode_varlen_workspace_bytes(32, 64, 1024) == 0
     ok = [ALIGNED] * 7
     assert _varlen(lib, ok, ALIGNED, need, 1, 64, 1000, 1001) == 2        # max_seq_len > cache
@@ -286,10 +289,10 @@ def test_masked_errors(lib):
     need = lib.mla_attn_decode_varlen_workspace_bytes(1, 64, 1001)
     assert dec(ok, ALIGNED, need, 1, 64, 1001, 999) == 2
     # the variable-length split plan: B*H fills the GPU, yet 8192 keys split in pieces
-    big = lib.mla_attn_decode_varlen_workspace_bytes(32, 64, 8192)
-    assert big > 0 and lib.mla_attn_decode_workspace_bytes(32, 64, 8192) == 0
-    assert dec(ok, ALIGNED, big - 1, 32, 64, 8192, 8191) == 5
-    assert dec(ok, MISALIGNED, big, 32, 64, 8192, 8191) == 3
+    big = lib.mla_attn_decode_varlen_workspace_bytes(16, 64, 8192)
+    assert big > 0 and lib.mla_attn_decode_workspace_bytes(16, 64, 8192) == 0
+    assert dec(ok, ALIGNED, big - 1, 16, 64, 8192, 8191) == 5
+    assert dec(ok, MISALIGNED, big, 16, 64, 8192, 8191) == 3
     assert dec(mask_none, ALIGNED, need, 1, 64, 1001, 1000) == 1
     assert dec(ok, None, need, 1, 64, 1001, 1000) == 5
     assert dec(odd, ALIGNED, need, 1, 64, 1001, 1000, float("inf")) == 4
