@@ -552,7 +552,6 @@ mla_status mla_attn_decode_latent(const void* q_nope, const void* q_pe, const vo
   a.qt = reinterpret_cast<uint16_t*>(ws);
   a.po = reinterpret_cast<float*>(ws + plan.qt_bytes);
   a.pml = reinterpret_cast<float*>(ws + plan.qt_bytes + plan.po_bytes);
-  a.olat = reinterpret_cast<float*>(ws + plan.qt_bytes + plan.po_bytes + plan.pml_bytes);
   a.B = B;
   a.H = H;
   a.S = S;

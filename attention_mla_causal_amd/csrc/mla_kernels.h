@@ -82,7 +82,6 @@ struct LatentArgs {
   uint16_t* qt;            // workspace: [B,H,576] absorbed queries joined with q_pe (bf16)
   float* po;               // workspace: [B,nsplit,H,512] partial latent outputs
   float* pml;              // workspace: [B,nsplit,H,2] partial (max, sum)
-  float* olat;             // workspace: [B,H,512] merged latent outputs
   int32_t B, H, S;
   int32_t nsplit, keys_per_split;
   float scale_log2;

@@ -14,7 +14,7 @@
 // which equals attention over the decompressed keys and values up to rounding.
 // A key costs 1152 bytes (latent + rotary key) instead of 64 heads x 512.
 //
-// Four kernels on the caller's stream:
+// Three kernels on the caller's stream:
 //  1. absorb: q~ for every (batch, head) on MFMA (W_k read transposed out of
 //     LDS), rounded to bf16, joined with q_pe into a 576-dim row (workspace).
 //  2. attention: one workgroup per (batch, key split), four waves. 32-key
@@ -28,9 +28,9 @@
 //     one tile behind the scores, its C^T fragments read with
 //     ds_read_b64_tr_b16 in the key order the score accumulator leaves P in.
 //     Each split writes an fp32 partial (o~, max, sum).
-//  3. merge: log-sum-exp over the splits of each (batch, head) -> o~ (fp32).
-//  4. up-projection: out = W_v o~ on MFMA (o~ split into two bf16 halves),
-//     rounded to bf16.
+//  3. merge + up-projection: log-sum-exp over the splits of each (batch,
+//     head) -> o~ (fp32, in LDS), then out = W_v o~ on MFMA (o~ split into two
+//     bf16 halves), rounded to bf16.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -82,8 +82,8 @@ __device__ __forceinline__ void wait_vmem_keep() {
 
 // ---- 1. absorb: q~[b,h,e] = sum_d q_nope[b,h,d] * W[256h + d, e]; q~[b,h,512+i] = q_pe[b,h,i]
 // As a product per head, Q~_h^T [512 x B] = W_k[h]^T [512 x 128] . Q_h^T [128 x B],
-// on v_mfma_f32_16x16x32_bf16. Workgroup: one head, 64 latent dims; wave w
-// owns the 16 dims e0 + 16w and runs over the batch 16 rows at a time. W_k is
+// on v_mfma_f32_16x16x32_bf16. Workgroup: 16 sequences, one head, 64 latent
+// dims; wave w owns the 16 dims e0 + 16w for the 16 sequences. W_k is
 // stored with e contiguous, so the workgroup stages its [128 d x 64 e] block
 // in LDS and reads it back transposed (ds_read_b64_tr_b16): lane (g, j) then
 // holds dim e0 + 16w + j at d = 32ks + 4g + 0..3 and 32ks + 16 + 4g + 0..3,
@@ -91,7 +91,12 @@ __device__ __forceinline__ void wait_vmem_keep() {
 constexpr int ABS_ROW = 144;  // bytes per staged W row: 128 + 16 keeps the 4 rows a read touches apart
 __global__ __launch_bounds__(256) void latent_absorb_kernel(LatentArgs a) {
   __shared__ __attribute__((aligned(16))) char wt[DN * ABS_ROW];
-  const int h = blockIdx.x >> 3, chunk = blockIdx.x & 7;
+  // workgroup: (16 sequences, head, 64 latent dims); the 16-sequence groups of
+  // one (head, dims) block sit 8 * H workgroups apart, on one XCD, and share
+  // its weight block in L2
+  const int chunk = blockIdx.x & 7, h = (blockIdx.x >> 3) % a.H;
+  const int bq0 = (blockIdx.x >> 3) / a.H * 16;
+  const int bq1 = (bq0 + 16 < a.B) ? bq0 + 16 : a.B;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, j = lane & 15;
   const int e0 = chunk * 64;
@@ -110,13 +115,13 @@ __global__ __launch_bounds__(256) void latent_absorb_kernel(LatentArgs a) {
   const uint32_t q_xor = cl2_in < 0.0f ? 0x80008000u : 0u;
   const float q_mul = cl2_in == 0.0f ? 0.0f : (cl2_in < 0.0f ? -1.0f : 1.0f);
   if (chunk == 0) {  // the rotary query goes through unchanged (but for that sign)
-    for (int c = tid; c < a.B * 8; c += 256) {
+    for (int c = bq0 * 8 + tid; c < bq1 * 8; c += 256) {
       const int64_t bh = (int64_t)(c >> 3) * a.H + h;
       *reinterpret_cast<u32x4*>(a.qt + bh * KW + R + (c & 7) * 8) =
           (*reinterpret_cast<const u32x4*>(a.q_pe + bh * DR + (c & 7) * 8) & q_and) ^ q_xor;
     }
   }
-  // query fragments of the first 16 batches load while W lands in LDS
+  // the query fragments load while W lands in LDS
   auto load_q = [&](int b0, u32x4* qv) {
     const int b = b0 + j;
     const uint16_t* q = a.q_nope + ((int64_t)(b < a.B ? b : 0) * a.H + h) * DN + 4 * g;
@@ -131,7 +136,7 @@ __global__ __launch_bounds__(256) void latent_absorb_kernel(LatentArgs a) {
     }
   };
   u32x4 qv[DN / 32];
-  load_q(0, qv);
+  load_q(bq0, qv);
   __syncthreads();
   bf16x8 wf[DN / 32];
 #pragma unroll
@@ -141,11 +146,11 @@ __global__ __launch_bounds__(256) void latent_absorb_kernel(LatentArgs a) {
     const bf16x4 hi = lds_tr_read(p + 16 * ABS_ROW);
     wf[ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
-  for (int b0 = 0; b0 < a.B; b0 += 16) {
+  {
+    const int b0 = bq0;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < DN / 32; ++ks) acc = mfma16(wf[ks], __builtin_bit_cast(bf16x8, qv[ks]), acc);
-    if (b0 + 16 < a.B) load_q(b0 + 16, qv);
     // acc[r] = q~[b][e0 + 16w + 4g + r]; RNE rounding is symmetric, so
     // bf16(-x) = -bf16(x) and the sign can be applied before rounding
 #pragma unroll
@@ -223,7 +228,18 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
   __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2][NWAVE][64];  // [phase parity][head group][lane]
   __shared__ float abuf[2][NWAVE * 16];                               // rescale factor per head
 
-  const int b = blockIdx.x / a.nsplit, split = blockIdx.x % a.nsplit;
+  // Workgroup w runs on XCD w % 8. With B a multiple of 8, XCD x takes every
+  // split of sequences x, x + 8, ..., so a sequence's splits share one L2 (its
+  // absorbed queries are fetched from HBM once per sequence, not per split).
+  int b, split;
+  if (a.B % 8 == 0) {
+    const int slot = blockIdx.x >> 3;
+    b = (blockIdx.x & 7) + 8 * (slot / a.nsplit);
+    split = slot % a.nsplit;
+  } else {
+    b = blockIdx.x / a.nsplit;
+    split = blockIdx.x % a.nsplit;
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, j = lane & 15;
@@ -304,16 +320,12 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     copy_tile(p + 2, fill);
     bf16x8 pin[NWAVE];
+    float al[NWAVE];
     if (do_out) {
-      // rescale by the factors of tile p-1 before its contribution lands
 #pragma unroll
       for (int hg = 0; hg < NWAVE; ++hg) {
-        const float al = abuf[(p - 1) & 1][16 * hg + j];
+        al[hg] = abuf[(p - 1) & 1][16 * hg + j];
         pin[hg] = pbuf[(p - 1) & 1][hg][lane];
-        if (__any(al != 1.0f)) {
-#pragma unroll
-          for (int d = 0; d < NDTW; ++d) o[hg * NDTW + d] *= al;
-        }
       }
     }
     if (do_scores) {
@@ -365,8 +377,10 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
         const bf16x4 lo = lds_tr_read(pp);
         const bf16x4 hi = lds_tr_read(pp + 16 * 64);
         const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        // rescaled by tile p-1's factors as its contribution lands (a factor
+        // of 1 leaves the accumulator unchanged)
 #pragma unroll
-        for (int hg = 0; hg < NWAVE; ++hg) o[hg * NDTW + d] = mfma16(va, pin[hg], o[hg * NDTW + d]);
+        for (int hg = 0; hg < NWAVE; ++hg) o[hg * NDTW + d] = mfma16(va, pin[hg], o[hg * NDTW + d] * al[hg]);
       }
     }
   };
@@ -394,14 +408,29 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
   wait_vmem_keep<0>();  // (copies past the end are never read; let them land before exit)
 
   // ---- partial of this split: o~ (unnormalised) for this wave's dims; max and
-  // sum of the wave's own heads
+  // sum of the wave's own heads. A lane holds 4 dims of one head per
+  // accumulator, so stored directly each instruction would touch 16 rows; the
+  // accumulators are turned into rows in LDS first (head group hg in tile
+  // buffer hg, rows of 512 dims 2064 bytes apart, so each 16-lane group of a
+  // write meets 16 distinct banks), then every wave stores whole rows.
+  __syncthreads();  // every wave is done with the tiles
+  auto stage = [&](int hg) -> char* { return hg == 0 ? tile0 : hg == 1 ? tile1 : hg == 2 ? tile2 : tile3; };
+  constexpr int ROWB = R * 4 + 16;
+#pragma unroll
+  for (int hg = 0; hg < NWAVE; ++hg)
+#pragma unroll
+    for (int d = 0; d < NDTW; ++d)
+      *reinterpret_cast<f32x4*>(stage(hg) + j * ROWB + (128 * wave + 16 * d + 4 * g) * 4) = o[hg * NDTW + d];
+  __syncthreads();
   const int64_t row0 = ((int64_t)b * a.nsplit + split) * H;
 #pragma unroll
-  for (int hg = 0; hg < NWAVE; ++hg) {
-    if (16 * hg + j < H) {
-      float* po = a.po + (row0 + 16 * hg + j) * R + 128 * wave + 4 * g;
-#pragma unroll
-      for (int d = 0; d < NDTW; ++d) *reinterpret_cast<f32x4*>(po + 16 * d) = o[hg * NDTW + d];
+  for (int k = 0; k < NWAVE * 16 * R / 4 / 256; ++k) {  // 32 stores of 16 bytes per thread
+    const int li = k * 256 + (int)threadIdx.x;
+    const int hd = li >> 7, q = li & 127;  // head (hd >> 4 == k >> 3), 4-dim group
+    if (hd < H) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(stage(k >> 3) + (hd & 15) * ROWB + 16 * q);
+      // non-temporal: the partials are read once, by the next kernel
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(a.po + (row0 + hd) * R + 4 * q));
     }
   }
   float l_tot = l_run + __shfl_xor(l_run, 16);
@@ -413,109 +442,176 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
   }
 }
 
-// ---- 3. merge the splits of each (batch, head): o~ = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
-// Workgroup: one (batch, head); wave w sums splits w, w + 4, ..., lane l holds
-// dims 8l .. 8l + 7; the four wave sums meet in LDS.
-__global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
-  __shared__ __attribute__((aligned(16))) float part[4][R + 4];
-  const int bh = blockIdx.x;
-  const int b = bh / a.H, h = bh % a.H;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t row0 = (int64_t)b * a.nsplit * a.H + h;  // split s: row0 + s * H
-  float M = -INFINITY;
-  for (int s = lane; s < a.nsplit; s += 64) M = fmaxf(M, a.pml[2 * (row0 + (int64_t)s * a.H)]);
+// ---- 3. merge + up-projection, one launch:
+//   o~[b,h]    = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s   (M = max_s m_s)
+//   out[b,h,d] = sum_e W[256h + 128 + d, e] * o~[b,h,e]
+// Workgroup: one head, up to eight sequences, 128 / C of the head's output
+// dims, eight waves. First the waves merge the splits of the workgroup's
+// sequences (a sequence's splits are dealt over 8 / n of the waves, n its live
+// sequences rounded up to a power of two, so a lone sequence still has all
+// eight waves loading) and leave o~ in LDS. Then, as
+// Out_h^T [128 x 8] = W_v[h] [128 x 512] . O~_h^T [512 x 8] on
+// v_mfma_f32_16x16x32_bf16, wave w computes 16 output dims over 512 / C of
+// the contraction (C waves per 16 dims, their sums added in LDS). W_v's
+// contraction dim is contiguous, so its fragments load straight from HBM, at
+// the start, while the merge runs; o~ is fp32 and enters as two bf16 operands,
+// hi = bf16(x) and lo = bf16(x - hi), whose sum carries x to about 2^-17
+// relative. The host picks C so that about 256 workgroups run: with few
+// sequences the head's weight rows are spread over C workgroups (each merging
+// the same splits again, from L2) rather than loaded by one. Workgroups of one
+// head share one L2 (H a multiple of 8 puts them on one XCD).
+constexpr int OUT_BG = 8;     // sequences per workgroup (MFMA columns 8..15 stay zero)
+constexpr int OUT_WAVES = 8;
+constexpr int OROW = R + 4;   // floats per LDS row: 2064 bytes, so the 16-byte reads of
+                              // eight rows at one offset meet distinct banks
+template <int C>
+__global__ __launch_bounds__(512) void latent_out_kernel(LatentArgs a) {
+  static_assert(C == 1 || C == 2 || C == 4, "C divides the 8 waves and the 16 K-steps");
+  constexpr int TILES = OUT_WAVES / C;  // 16-dim output tiles per workgroup
+  constexpr int KS = R / 32 / C;        // K-steps per wave
+  __shared__ __attribute__((aligned(16))) float part[OUT_WAVES][OROW];
+  __shared__ float lpart[OUT_WAVES][2];
+  __shared__ __attribute__((aligned(16))) float orow[OUT_BG][OROW];
+  const int h = blockIdx.x % a.H, rest = blockIdx.x / a.H;
+  const int chunk = rest % C, b0 = (rest / C) * OUT_BG;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, j = lane & 15;
+
+  const int tile = wave % TILES, epart = wave / TILES;
+  const int d0 = chunk * (DV / C) + 16 * tile;
+  const uint16_t* wrow = a.w_kv_b + ((int64_t)h * KVB + DN + d0 + j) * R + 8 * g + 32 * KS * epart;
+  u32x4 wf[KS];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float L = 0.0f, O[8];
+  for (int ks = 0; ks < KS; ++ks) wf[ks] = *reinterpret_cast<const u32x4*>(wrow + 32 * ks);
+
+  // merge: wave w takes sequence slot w / wpb and splits s = w % wpb (mod wpb)
+  const int nb = (a.B - b0 < OUT_BG) ? a.B - b0 : OUT_BG;  // live sequences, >= 1
+  const int nbp = nb > 4 ? 8 : (nb > 2 ? 4 : nb);         // rounded up to a power of two
+  const int wpb = OUT_WAVES / nbp;
+  const int slot = wave / wpb, sub = wave % wpb;
+  // Each wave merges its splits in order with a running maximum (every load
+  // of a batch of splits is issued at once; no pass over the maxima first),
+  // leaving (max, sum) and its unnormalised sum in LDS.
+  f32x4 o0 = {0.0f, 0.0f, 0.0f, 0.0f}, o1 = o0;
+  float mrun = -INFINITY, lsum = 0.0f;
+  if (slot < nb) {
+    const int64_t row0 = (int64_t)(b0 + slot) * a.nsplit * a.H + h;  // split s: row0 + s * H
+    constexpr int U = 4;
+    for (int s0 = sub; s0 < a.nsplit; s0 += U * wpb) {
+      float ms[U], ls[U];
+      f32x4 p0[U], p1[U];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) O[e] = 0.0f;
-#pragma unroll 4
-  for (int s = wave; s < a.nsplit; s += 4) {
-    const int64_t row = row0 + (int64_t)s * a.H;
-    const float w = __builtin_amdgcn_exp2f(a.pml[2 * row] - M);
-    L = __builtin_fmaf(w, a.pml[2 * row + 1], L);
-    const f32x4 p0 = *reinterpret_cast<const f32x4*>(a.po + row * R + 8 * lane);
-    const f32x4 p1 = *reinterpret_cast<const f32x4*>(a.po + row * R + 8 * lane + 4);
+      for (int u = 0; u < U; ++u) {
+        const int s = s0 + u * wpb;
+        const int64_t row = row0 + (int64_t)(s < a.nsplit ? s : s0) * a.H;
+        const float2 ml = *reinterpret_cast<const float2*>(a.pml + 2 * row);
+        ms[u] = s < a.nsplit ? ml.x : -INFINITY;
+        ls[u] = ml.y;
+        p0[u] = *reinterpret_cast<const f32x4*>(a.po + row * R + 4 * lane);
+        p1[u] = *reinterpret_cast<const f32x4*>(a.po + row * R + R / 2 + 4 * lane);
+      }
+      float mnew = mrun;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      O[e] = __builtin_fmaf(w, p0[e], O[e]);
-      O[4 + e] = __builtin_fmaf(w, p1[e], O[4 + e]);
+      for (int u = 0; u < U; ++u) mnew = fmaxf(mnew, ms[u]);
+      const float al = __builtin_amdgcn_exp2f(mrun - mnew);  // mnew is finite: split s0 is live
+      lsum *= al;
+      o0 *= al;
+      o1 *= al;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float w = __builtin_amdgcn_exp2f(ms[u] - mnew);  // 0 for splits past the end
+        lsum = __builtin_fmaf(w, ls[u], lsum);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o0[e] = __builtin_fmaf(w, p0[u][e], o0[e]);
+          o1[e] = __builtin_fmaf(w, p1[u][e], o1[e]);
+        }
+      }
+      mrun = mnew;
     }
   }
-  *reinterpret_cast<f32x4*>(&part[wave][8 * lane]) = f32x4{O[0], O[1], O[2], O[3]};
-  *reinterpret_cast<f32x4*>(&part[wave][8 * lane + 4]) = f32x4{O[4], O[5], O[6], O[7]};
-  if (lane == 0) part[wave][R] = L;
+  *reinterpret_cast<f32x4*>(&part[wave][4 * lane]) = o0;
+  *reinterpret_cast<f32x4*>(&part[wave][R / 2 + 4 * lane]) = o1;
+  if (lane == 0) {
+    lpart[wave][0] = mrun;
+    lpart[wave][1] = lsum;
+  }
   __syncthreads();
-  const int e = 2 * threadIdx.x;
-  const float inv = 1.0f / (part[0][R] + part[1][R] + part[2][R] + part[3][R]);
-  const float o0 = part[0][e] + part[1][e] + part[2][e] + part[3][e];
-  const float o1 = part[0][e + 1] + part[1][e + 1] + part[2][e + 1] + part[3][e + 1];
-  *reinterpret_cast<float2*>(a.olat + (int64_t)bh * R + e) = float2{o0 * inv, o1 * inv};
-}
+  {  // row r = wave of o~: the wpb partial sums of slot r, in order, over their total weight
+    f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
+    if (wave < nb) {
+      float M = -INFINITY;
+      for (int i = 0; i < wpb; ++i) M = fmaxf(M, lpart[wave * wpb + i][0]);
+      float L = 0.0f;
+      for (int i = 0; i < wpb; ++i) {
+        const int pw = wave * wpb + i;
+        const float w = __builtin_amdgcn_exp2f(lpart[pw][0] - M);  // 0 for a wave with no split
+        s0 += w * *reinterpret_cast<const f32x4*>(&part[pw][4 * lane]);
+        s1 += w * *reinterpret_cast<const f32x4*>(&part[pw][R / 2 + 4 * lane]);
+        L = __builtin_fmaf(w, lpart[pw][1], L);
+      }
+      const float inv = 1.0f / L;
+      s0 *= inv;
+      s1 *= inv;
+    }
+    if (wave < OUT_BG) {
+      *reinterpret_cast<f32x4*>(&orow[wave][4 * lane]) = s0;
+      *reinterpret_cast<f32x4*>(&orow[wave][R / 2 + 4 * lane]) = s1;
+    }
+  }
+  __syncthreads();
 
-// ---- 4. up-projection: out[b,h,d] = sum_e W[256h + 128 + d, e] * o~[b,h,e]
-// Per head, Out_h^T [128 x B] = W_v[h] [128 x 512] . O~_h^T [512 x B] on
-// v_mfma_f32_16x16x32_bf16. W_v is stored with e (the contraction) contiguous,
-// so its fragments load straight from HBM. o~ is fp32: it enters as two bf16
-// operands, hi = bf16(x) and lo = bf16(x - hi), whose sum carries x to about
-// 2^-17 relative. Workgroup: one head, 32 output dims; wave w owns 16 of them
-// and runs over the batch 16 rows at a time.
-__global__ __launch_bounds__(128) void latent_up_kernel(LatentArgs a) {
-  const int h = blockIdx.x >> 2, chunk = blockIdx.x & 3;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, j = lane & 15;
-  const int d0 = chunk * 32 + wave * 16;
-  const uint16_t* wrow = a.w_kv_b + ((int64_t)h * KVB + DN + d0 + j) * R + 8 * g;
-  u32x4 wf[R / 32];
+  // up-projection: lane (g, j) feeds o~ of sequence b0 + j (zero for j >= 8)
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int ks = 0; ks < R / 32; ++ks) wf[ks] = *reinterpret_cast<const u32x4*>(wrow + 32 * ks);
-  for (int b0 = 0; b0 < a.B; b0 += 16) {
-    const int b = b0 + j;
-    const bool live = b < a.B;
-    const float* ol = a.olat + ((int64_t)(live ? b : 0) * a.H + h) * R + 8 * g;
-    f32x4 x[R / 32][2];  // every load of the group in flight at once
-#pragma unroll
-    for (int ks = 0; ks < R / 32; ++ks) {
-      x[ks][0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      x[ks][1] = x[ks][0];
-      if (live) {
-        x[ks][0] = *reinterpret_cast<const f32x4*>(ol + 32 * ks);
-        x[ks][1] = *reinterpret_cast<const f32x4*>(ol + 32 * ks + 4);
-      }
+  for (int ks = 0; ks < KS; ++ks) {
+    const int e0 = 32 * (KS * epart + ks) + 8 * g;
+    f32x4 x0 = {0.0f, 0.0f, 0.0f, 0.0f}, x1 = x0;
+    if (j < OUT_BG) {
+      x0 = *reinterpret_cast<const f32x4*>(&orow[j][e0]);
+      x1 = *reinterpret_cast<const f32x4*>(&orow[j][e0 + 4]);
     }
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8 hi, lo;
 #pragma unroll
-    for (int ks = 0; ks < R / 32; ++ks) {
-      bf16x8 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v0 = x[ks][0][e], v1 = x[ks][1][e];
-        const __bf16 h0 = (__bf16)v0, h1 = (__bf16)v1;
-        hi[e] = h0;
-        hi[4 + e] = h1;
-        lo[e] = (__bf16)(v0 - (float)h0);
-        lo[4 + e] = (__bf16)(v1 - (float)h1);
-      }
-      const bf16x8 w = __builtin_bit_cast(bf16x8, wf[ks]);
-      acc = mfma16(w, hi, acc);
-      acc = mfma16(w, lo, acc);
+    for (int e = 0; e < 4; ++e) {
+      const __bf16 h0 = (__bf16)x0[e], h1 = (__bf16)x1[e];
+      hi[e] = h0;
+      hi[4 + e] = h1;
+      lo[e] = (__bf16)(x0[e] - (float)h0);
+      lo[4 + e] = (__bf16)(x1[e] - (float)h1);
     }
-    // acc[r] = out[b][d0 + 4g + r]
-    if (live) {
-      const uint32_t p0 = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
-      const uint32_t p1 = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
-      *reinterpret_cast<uint2*>(a.out + ((int64_t)b * a.H + h) * DV + d0 + 4 * g) = uint2{p0, p1};
-    }
+    const bf16x8 w = __builtin_bit_cast(bf16x8, wf[ks]);
+    acc = mfma16(w, hi, acc);
+    acc = mfma16(w, lo, acc);
+  }
+  if constexpr (C > 1) {  // the C parts of each tile's contraction, added in order
+    *reinterpret_cast<f32x4*>(&part[wave][4 * lane]) = acc;  // (part is free again)
+    __syncthreads();
+    if (epart != 0) return;
+    for (int i = 1; i < C; ++i) acc += *reinterpret_cast<const f32x4*>(&part[i * TILES + tile][4 * lane]);
+  }
+  // acc[r] = out[b0 + j][d0 + 4g + r]
+  if (j < nb) {
+    const uint32_t p0 = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+    const uint32_t p1 = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+    *reinterpret_cast<uint2*>(a.out + ((int64_t)(b0 + j) * a.H + h) * DV + d0 + 4 * g) = uint2{p0, p1};
   }
 }
 
 }  // namespace
 
 hipError_t launch_latent_decode(const LatentArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(latent_absorb_kernel, dim3(a.H * 8), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(latent_absorb_kernel, dim3((a.B + 15) / 16 * a.H * 8), dim3(256), 0, stream, a);
   hipLaunchKernelGGL(latent_attn_kernel, dim3(a.B * a.nsplit), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(latent_merge_kernel, dim3(a.B * a.H), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(latent_up_kernel, dim3(a.H * 4), dim3(128), 0, stream, a);
+  // merge + up-projection: C workgroups per (head, eight sequences), about 256 in all
+  const int groups = (a.B + OUT_BG - 1) / OUT_BG * a.H;
+  if (groups >= 256)
+    hipLaunchKernelGGL(latent_out_kernel<1>, dim3(groups), dim3(512), 0, stream, a);
+  else if (groups >= 128)
+    hipLaunchKernelGGL(latent_out_kernel<2>, dim3(groups * 2), dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL(latent_out_kernel<4>, dim3(groups * 4), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
