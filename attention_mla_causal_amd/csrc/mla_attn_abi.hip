@@ -557,6 +557,7 @@ mla_status mla_attn_decode_latent(const void* q_nope, const void* q_pe, const vo
   a.S = S;
   a.nsplit = (int32_t)plan.nsplit;
   a.keys_per_split = (int32_t)plan.keys_per_split;
+  a.head_groups = (int32_t)plan.head_groups;
   a.scale_log2 = softmax_scale * kLog2e;
   const hipError_t e = mla::launch_latent_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error("mla_attn_decode_latent", e);

@@ -84,6 +84,7 @@ struct LatentArgs {
   float* pml;              // workspace: [B,nsplit,H,2] partial (max, sum)
   int32_t B, H, S;
   int32_t nsplit, keys_per_split;
+  int32_t head_groups;     // attention workgroups per (sequence, split): 1 (every head), or ceil(H/16)
   float scale_log2;
 };
 

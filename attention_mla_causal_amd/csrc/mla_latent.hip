@@ -220,25 +220,38 @@ __device__ __forceinline__ void wait_vmem_keep_lds_done() {
   __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | ((N >> 4) << 14));
 }
 
+// HG: head groups of 16 per workgroup. HG = 4 serves all (up to) 64 heads
+// from each tile copy, as above. HG = 1 serves one head group (head_groups
+// workgroups per split, each copying the tiles, from L2 after the first):
+// wave 0 scores, all four waves accumulate the output of those 16 heads. For
+// few sequences it gives each split several tiles for the same number of
+// workgroups, so the partials (64 heads x 512 fp32 per split) shrink.
+template <int HG>
 __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
+  static_assert(HG == 4 || HG == 1, "all four head groups, or one");
   __shared__ __attribute__((aligned(1024))) char tile0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char tile1[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char tile2[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char tile3[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2][NWAVE][64];  // [phase parity][head group][lane]
-  __shared__ float abuf[2][NWAVE * 16];                               // rescale factor per head
+  __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2][HG][64];  // [phase parity][head group][lane]
+  __shared__ float abuf[2][HG * 16];                               // rescale factor per head
 
-  // Workgroup w runs on XCD w % 8. With B a multiple of 8, XCD x takes every
-  // split of sequences x, x + 8, ..., so a sequence's splits share one L2 (its
-  // absorbed queries are fetched from HBM once per sequence, not per split).
+  // With HG = 1 the head groups of one (sequence, split) sit B * nsplit
+  // workgroups apart. Workgroup w runs on XCD w % 8: with B a multiple of 8,
+  // XCD x takes every split (and head group) of sequences x, x + 8, ..., so a
+  // sequence's splits share one L2 (its absorbed queries and, with HG = 1,
+  // its tiles are fetched from HBM once per sequence).
+  const unsigned nbs = (unsigned)(a.B * a.nsplit);
+  const int hg0 = HG == 4 ? 0 : (int)(blockIdx.x / nbs);  // first head group served
+  const unsigned wg = HG == 4 ? blockIdx.x : blockIdx.x % nbs;
   int b, split;
   if (a.B % 8 == 0) {
-    const int slot = blockIdx.x >> 3;
-    b = (blockIdx.x & 7) + 8 * (slot / a.nsplit);
+    const int slot = wg >> 3;
+    b = (wg & 7) + 8 * (slot / a.nsplit);
     split = slot % a.nsplit;
   } else {
-    b = blockIdx.x / a.nsplit;
-    split = blockIdx.x % a.nsplit;
+    b = wg / a.nsplit;
+    split = wg % a.nsplit;
   }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -250,11 +263,14 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
   const uint16_t* c_seq = a.c_kv + (int64_t)b * S * R;
   const uint16_t* kp_seq = a.k_pe + (int64_t)b * S * DR;
 
-  // absorbed queries of heads 16w + j (B operand): lane (g, j) holds dims
-  // 32 ks + 8 g .. + 8; zero for heads at or past H
+  // absorbed queries of heads 16 (hg0 + w) + j for the scoring waves w < HG
+  // (B operand): lane (g, j) holds dims 32 ks + 8 g .. + 8; zero for heads at
+  // or past H
+  const int hq = 16 * (hg0 + wave) + j;
+  const bool scoring = HG == 4 || wave < HG;  // (wave < 4 always; written so it folds)
   bf16x8 qf[KSTEPS];
-  if (16 * wave + j < H) {
-    const uint16_t* q = a.qt + ((int64_t)b * H + 16 * wave + j) * KW + 8 * g;
+  if (scoring && hq < H) {
+    const uint16_t* q = a.qt + ((int64_t)b * H + hq) * KW + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(q + 32 * ks);
   } else {
@@ -306,10 +322,10 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
   const int vA1 = vrow * 64 + ((2 + ((j & 3) >> 1)) ^ tile_swz(vrow)) * 16 + 8 * (j & 1);  // odd dt
 
   const float cl2 = positive_cl2(a.scale_log2);
-  // o[hg * NDTW + d]: dims 128w + 16d + 4g + r, head 16 hg + j
-  f32x4 o[NWAVE * NDTW];
+  // o[hg * NDTW + d]: dims 128w + 16d + 4g + r, head 16 (hg0 + hg) + j
+  f32x4 o[HG * NDTW];
 #pragma unroll
-  for (int i = 0; i < NWAVE * NDTW; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int i = 0; i < HG * NDTW; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
 
   auto phase = [&](int p, const char* cur, const char* prv, char* fill, bool do_scores,
@@ -319,18 +335,18 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
     __builtin_amdgcn_s_barrier();      // ... every wave's; tile p-2's buffer is free
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     copy_tile(p + 2, fill);
-    bf16x8 pin[NWAVE];
-    float al[NWAVE];
+    bf16x8 pin[HG];
+    float al[HG];
     if (do_out) {
 #pragma unroll
-      for (int hg = 0; hg < NWAVE; ++hg) {
+      for (int hg = 0; hg < HG; ++hg) {
         al[hg] = abuf[(p - 1) & 1][16 * hg + j];
         pin[hg] = pbuf[(p - 1) & 1][hg][lane];
       }
     }
-    if (do_scores) {
+    if (do_scores && scoring) {
       const int64_t kb = k0 + (int64_t)p * BN;
-      // scores S^T: keys kb + kt*16 + 4g + r, head 16w + j
+      // scores S^T: keys kb + kt*16 + 4g + r, head 16 (hg0 + w) + j
       f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -380,7 +396,7 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
         // rescaled by tile p-1's factors as its contribution lands (a factor
         // of 1 leaves the accumulator unchanged)
 #pragma unroll
-        for (int hg = 0; hg < NWAVE; ++hg) o[hg * NDTW + d] = mfma16(va, pin[hg], o[hg * NDTW + d] * al[hg]);
+        for (int hg = 0; hg < HG; ++hg) o[hg * NDTW + d] = mfma16(va, pin[hg], o[hg * NDTW + d] * al[hg]);
       }
     }
   };
@@ -417,26 +433,27 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
   auto stage = [&](int hg) -> char* { return hg == 0 ? tile0 : hg == 1 ? tile1 : hg == 2 ? tile2 : tile3; };
   constexpr int ROWB = R * 4 + 16;
 #pragma unroll
-  for (int hg = 0; hg < NWAVE; ++hg)
+  for (int hg = 0; hg < HG; ++hg)
 #pragma unroll
     for (int d = 0; d < NDTW; ++d)
       *reinterpret_cast<f32x4*>(stage(hg) + j * ROWB + (128 * wave + 16 * d + 4 * g) * 4) = o[hg * NDTW + d];
   __syncthreads();
   const int64_t row0 = ((int64_t)b * a.nsplit + split) * H;
 #pragma unroll
-  for (int k = 0; k < NWAVE * 16 * R / 4 / 256; ++k) {  // 32 stores of 16 bytes per thread
+  for (int k = 0; k < HG * 16 * R / 4 / 256; ++k) {  // 8 stores of 16 bytes per thread and head group
     const int li = k * 256 + (int)threadIdx.x;
-    const int hd = li >> 7, q = li & 127;  // head (hd >> 4 == k >> 3), 4-dim group
+    const int hl = li >> 7, q = li & 127;  // head within the workgroup (hl >> 4 == k >> 3), 4-dim group
+    const int hd = 16 * hg0 + hl;
     if (hd < H) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(stage(k >> 3) + (hd & 15) * ROWB + 16 * q);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(stage(k >> 3) + (hl & 15) * ROWB + 16 * q);
       // non-temporal: the partials are read once, by the next kernel
       __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(a.po + (row0 + hd) * R + 4 * q));
     }
   }
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  if (16 * wave + j < H && g == 0) {
-    const int64_t row = row0 + 16 * wave + j;
+  if (scoring && hq < H && g == 0) {
+    const int64_t row = row0 + hq;
     a.pml[2 * row] = m_run;
     a.pml[2 * row + 1] = l_tot;
   }
@@ -603,7 +620,10 @@ __global__ __launch_bounds__(512) void latent_out_kernel(LatentArgs a) {
 
 hipError_t launch_latent_decode(const LatentArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(latent_absorb_kernel, dim3((a.B + 15) / 16 * a.H * 8), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(latent_attn_kernel, dim3(a.B * a.nsplit), dim3(256), 0, stream, a);
+  if (a.head_groups == 1)
+    hipLaunchKernelGGL(latent_attn_kernel<4>, dim3(a.B * a.nsplit), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(latent_attn_kernel<1>, dim3(a.B * a.nsplit * a.head_groups), dim3(256), 0, stream, a);
   // merge + up-projection: C workgroups per (head, eight sequences), about 256 in all
   const int groups = (a.B + OUT_BG - 1) / OUT_BG * a.H;
   if (groups >= 256)

@@ -42,9 +42,12 @@ def test_latent_decode_as_on_the_pages():
 # (B, H, past_len): one key; one key short of a tile, a full tile, one past it;
 # head counts that fill 1..4 waves, and ones that leave a wave part-filled
 # (8 = one GPU's share of 64 heads over 8 GPUs, 1, 20, 63); several key
-# splits with a ragged last tile.
+# splits with a ragged last tile. With more than 48 heads and few sequences x
+# tiles, each attention workgroup serves one group of 16 heads (the last
+# group part-filled at 63); 8 sequences take the placement that keeps a
+# sequence's splits and head groups on one XCD.
 EDGE = [(1, 16, 0), (1, 64, 30), (2, 32, 31), (1, 48, 32), (3, 64, 777), (2, 16, 4095), (4, 64, 2000),
-        (2, 8, 500), (3, 1, 40), (1, 20, 63), (1, 63, 1000)]
+        (2, 8, 500), (3, 1, 40), (1, 20, 63), (1, 63, 1000), (8, 64, 1000)]
 
 
 @pytest.mark.parametrize("B,H,P", EDGE)
