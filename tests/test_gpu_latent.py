@@ -103,3 +103,67 @@ def test_latent_batched_decode_full_size_sampled():
                                           wl.past_len, ALPHA, [(0, 0)])[0])
         got.append(to_host_f64(out[b, h, 0]))
     assert_parity(np.stack(got), np.stack(ref), "latent batched decode sampled")
+
+
+def _times(bits, k):
+    """bf16 values times k (a power of two: exact)."""
+    f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(k)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_latent_sharp_softmax():
+    """Queries scaled by 2: sharper weights, so the running maximum moves late
+    and the splits' maxima differ. (Sharper still, bf16 arithmetic itself
+    leaves the bar against the fp64 oracle: with the queries scaled by 8, the
+    pages' own order of operations, keys and values decompressed to bf16, is
+    off by 0.032 at worst on these inputs, and rounding only the absorbed
+    query to bf16, as this path does, by 0.039; by 4, both sit at the bar.)"""
+    B, H, P = 2, 64, 1200
+    x = latent_random_inputs(B, H, P, seed=77)
+    x["q_nope"] = _times(x["q_nope"], 2)
+    x["q_pe"] = _times(x["q_pe"], 2)
+    log(f"case latent sharp B={B} H={H} P={P}")
+    out = _gpu(upload(x), P)
+    assert_parity(to_host_f64(out), _oracle(x, P), "latent sharp softmax")
+
+
+@pytest.mark.parametrize("B,H,P", [(3, 64, 777), (8, 64, 4095)])
+def test_latent_graph_replays_with_new_inputs(B, H, P):
+    """The three launches captured once and replayed after new inputs are
+    copied into the captured buffers: every replay equals an eager call on the
+    same inputs bit for bit, with eager work and synchronisations between
+    replays (3 sequences take the one-head-group workgroups, 8 x 4096 keys the
+    all-heads ones)."""
+    import torch
+    m = _lib()
+    need = m.mla_attn_decode_latent_workspace_bytes(B, H, P + 1)
+    log(f"case latent graph B={B} H={H} P={P} ws={need}")
+    sets = [upload(latent_random_inputs(B, H, P, seed=300 + i)) for i in range(3)]
+    d = {k: v.clone() for k, v in sets[0].items()}
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, H, 1, 128), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _gpu(d, P, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        m.mla_attn_decode_latent(d["q_nope"], d["q_pe"], d["c_kv"], d["k_pe"], d["w_kv_b"], P, ALPHA,
+                                 out=out, workspace=ws)
+    for i in (1, 2, 0, 1):
+        for k in d:
+            d[k].copy_(sets[i][k])
+        g.replay()
+        torch.cuda.synchronize()
+        got = to_host_bits(out)
+        ref = to_host_bits(_gpu(sets[i], P))
+        assert np.array_equal(got, ref), f"replay with set {i} differs from the eager call"
+    x = latent_random_inputs(B, H, P, seed=301)
+    if B * H <= 192:
+        assert_parity(to_host_f64(out), _oracle(x, P), "latent graph replay")
+    else:
+        picks = sorted(spread_pairs(B, H, 16, seed=2))
+        ref = mla_decode_latent_rows(x["q_nope"], x["q_pe"], x["c_kv"], x["k_pe"], x["w_kv_b"], P, ALPHA, picks)
+        assert_parity(np.stack([to_host_f64(out[b, h, 0]) for b, h in picks]), ref, "latent graph replay rows")
