@@ -137,8 +137,28 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   const int logical = (nwg % 8 == 0) ? (wg % 8) * (nwg / 8) + wg / 8 : wg;
   const int src = a.interleave ? k8 : logical;
   const int q = src / a.nsplit;
-  const int bh = a.interleave ? (wg & 7) + 8 * q : q;
+  int bh = a.interleave ? (wg & 7) + 8 * q : q;
   const int split = src - q * a.nsplit;
+  // With a length per sequence and one split per (b, h), sequences are taken
+  // longest first: the workgroup's position bh / H in dispatch order names the
+  // sequence of that rank (lengths clamped as below, ties by index), so the
+  // long (b, h) pairs start first and the short ones fill the tail.
+  if (a.seq_lens != nullptr && a.nsplit == 1 && a.B > 1 && a.B <= 64) {
+    const int ln = threadIdx.x & 63;
+    int32_t len = -1;
+    if (ln < a.B) {
+      const int32_t raw = a.seq_lens[ln];
+      len = raw < 0 ? 0 : (raw > a.S ? a.S : raw);
+    }
+    int rank = 0;
+    for (int jj = 0; jj < a.B; ++jj) {
+      const int32_t lj = __builtin_amdgcn_readlane(len, jj);
+      rank += (lj > len || (lj == len && jj < ln)) ? 1 : 0;
+    }
+    const int r = bh / a.H;
+    const unsigned long long hit = __ballot(ln < a.B && rank == r);
+    bh = (__builtin_ffsll((long long)hit) - 1) * a.H + (bh - r * a.H);
+  }
   const int b = bh / a.H;
   const int h = bh - b * a.H;
 
