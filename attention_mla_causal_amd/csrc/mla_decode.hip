@@ -143,10 +143,18 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   // longest first: the workgroup's position bh / H in dispatch order names the
   // sequence of that rank (lengths clamped as below, ties by index), so the
   // long (b, h) pairs start first and the short ones fill the tail.
-  if (a.seq_lens != nullptr && a.nsplit == 1 && a.B > 1 && a.B <= 64) {
+  if ((MASKED || a.seq_lens != nullptr) && a.nsplit == 1 && a.B > 1 && a.B <= 64) {
     const int ln = threadIdx.x & 63;
     int32_t len = -1;
-    if (ln < a.B) {
+    if constexpr (MASKED) {
+      // the 2D mask's kept positions among 64 evenly spaced samples of each
+      // row stand in for the length (an estimate: it only orders the work)
+      const int64_t pos = (int64_t)ln * a.S / 64;
+      for (int bb = 0; bb < a.B; ++bb) {
+        const int kept = __popcll(__ballot(a.key_mask[(int64_t)bb * a.S + pos] != 0));
+        if (ln == bb) len = kept;
+      }
+    } else if (ln < a.B) {
       const int32_t raw = a.seq_lens[ln];
       len = raw < 0 ? 0 : (raw > a.S ? a.S : raw);
     }
