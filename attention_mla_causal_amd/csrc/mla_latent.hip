@@ -17,7 +17,8 @@
 // Three kernels on the caller's stream:
 //  1. absorb: q~ for every (batch, head) on MFMA (W_k read transposed out of
 //     LDS), rounded to bf16, joined with q_pe into a 576-dim row (workspace).
-//  2. attention: one workgroup per (batch, key split), four waves. 32-key
+//  2. attention: one workgroup per (batch, key split), four waves (with few
+//     sequences x tiles, one per (batch, key split, group of 16 heads)). 32-key
 //     tiles of [latent | k_pe] (36 KiB) are copied straight from HBM into LDS
 //     (buffer_load ... lds; four buffers, two tiles ahead), in 64-byte column
 //     blocks with swizzled 16-byte chunks. Scores use v_mfma_f32_16x16x32_bf16
