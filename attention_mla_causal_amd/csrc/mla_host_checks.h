@@ -185,7 +185,7 @@ inline CheckResult check_common(const void* q_nope, const void* q_pe, const void
 // merges.
 constexpr int64_t kPrefillTargetWorkgroups = 512;
 constexpr int64_t kPrefillMinTilesPerSplit = 16;  // 512 keys: pipeline fill and drain stay small
-constexpr int64_t kPrefillMaxSplits = 16;
+constexpr int64_t kPrefillMaxSplits = 16;  // the merge kernel holds at most 16 partials per row
 
 struct PrefillPlan {
   int64_t nsplit = 1;           // key ranges per query tile

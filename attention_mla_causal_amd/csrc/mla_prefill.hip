@@ -826,29 +826,47 @@ __global__ __launch_bounds__(NT, 2) void mla_prefill_split_kernel(PrefillArgs a)
 __global__ __launch_bounds__(NT, 2) void mla_prefill_varlen_kernel(PrefillArgs a) { prefill_body<kVarlen>(a); }
 __global__ __launch_bounds__(NT, 2) void mla_prefill_masked_kernel(PrefillArgs a) { prefill_body<kMasked>(a); }
 
-// Log-sum-exp merge of the key-range partials of every query row: one wave
-// per row, lane l owns output dims 2l, 2l+1.
+// Log-sum-exp merge of the key-range partials of every query row: 32 lanes
+// per row, lane c owning output dims 4c..4c+3, eight rows per workgroup. All
+// of a row's partial loads (at most kMergeMaxSplits ranges) issue before any
+// is used; the sums run over the ranges in order.
+constexpr int kMergeMaxSplits = 16;  // the host plans at most this many key ranges
 __global__ __launch_bounds__(256) void mla_prefill_merge_kernel(PrefillArgs a) {
   const int64_t rows = (int64_t)a.B * a.H * a.T;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
   if (row >= rows) return;
-  const int lane = threadIdx.x & 63;
+  const int c = threadIdx.x & 31;
   const float* ml = a.ws_ml + row * a.nsplit * 2;
+  const float* po = a.ws_o + row * a.nsplit * DV + 4 * c;
+  f32x2 mls[kMergeMaxSplits];
+  f32x4 ps[kMergeMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMergeMaxSplits; ++s) {
+    mls[s] = f32x2{-INFINITY, 0.0f};
+    ps[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (s < a.nsplit) {
+      mls[s] = *reinterpret_cast<const f32x2*>(ml + 2 * s);
+      ps[s] = *reinterpret_cast<const f32x4*>(po + (int64_t)s * DV);
+    }
+  }
   float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, ml[2 * s]);
-  float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float m = ml[2 * s];
+#pragma unroll
+  for (int s = 0; s < kMergeMaxSplits; ++s) M = fmaxf(M, mls[s][0]);
+  float L = 0.0f;
+  f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < kMergeMaxSplits; ++s) {
+    const float m = mls[s][0];
     const float w = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-    const f32x2 p = *reinterpret_cast<const f32x2*>(a.ws_o + (row * a.nsplit + s) * DV + 2 * lane);
-    L = __builtin_fmaf(w, ml[2 * s + 1], L);
-    o0 = __builtin_fmaf(w, p[0], o0);
-    o1 = __builtin_fmaf(w, p[1], o1);
+    L = __builtin_fmaf(w, mls[s][1], L);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(w, ps[s][e], o[e]);
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  const uint32_t packed = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(o0 * inv)) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(o1 * inv)) << 16);
-  *reinterpret_cast<uint32_t*>(a.out + row * DV + 2 * lane) = packed;
+  bf16x4 w4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w4[e] = (__bf16)(o[e] * inv);
+  *reinterpret_cast<bf16x4*>(a.out + row * DV + 4 * c) = w4;
 }
 
 }  // namespace
@@ -866,7 +884,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(mla_prefill_split_kernel, dim3(a.B * a.H * a.ntiles * a.nsplit), dim3(NT), 0,
                        stream, a);
     const int64_t rows = (int64_t)a.B * a.H * a.T;
-    hipLaunchKernelGGL(mla_prefill_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+    hipLaunchKernelGGL(mla_prefill_merge_kernel, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0,
                        stream, a);
   }
   return hipGetLastError();
