@@ -202,7 +202,9 @@ inline PrefillPlan plan_prefill(int64_t B, int64_t H, int64_t T, int64_t S, int6
   const int64_t wgs = B * H * ((T + block_m - 1) / block_m);
   if (wgs >= kPrefillTargetWorkgroups) return p;
   const int64_t tiles = (S + key_tile - 1) / key_tile;
-  int64_t n = (kPrefillTargetWorkgroups + wgs - 1) / wgs;
+  // never past two workgroups per CU: a grid just past 512 runs a second
+  // round for a few workgroups
+  int64_t n = kPrefillTargetWorkgroups / wgs;
   const int64_t by_len = tiles / kPrefillMinTilesPerSplit;
   if (n > by_len) n = by_len;
   if (n > kPrefillMaxSplits) n = kPrefillMaxSplits;
@@ -530,13 +532,15 @@ constexpr int64_t kLatentRank = 512;             // kv_lora_rank
 constexpr int64_t kLatentKeyWidth = 512 + 64;    // latent + shared rotary key, per key
 constexpr int64_t kLatentKeysPerTile = 32;
 constexpr int64_t kLatentTargetWorkgroups = 256; // one per CU
-// Sequences x key tiles at or above which every attention workgroup serves
-// all heads (a tile copied once for 64 heads); below it, with more than 48
+// Sequences x key tiles above which every attention workgroup serves all
+// heads (a tile copied once for 64 heads); up to it, with more than 48
 // heads, a workgroup serves one group of 16 heads: four times the workgroups
 // for the same splits, each with a quarter of the queries to load, the
 // output to accumulate and the partial to store (the pages' decode over the
 // latent cache, 32 tiles: 20.7 -> 17.9 us; two tiles per split instead, with
-// the same 64 workgroups as before, 18.7 us; four, 21.0 us).
+// the same 64 workgroups as before, 18.7 us; four, 21.0 us). Measured
+// crossover: at 1024 sequences x tiles one head group is 0-5% faster, from
+// 1280 on all heads are (13-25% at 1280-1536, 2x at 8192).
 constexpr int64_t kLatentAllHeadsTiles = 4 * kLatentTargetWorkgroups;
 
 struct LatentPlan {
@@ -549,18 +553,21 @@ struct LatentPlan {
   size_t workspace_bytes = 0;  // total, each region 256-byte aligned
 };
 
-// Split each sequence's keys so about one attention workgroup per CU runs.
+// Split each sequence's keys so about one attention workgroup per CU runs,
+// never more than one per CU (the attention kernel's LDS holds one): a grid
+// just past 256 would run a second round for a few workgroups (12 sequences
+// of 4096 keys: 264 workgroups 58.0 us, 228 workgroups 42.7 us).
 inline LatentPlan plan_latent(int64_t B, int64_t H, int64_t S) {
   LatentPlan p;
   if (B <= 0 || H <= 0 || S <= 0) return p;
   const int64_t tiles = (S + kLatentKeysPerTile - 1) / kLatentKeysPerTile;
   const int64_t groups = (H + 15) / 16;
   int64_t nsplit;
-  if (groups < 4 || B * tiles >= kLatentAllHeadsTiles) {
-    nsplit = (kLatentTargetWorkgroups + B - 1) / B;
+  if (groups < 4 || B * tiles > kLatentAllHeadsTiles) {
+    nsplit = kLatentTargetWorkgroups / B;  // one workgroup per CU: never a second round
   } else {
     p.head_groups = groups;
-    nsplit = (kLatentTargetWorkgroups + B * groups - 1) / (B * groups);
+    nsplit = kLatentTargetWorkgroups / (B * groups);
   }
   if (nsplit > tiles) nsplit = tiles;
   if (nsplit < 1) nsplit = 1;

@@ -167,3 +167,25 @@ def test_latent_graph_replays_with_new_inputs(B, H, P):
         picks = sorted(spread_pairs(B, H, 16, seed=2))
         ref = mla_decode_latent_rows(x["q_nope"], x["q_pe"], x["c_kv"], x["k_pe"], x["w_kv_b"], P, ALPHA, picks)
         assert_parity(np.stack([to_host_f64(out[b, h, 0]) for b, h in picks]), ref, "latent graph replay rows")
+
+
+@pytest.mark.parametrize("B,P", [(4, 8191), (12, 4095)])
+def test_latent_plan_boundary_sampled(B, P):
+    """Sequences x key tiles on either side of the switch between the two
+    attention plans: 4 x 8192 keys (1024 tiles: one head group per
+    workgroup) and 12 x 4096 (1536: all heads, 21 splits of 196 keys rounded
+    to whole tiles, so the grid stays within one workgroup per CU). Inputs
+    drawn on the device, 24 (b, h) rows against the oracle."""
+    import torch
+    from seeded_inputs import LatentWorkload
+    H = 64
+    wl = LatentWorkload("boundary", B, H, P)
+    log(f"case latent plan boundary B={B} H={H} S={P + 1}")
+    d = latent_device_inputs(wl, "cuda", seed=B)
+    out = _gpu(d, P)
+    assert torch.isfinite(out).all().item()
+    picks = sorted(spread_pairs(B, H, 24, seed=3))
+    w = to_host_bits(d["w_kv_b"])
+    x = {k: to_host_bits(d[k]) for k in ("q_nope", "q_pe", "c_kv", "k_pe")}
+    ref = mla_decode_latent_rows(x["q_nope"], x["q_pe"], x["c_kv"], x["k_pe"], w, P, ALPHA, picks)
+    assert_parity(np.stack([to_host_f64(out[b, h, 0]) for b, h in picks]), ref, f"latent boundary B={B}")
