@@ -344,8 +344,9 @@ def run_varlen(wl, steps, warmup, seed=0):
     t = measure(step, steps, warmup, graph=True)
     rec = record(f"B{wl.B} H{wl.H} cap{wl.cap} sum_len{int(lens.sum())}", t, varlen_bytes(wl, lens), "hbm",
                  "mla_decode_kernel", measured_traffic("mla_decode_kernel", wl.name), "hip_graph")
-    del d
-    return rec, None
+    step(0)
+    torch.cuda.synchronize()
+    return rec, {"dev": d, "out": out.clone(), "lens": lens}
 
 
 def run_paged(wl, steps, warmup, seed=0):
@@ -370,8 +371,9 @@ def run_paged(wl, steps, warmup, seed=0):
     t = measure(step, steps, warmup, graph=True)
     rec = record(f"B{wl.B} H{wl.H} bs{wl.block_size} sum_len{int(lens.sum())} append", t, paged_bytes(wl, lens),
                  "hbm", "mla_decode_kernel", measured_traffic("mla_decode_kernel", wl.name), "hip_graph")
-    del d
-    return rec, None
+    step(0)
+    torch.cuda.synchronize()
+    return rec, {"dev": d, "out": out.clone(), "lens": lens, "table": table}
 
 
 def run_prefill_varlen(wl, steps, warmup, seed=0):
@@ -604,6 +606,68 @@ def cpu_decode_sampled(wl, state, seconds):
                       f"device inputs), {el:.1f} s", par)
 
 
+def _pair_bytes(L, H):
+    """Algorithmic bytes of one (b, h) pair of a decode over L keys: its k_nope
+    and v rows, its share of the shared rotary rows, query and output."""
+    return L * (128 + 128) * 2 + L * 64 * 2 / H + (192 + 128) * 2
+
+
+def cpu_varlen_decode(wl, state, seconds):
+    """The variable-length decode oracle on sampled (b, h) pairs; each pair's
+    valid cache rows are copied back from the device inputs."""
+    from oracle import mla_decode_varlen_rows
+    d, out, lens = state["dev"], state["out"], state["lens"]
+    par, el, n, work = Parity(), 0.0, 0, 0.0
+    for b, h in sampled_pairs(wl.B, wl.H, 64):
+        L = int(lens[b])
+        xs = {"q_nope": to_host_bits(d["q_nope"][b:b + 1, h:h + 1]), "q_pe": to_host_bits(d["q_pe"][b:b + 1, h:h + 1]),
+              "k_nope": to_host_bits(d["k_nope"][b:b + 1, h:h + 1, :max(L, 1)]),
+              "k_pe": to_host_bits(d["k_pe"][b:b + 1, :, :max(L, 1)]),
+              "v": to_host_bits(d["v"][b:b + 1, h:h + 1, :max(L, 1)])}
+        ref, dt = _timed(lambda: mla_decode_varlen_rows(xs["q_nope"], xs["q_pe"], xs["k_nope"], xs["k_pe"], xs["v"],
+                                                        np.array([L]), wl.softmax_scale, [(0, 0)]))
+        el += dt
+        n += 1
+        work += _pair_bytes(L, wl.H)
+        par.add(to_host_bits(out[b, h, 0]), ref[0])
+        if el >= seconds:
+            break
+    return cpu_record(work / el / 1e9, "GB/s", f"{n} of {wl.B * wl.H} (b, h) pairs (valid rows copied from the "
+                      f"device cache), {el:.1f} s", par)
+
+
+def cpu_paged_decode(wl, state, seconds):
+    """The paged-decode oracle (append, then attend) on sampled (b, h) pairs:
+    the blocks a sequence's table names, for that head, are copied back and
+    renumbered, with the new token's rows from the call's inputs."""
+    import torch
+    from oracle import mla_decode_paged
+    d, out, lens, table = state["dev"], state["out"], state["lens"], state["table"]
+    bs = wl.block_size
+    par, el, n, work = Parity(), 0.0, 0, 0.0
+    for b, h in sampled_pairs(wl.B, wl.H, 64):
+        L = int(lens[b])
+        nblk = max((L + bs - 1) // bs, 1)
+        idx = torch.as_tensor(np.asarray(table[b, :nblk], dtype=np.int64), device=d["k_pe_pages"].device)
+        kn = to_host_bits(d["k_nope_pages"].index_select(0, idx)[:, h:h + 1])
+        vv = to_host_bits(d["v_pages"].index_select(0, idx)[:, h:h + 1])
+        kp = to_host_bits(d["k_pe_pages"].index_select(0, idx))
+        new = (to_host_bits(d["k_nope_new"][b:b + 1, h:h + 1]), to_host_bits(d["k_pe_new"][b:b + 1]),
+               to_host_bits(d["v_new"][b:b + 1, h:h + 1]))
+        q = (to_host_bits(d["q_nope"][b:b + 1, h:h + 1]), to_host_bits(d["q_pe"][b:b + 1, h:h + 1]))
+        local = np.arange(nblk, dtype=np.int32)[None]
+        res, dt = _timed(lambda: mla_decode_paged(q[0], q[1], kn, kp, vv, local, np.array([L]), wl.softmax_scale,
+                                                  new=new))
+        el += dt
+        n += 1
+        work += _pair_bytes(max(L - 1, 0), wl.H) + 2 * ((128 + 128) * 2 + 64 * 2 / wl.H)
+        par.add(to_host_bits(out[b, h, 0]), res[0][0, 0, 0])
+        if el >= seconds:
+            break
+    return cpu_record(work / el / 1e9, "GB/s", f"{n} of {wl.B * wl.H} (b, h) pairs (the sequence's blocks for the "
+                      f"head copied from the device pages), {el:.1f} s", par)
+
+
 def cpu_varlen_prefill(wl, state, seconds):
     """Heads of the longest sequence (device inputs copied back), through the
     padded-batch oracle, until `seconds` pass."""
@@ -809,9 +873,17 @@ def run_workload(name, steps, warmup, cpu_seconds, eager=False):
             rec["cpu_baseline"] = cpu_rope(WORKLOADS["chunked_prefill"], min(cpu_seconds, 3.0))
         return rec
     if name in VARLEN_WORKLOADS:
-        return run_varlen(VARLEN_WORKLOADS[name], steps, warmup)[0]
+        wl = VARLEN_WORKLOADS[name]
+        rec, st = run_varlen(wl, steps, warmup)
+        if cpu_seconds > 0:
+            rec["cpu_baseline"] = cpu_varlen_decode(wl, st, cpu_seconds)
+        return rec
     if name in PAGED_WORKLOADS:
-        return run_paged(PAGED_WORKLOADS[name], steps, warmup)[0]
+        wl = PAGED_WORKLOADS[name]
+        rec, st = run_paged(wl, steps, warmup)
+        if cpu_seconds > 0:
+            rec["cpu_baseline"] = cpu_paged_decode(wl, st, cpu_seconds)
+        return rec
     if name in VARLEN_PREFILL_WORKLOADS:
         wl = VARLEN_PREFILL_WORKLOADS[name]
         rec, st = run_prefill_varlen(wl, steps, warmup)
