@@ -568,6 +568,32 @@ def cpu_decode_whole(wl, state, seconds):
                       f"whole workload (B={wl.B} H={wl.H} S={wl.S}), {reps} repetitions, {el:.1f} s", par)
 
 
+def cpu_decode_rope_whole(wl, state, seconds):
+    """The pages' decode with the rotary prologue, whole (input set 0): the
+    rotary oracle turns the query at position S-1 (the released
+    configuration's YaRN table), then the attention oracle runs; repeated
+    for ~`seconds`."""
+    from oracle import KIMI_K2_ROPE, apply_rope, bf16_bits_to_f64, mla_attention, rope_cos_sin, rope_positions
+    x = state["host"]
+    par = Parity()
+
+    def oracle():
+        cos, sin = rope_cos_sin(wl.S, **KIMI_K2_ROPE)
+        q_rot = apply_rope(bf16_bits_to_f64(x["q_pe"]), rope_positions(wl.B, 1, past_len=wl.past_len), cos, sin)
+        return mla_attention(x["q_nope"], q_rot, x["k_nope"], x["k_pe"], x["v"], wl.past_len, wl.softmax_scale)
+
+    reps, el, ref = 0, 0.0, None
+    while el < seconds and reps < 1000:
+        ref, dt = _timed(oracle)
+        el += dt
+        reps += 1
+    par.add(to_host_bits(state["out"]), ref)
+    nbytes = decode_bytes(wl) + wl.B * 256
+    return cpu_record(nbytes * reps / el / 1e9, "GB/s",
+                      f"whole workload (B={wl.B} H={wl.H} S={wl.S}, table included), {reps} repetitions, "
+                      f"{el:.1f} s", par)
+
+
 def sampled_pairs(B, H, n, seed=0):
     """Up to n (b, h) pairs: both ends, one in each eighth of the b*H + h
     range and one of each residue of b*H + h mod 8 (the two ways the decode
@@ -865,7 +891,10 @@ def run_workload(name, steps, warmup, cpu_seconds, eager=False):
                 rec["cpu_baseline"] = cpu_prefill(wl, st, cpu_seconds)
         return rec
     if name == "decode_p1000_rope":
-        rec, _ = run_decode(WORKLOADS["decode_p1000"], steps, warmup, graph=graph, rope=True)
+        wl = WORKLOADS["decode_p1000"]
+        rec, st = run_decode(wl, steps, warmup, graph=graph, rope=True)
+        if cpu_seconds > 0:
+            rec["cpu_baseline"] = cpu_decode_rope_whole(wl, st, cpu_seconds)
         return rec
     if name == "rope_chunked_prefill":
         rec, _ = run_rope_apply(WORKLOADS["chunked_prefill"], steps, warmup)
