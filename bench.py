@@ -452,7 +452,14 @@ def run_rope_apply(wl, steps, warmup, seed=0):
                  measured_traffic("mla_rope_apply_kernel", "rope_" + wl.name), "hip_graph")
     rec["input_copies"] = copies
     del sets
-    return rec, None
+    # one more call on fresh rows, kept for the CPU leg's comparison
+    q = torch.randn((wl.B, wl.H, wl.T, 64), generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn((wl.B, 1, wl.T, 64), generator=g, device=dev).to(torch.bfloat16)
+    state = {"q_in": to_host_bits(q), "k_in": to_host_bits(k)}
+    mla.mla_rope_apply_qk(q, k, table, past_len=wl.past_len)
+    torch.cuda.synchronize()
+    state.update(q_out=to_host_bits(q), k_out=to_host_bits(k))
+    return rec, state
 
 
 def run_latent(wl, steps, warmup, seed=0):
@@ -787,20 +794,24 @@ def cpu_latent(wl, state, seconds):
     return cpu_record(per * n / el / 1e9, "GB/s", f"{n} of {wl.B * wl.H} (b, h) pairs, {el:.1f} s", par)
 
 
-def cpu_rope(wl, seconds, seed=0):
-    """The fp64 rotation oracle over rows of the same shape (table built once)."""
-    from oracle import KIMI_K2_ROPE, apply_rope, rope_cos_sin, rope_positions
-    rng = np.random.default_rng(seed)
-    q = rng.standard_normal((wl.B, wl.H, wl.T, 64))
-    k = rng.standard_normal((wl.B, 1, wl.T, 64))
+def cpu_rope(wl, state, seconds):
+    """The fp64 rotation oracle on the rows of the GPU's last call (table
+    built once), the whole workload repeated for ~`seconds`; the GPU's rotated
+    rows are compared with it."""
+    from oracle import KIMI_K2_ROPE, apply_rope, bf16_bits_to_f64, rope_cos_sin, rope_positions
+    q, k = bf16_bits_to_f64(state["q_in"]), bf16_bits_to_f64(state["k_in"])
     cos, sin = rope_cos_sin(wl.S, **KIMI_K2_ROPE)
     pos = rope_positions(wl.B, wl.T, past_len=wl.past_len)
-    n, el = 0, 0.0
+    n, el, res = 0, 0.0, None
     while el < seconds:
-        _, dt = _timed(lambda: (apply_rope(q, pos, cos, sin), apply_rope(k, pos, cos, sin)))
+        res, dt = _timed(lambda: (apply_rope(q, pos, cos, sin), apply_rope(k, pos, cos, sin)))
         el += dt
         n += 1
-    return cpu_record(rope_apply_bytes(wl) * n / el / 1e9, "GB/s", f"the whole workload {n} times, {el:.1f} s")
+    par = Parity()
+    par.add(state["q_out"], res[0])
+    par.add(state["k_out"], res[1])
+    return cpu_record(rope_apply_bytes(wl) * n / el / 1e9, "GB/s", f"the whole workload {n} times, {el:.1f} s",
+                      par)
 
 
 # ---------------------------------------------------------------- probes
@@ -897,9 +908,9 @@ def run_workload(name, steps, warmup, cpu_seconds, eager=False):
             rec["cpu_baseline"] = cpu_decode_rope_whole(wl, st, cpu_seconds)
         return rec
     if name == "rope_chunked_prefill":
-        rec, _ = run_rope_apply(WORKLOADS["chunked_prefill"], steps, warmup)
+        rec, st = run_rope_apply(WORKLOADS["chunked_prefill"], steps, warmup)
         if cpu_seconds > 0:
-            rec["cpu_baseline"] = cpu_rope(WORKLOADS["chunked_prefill"], min(cpu_seconds, 3.0))
+            rec["cpu_baseline"] = cpu_rope(WORKLOADS["chunked_prefill"], st, min(cpu_seconds, 3.0))
         return rec
     if name in VARLEN_WORKLOADS:
         wl = VARLEN_WORKLOADS[name]
