@@ -151,8 +151,10 @@ def test_chunked_prefill_matches_full_prefill_suffix():
 
 # (B, H, T, P): grids too small to fill the GPU, so the keys of each query
 # tile split over several workgroups: several ranges, a ragged last range,
-# causal tiles that see no key of the later ranges, 2..5 ranges.
-SPLIT = [(1, 2, 256, 3840), (1, 1, 100, 5000), (2, 4, 1024, 0), (1, 3, 777, 2000), (1, 8, 129, 1023)]
+# causal tiles that see no key of the later ranges, 2..16 ranges (16, the
+# most the merge holds per row, for the last two).
+SPLIT = [(1, 2, 256, 3840), (1, 1, 100, 5000), (2, 4, 1024, 0), (1, 3, 777, 2000), (1, 8, 129, 1023),
+         (1, 1, 128, 8192), (1, 1, 100, 16000)]
 
 
 @pytest.mark.parametrize("B,H,T,P", SPLIT)
