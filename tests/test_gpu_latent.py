@@ -47,7 +47,7 @@ def test_latent_decode_as_on_the_pages():
 # group part-filled at 63); 8 sequences take the placement that keeps a
 # sequence's splits and head groups on one XCD.
 EDGE = [(1, 16, 0), (1, 64, 30), (2, 32, 31), (1, 48, 32), (3, 64, 777), (2, 16, 4095), (4, 64, 2000),
-        (2, 8, 500), (3, 1, 40), (1, 20, 63), (1, 63, 1000), (8, 64, 1000)]
+        (2, 8, 500), (3, 1, 40), (1, 20, 63), (1, 63, 1000), (8, 64, 1000), (1, 64, 0)]
 
 
 @pytest.mark.parametrize("B,H,P", EDGE)

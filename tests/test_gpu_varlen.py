@@ -73,6 +73,10 @@ EDGE = [
     (3, 16, 512, [600, -4, 200], 256),
     (3, 100, 3000, [3000, 1, 2049], 3000),   # long sequences split in the varlen plan; merge kernel
     (4, 64, 2500, [2500, 1025, 1024, 3], 2500),  # varlen split, merged in the split kernel
+    # one split per (b, h): 64 sequences taken longest first (ties and empty
+    # ones among them), and 65, past the ranking, in index order
+    (64, 32, 160, [(37 * b) % 53 * 3 for b in range(64)], 160),
+    (65, 32, 160, [(23 * b) % 53 * 3 for b in range(65)], 160),
 ]
 
 
