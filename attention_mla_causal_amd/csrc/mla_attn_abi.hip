@@ -550,7 +550,7 @@ mla_status mla_attn_decode_latent(const void* q_nope, const void* q_pe, const vo
   a.out = static_cast<uint16_t*>(out);
   char* ws = static_cast<char*>(workspace);
   a.qt = reinterpret_cast<uint16_t*>(ws);
-  a.po = reinterpret_cast<float*>(ws + plan.qt_bytes);
+  a.po = reinterpret_cast<uint16_t*>(ws + plan.qt_bytes);
   a.pml = reinterpret_cast<float*>(ws + plan.qt_bytes + plan.po_bytes);
   a.B = B;
   a.H = H;

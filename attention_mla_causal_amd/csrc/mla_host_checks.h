@@ -548,7 +548,7 @@ struct LatentPlan {
   int64_t keys_per_split = 0;  // multiple of kLatentKeysPerTile
   int64_t head_groups = 1;     // attention workgroups per (sequence, split): 1, or ceil(H / 16)
   size_t qt_bytes = 0;         // bf16 [B, H, 576]: absorbed queries joined with q_pe
-  size_t po_bytes = 0;         // fp32 [B, nsplit, H, 512]: partial latent outputs
+  size_t po_bytes = 0;         // bf16 [B, nsplit, H, 512]: partial latent outputs
   size_t pml_bytes = 0;        // fp32 [B, nsplit, H, 2]: partial (max, sum)
   size_t workspace_bytes = 0;  // total, each region 256-byte aligned
 };
@@ -577,7 +577,7 @@ inline LatentPlan plan_latent(int64_t B, int64_t H, int64_t S) {
   p.nsplit = nsplit;
   p.keys_per_split = kps;
   p.qt_bytes = align256(size_t(B) * size_t(H) * size_t(kLatentKeyWidth) * 2);
-  p.po_bytes = align256(size_t(B) * size_t(nsplit) * size_t(H) * size_t(kLatentRank) * 4);
+  p.po_bytes = align256(size_t(B) * size_t(nsplit) * size_t(H) * size_t(kLatentRank) * 2);
   p.pml_bytes = align256(size_t(B) * size_t(nsplit) * size_t(H) * 2 * 4);
   p.workspace_bytes = p.qt_bytes + p.po_bytes + p.pml_bytes;
   return p;

@@ -80,7 +80,7 @@ struct LatentArgs {
   const uint16_t* w_kv_b;  // [H*256, 512] kv_b_proj weight (key rows, then value rows, per head)
   uint16_t* out;           // [B,H,1,128]
   uint16_t* qt;            // workspace: [B,H,576] absorbed queries joined with q_pe (bf16)
-  float* po;               // workspace: [B,nsplit,H,512] partial latent outputs
+  uint16_t* po;            // workspace: [B,nsplit,H,512] partial latent outputs (bf16)
   float* pml;              // workspace: [B,nsplit,H,2] partial (max, sum)
   int32_t B, H, S;
   int32_t nsplit, keys_per_split;

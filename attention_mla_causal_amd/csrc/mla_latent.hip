@@ -28,7 +28,7 @@
 //     128 dims of all heads from the probabilities every wave leaves in LDS,
 //     one tile behind the scores, its C^T fragments read with
 //     ds_read_b64_tr_b16 in the key order the score accumulator leaves P in.
-//     Each split writes an fp32 partial (o~, max, sum).
+//     Each split writes a partial: o~ rounded to bf16, (max, sum) in fp32.
 //  3. merge + up-projection: log-sum-exp over the splits of each (batch,
 //     head) -> o~ (fp32, in LDS), then out = W_v o~ on MFMA (o~ split into two
 //     bf16 halves), rounded to bf16.
@@ -44,6 +44,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int R = 512;                       // latent dims (kv_lora_rank)
@@ -226,7 +227,7 @@ __device__ __forceinline__ void wait_vmem_keep_lds_done() {
 // workgroups per split, each copying the tiles, from L2 after the first):
 // wave 0 scores, all four waves accumulate the output of those 16 heads. For
 // few sequences it gives each split several tiles for the same number of
-// workgroups, so the partials (64 heads x 512 fp32 per split) shrink.
+// workgroups, so the partials (64 heads x 512 dims per split) shrink.
 template <int HG>
 __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
   static_assert(HG == 4 || HG == 1, "all four head groups, or one");
@@ -429,7 +430,10 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
   // accumulator, so stored directly each instruction would touch 16 rows; the
   // accumulators are turned into rows in LDS first (head group hg in tile
   // buffer hg, rows of 512 dims 2064 bytes apart, so each 16-lane group of a
-  // write meets 16 distinct banks), then every wave stores whole rows.
+  // write meets 16 distinct banks), then every wave stores whole rows. The
+  // partial is stored rounded to bf16 (round to nearest even): it is the
+  // output of a bf16 product, which the pages' attention rounds to bf16 as
+  // well; the (max, sum) pair stays fp32 and the merge runs in fp32.
   __syncthreads();  // every wave is done with the tiles
   auto stage = [&](int hg) -> char* { return hg == 0 ? tile0 : hg == 1 ? tile1 : hg == 2 ? tile2 : tile3; };
   constexpr int ROWB = R * 4 + 16;
@@ -441,14 +445,23 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
   __syncthreads();
   const int64_t row0 = ((int64_t)b * a.nsplit + split) * H;
 #pragma unroll
-  for (int k = 0; k < HG * 16 * R / 4 / 256; ++k) {  // 8 stores of 16 bytes per thread and head group
-    const int li = k * 256 + (int)threadIdx.x;
-    const int hl = li >> 7, q = li & 127;  // head within the workgroup (hl >> 4 == k >> 3), 4-dim group
+  for (int k = 0; k < HG * 16 / NWAVE; ++k) {  // one row per wave: lane l stores dims 4l.. and 256+4l..
+    const int hl = k * NWAVE + wave;           // head within the workgroup (hl >> 4 == k >> 2)
     const int hd = 16 * hg0 + hl;
     if (hd < H) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(stage(k >> 3) + (hl & 15) * ROWB + 16 * q);
+      const char* src = stage(k >> 2) + (hl & 15) * ROWB;
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(src + 16 * lane);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + R * 2 + 16 * lane);
+      bf16x4 w0, w1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w0[e] = (__bf16)v0[e];
+        w1[e] = (__bf16)v1[e];
+      }
       // non-temporal: the partials are read once, by the next kernel
-      __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(a.po + (row0 + hd) * R + 4 * q));
+      uint16_t* dst = a.po + (row0 + hd) * R + 4 * lane;
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x2, w0), reinterpret_cast<u32x2*>(dst));
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x2, w1), reinterpret_cast<u32x2*>(dst + R / 2));
     }
   }
   float l_tot = l_run + __shfl_xor(l_run, 16);
@@ -472,7 +485,7 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
 // v_mfma_f32_16x16x32_bf16, wave w computes 16 output dims over 512 / C of
 // the contraction (C waves per 16 dims, their sums added in LDS). W_v's
 // contraction dim is contiguous, so its fragments load straight from HBM, at
-// the start, while the merge runs; o~ is fp32 and enters as two bf16 operands,
+// the start, while the merge runs; o~ (merged in fp32) enters as two bf16 operands,
 // hi = bf16(x) and lo = bf16(x - hi), whose sum carries x to about 2^-17
 // relative. The host picks C so that about 256 workgroups run: with few
 // sequences the head's weight rows are spread over C workgroups (each merging
@@ -526,8 +539,14 @@ __global__ __launch_bounds__(512) void latent_out_kernel(LatentArgs a) {
         const float2 ml = *reinterpret_cast<const float2*>(a.pml + 2 * row);
         ms[u] = s < a.nsplit ? ml.x : -INFINITY;
         ls[u] = ml.y;
-        p0[u] = *reinterpret_cast<const f32x4*>(a.po + row * R + 4 * lane);
-        p1[u] = *reinterpret_cast<const f32x4*>(a.po + row * R + R / 2 + 4 * lane);
+        const uint16_t* src = a.po + row * R + 4 * lane;  // bf16 dims 4 lane .. and 256 + 4 lane ..
+        const bf16x4 q0 = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(src));
+        const bf16x4 q1 = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(src + R / 2));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p0[u][e] = (float)q0[e];
+          p1[u][e] = (float)q1[e];
+        }
       }
       float mnew = mrun;
 #pragma unroll

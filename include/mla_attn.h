@@ -375,8 +375,11 @@ size_t mla_attn_decode_latent_workspace_bytes(int32_t B, int32_t H, int32_t S);
  * workspace: caller-owned device scratch of at least
  * mla_attn_decode_latent_workspace_bytes(B, H, S) bytes, 16-byte aligned;
  * contents on entry do not matter. Calls that may run at the same time must
- * not share a workspace. Errors as for mla_attn_decode. Four kernels are
- * enqueued on `stream` (absorb, attention, merge, up-projection).
+ * not share a workspace. Errors as for mla_attn_decode. Three kernels are
+ * enqueued on `stream`: absorb (kv_b_proj's key half into the query),
+ * attention over key splits (each split's latent output kept in the
+ * workspace, rounded to bf16, with its fp32 max and sum), and the merge of
+ * the splits followed by the value half of kv_b_proj.
  */
 mla_status mla_attn_decode_latent(const void* q_nope, const void* q_pe,
                                   const void* c_kv, const void* k_pe,
