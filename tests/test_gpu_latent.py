@@ -45,9 +45,12 @@ def test_latent_decode_as_on_the_pages():
 # splits with a ragged last tile. With more than 48 heads and few sequences x
 # tiles, each attention workgroup serves one group of 16 heads (the last
 # group part-filled at 63); 8 sequences take the placement that keeps a
-# sequence's splits and head groups on one XCD.
+# sequence's splits and head groups on one XCD. From five sequences on, the
+# absorb stages query and output rows through LDS: 5 (the first such batch)
+# and 17 (a second group of 16 holding one sequence).
 EDGE = [(1, 16, 0), (1, 64, 30), (2, 32, 31), (1, 48, 32), (3, 64, 777), (2, 16, 4095), (4, 64, 2000),
-        (2, 8, 500), (3, 1, 40), (1, 20, 63), (1, 63, 1000), (8, 64, 1000), (1, 64, 0)]
+        (2, 8, 500), (3, 1, 40), (1, 20, 63), (1, 63, 1000), (8, 64, 1000), (1, 64, 0), (5, 64, 40),
+        (17, 8, 100)]
 
 
 @pytest.mark.parametrize("B,H,P", EDGE)
