@@ -253,6 +253,34 @@ int main() {
     EXPECT(check_latent_decode(p, p, p, p, p, p, p, size_t(1) << 30, 1, 64, 1001, 1000, -0.07f, &lp).status == MLA_OK);
     EXPECT(check_latent_decode(p, p, p, p, p, p, p, size_t(1) << 30, 1, 64, 1001, 1000, 0.0f, &lp).status == MLA_OK);
   }
+  // latent plan properties over a grid of shapes: every split holds at least
+  // one key and a whole number of 32-key tiles; no more than one attention
+  // workgroup per CU while B allows it; one head group per workgroup only for
+  // more than 48 heads over at most 1024 sequence-tiles; the workspace holds
+  // the bf16 absorbed rows, the bf16 partials and their fp32 (max, sum).
+  {
+    const int64_t Bs[] = {1, 2, 3, 5, 8, 12, 16, 17, 32, 64, 255, 256, 257, 1000};
+    const int64_t Hs[] = {1, 8, 16, 17, 48, 49, 63, 64};
+    const int64_t Ss[] = {1, 31, 32, 33, 1001, 4096, 8192, 65537, 2097151};
+    for (int64_t B : Bs)
+      for (int64_t H : Hs)
+        for (int64_t S : Ss) {
+          const LatentPlan lp = plan_latent(B, H, S);
+          const int64_t tiles = (S + 31) / 32, groups = (H + 15) / 16;
+          EXPECT(lp.nsplit >= 1 && lp.keys_per_split % 32 == 0 && lp.keys_per_split >= 32);
+          EXPECT((lp.nsplit - 1) * lp.keys_per_split < S && S <= lp.nsplit * lp.keys_per_split);
+          EXPECT(lp.head_groups == 1 || (lp.head_groups == groups && H > 48 && B * tiles <= 1024));
+          if (B * lp.head_groups <= 256) EXPECT(B * lp.nsplit * lp.head_groups <= 256);
+          else EXPECT(lp.nsplit == 1);
+          EXPECT(lp.qt_bytes >= size_t(B * H * 576 * 2) && lp.po_bytes >= size_t(B * lp.nsplit * H * 512 * 2) &&
+                 lp.pml_bytes >= size_t(B * lp.nsplit * H * 2 * 4));
+          EXPECT(lp.workspace_bytes == lp.qt_bytes + lp.po_bytes + lp.pml_bytes);
+          EXPECT(lp.qt_bytes % 256 == 0 && lp.po_bytes % 256 == 0 && lp.pml_bytes % 256 == 0);
+        }
+    EXPECT(plan_latent(0, 64, 1001).workspace_bytes == 0);
+    EXPECT(plan_latent(1, 64, 1001).head_groups == 4 && plan_latent(1, 64, 1001).nsplit == 32);
+    EXPECT(plan_latent(32, 64, 8192).head_groups == 1 && plan_latent(32, 64, 8192).nsplit == 8);
+  }
   if (failures) {
     std::printf("%d failures\n", failures);
     return 1;
