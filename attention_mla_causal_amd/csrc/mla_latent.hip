@@ -515,8 +515,9 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
 // Out_h^T [128 x 8] = W_v[h] [128 x 512] . O~_h^T [512 x 8] on
 // v_mfma_f32_16x16x32_bf16, wave w computes 16 output dims over 512 / C of
 // the contraction (C waves per 16 dims, their sums added in LDS). W_v's
-// contraction dim is contiguous, so its fragments load straight from HBM, at
-// the start, while the merge runs; o~ (merged in fp32) enters as two bf16 operands,
+// contraction dim is contiguous, so its fragments load straight from HBM,
+// right after the first batch of partials (whose merge thus waits for the
+// partials alone) and while the merge runs; o~ (merged in fp32) enters as two bf16 operands,
 // hi = bf16(x) and lo = bf16(x - hi), whose sum carries x to about 2^-17
 // relative. The host picks C so that about 256 workgroups run: with few
 // sequences the head's weight rows are spread over C workgroups (each merging
@@ -526,9 +527,13 @@ constexpr int OUT_BG = 8;     // sequences per workgroup (MFMA columns 8..15 sta
 constexpr int OUT_WAVES = 8;
 constexpr int OROW = R + 4;   // floats per LDS row: 2064 bytes, so the 16-byte reads of
                               // eight rows at one offset meet distinct banks
-template <int C>
+// U: splits a wave loads in one batch (the host takes 8 when a wave merges
+// more than four, so the batched decode's eight splits per sequence arrive in
+// one round trip, else 4).
+template <int C, int U>
 __global__ __launch_bounds__(512) void latent_out_kernel(LatentArgs a) {
   static_assert(C == 1 || C == 2 || C == 4, "C divides the 8 waves and the 16 K-steps");
+  static_assert(U == 4 || U == 8, "splits per batch");
   constexpr int TILES = OUT_WAVES / C;  // 16-dim output tiles per workgroup
   constexpr int KS = R / 32 / C;        // K-steps per wave
   __shared__ __attribute__((aligned(16))) float part[OUT_WAVES][OROW];
@@ -543,9 +548,6 @@ __global__ __launch_bounds__(512) void latent_out_kernel(LatentArgs a) {
   const int tile = wave % TILES, epart = wave / TILES;
   const int d0 = chunk * (DV / C) + 16 * tile;
   const uint16_t* wrow = a.w_kv_b + ((int64_t)h * KVB + DN + d0 + j) * R + 8 * g + 32 * KS * epart;
-  u32x4 wf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) wf[ks] = *reinterpret_cast<const u32x4*>(wrow + 32 * ks);
 
   // merge: wave w takes sequence slot w / wpb and splits s = w % wpb (mod wpb)
   const int nb = (a.B - b0 < OUT_BG) ? a.B - b0 : OUT_BG;  // live sequences, >= 1
@@ -557,46 +559,63 @@ __global__ __launch_bounds__(512) void latent_out_kernel(LatentArgs a) {
   // leaving (max, sum) and its unnormalised sum in LDS.
   f32x4 o0 = {0.0f, 0.0f, 0.0f, 0.0f}, o1 = o0;
   float mrun = -INFINITY, lsum = 0.0f;
-  if (slot < nb) {
-    const int64_t row0 = (int64_t)(b0 + slot) * a.nsplit * a.H + h;  // split s: row0 + s * H
-    constexpr int U = 4;
-    for (int s0 = sub; s0 < a.nsplit; s0 += U * wpb) {
-      float ms[U], ls[U];
-      f32x4 p0[U], p1[U];
+  const bool live = slot < nb;
+  const int64_t row0 = (int64_t)(b0 + (live ? slot : 0)) * a.nsplit * a.H + h;  // split s: row0 + s * H
+  float ms[U], ls[U];
+  f32x4 p0[U], p1[U];
+  // loads of the splits s0, s0 + wpb, ...; rows past the end (or of a wave
+  // with no sequence) reread split 0 and take no weight
+  auto load_batch = [&](int s0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int s = s0 + u * wpb;
-        const int64_t row = row0 + (int64_t)(s < a.nsplit ? s : s0) * a.H;
-        const float2 ml = *reinterpret_cast<const float2*>(a.pml + 2 * row);
-        ms[u] = s < a.nsplit ? ml.x : -INFINITY;
-        ls[u] = ml.y;
-        const uint16_t* src = a.po + row * R + 4 * lane;  // bf16 dims 4 lane .. and 256 + 4 lane ..
-        const bf16x4 q0 = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(src));
-        const bf16x4 q1 = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(src + R / 2));
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * wpb;
+      const bool ok = live && s < a.nsplit;
+      const int64_t row = row0 + (int64_t)(ok ? s : 0) * a.H;
+      const float2 ml = *reinterpret_cast<const float2*>(a.pml + 2 * row);
+      ms[u] = ok ? ml.x : -INFINITY;
+      ls[u] = ml.y;
+      const uint16_t* src = a.po + row * R + 4 * lane;  // bf16 dims 4 lane .. and 256 + 4 lane ..
+      const bf16x4 q0 = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(src));
+      const bf16x4 q1 = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(src + R / 2));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p0[u][e] = (float)q0[e];
-          p1[u][e] = (float)q1[e];
-        }
+      for (int e = 0; e < 4; ++e) {
+        p0[u][e] = (float)q0[e];
+        p1[u][e] = (float)q1[e];
       }
-      float mnew = mrun;
+    }
+  };
+  auto fold_batch = [&]() {
+    float mnew = mrun;
 #pragma unroll
-      for (int u = 0; u < U; ++u) mnew = fmaxf(mnew, ms[u]);
-      const float al = __builtin_amdgcn_exp2f(mrun - mnew);  // mnew is finite: split s0 is live
-      lsum *= al;
-      o0 *= al;
-      o1 *= al;
+    for (int u = 0; u < U; ++u) mnew = fmaxf(mnew, ms[u]);
+    const float al = __builtin_amdgcn_exp2f(mrun - mnew);  // mnew is finite: the batch's first split is live
+    lsum *= al;
+    o0 *= al;
+    o1 *= al;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float w = __builtin_amdgcn_exp2f(ms[u] - mnew);  // 0 for splits past the end
-        lsum = __builtin_fmaf(w, ls[u], lsum);
+    for (int u = 0; u < U; ++u) {
+      const float w = __builtin_amdgcn_exp2f(ms[u] - mnew);  // 0 for splits past the end
+      lsum = __builtin_fmaf(w, ls[u], lsum);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          o0[e] = __builtin_fmaf(w, p0[u][e], o0[e]);
-          o1[e] = __builtin_fmaf(w, p1[u][e], o1[e]);
-        }
+      for (int e = 0; e < 4; ++e) {
+        o0[e] = __builtin_fmaf(w, p0[u][e], o0[e]);
+        o1[e] = __builtin_fmaf(w, p1[u][e], o1[e]);
       }
-      mrun = mnew;
+    }
+    mrun = mnew;
+  };
+  load_batch(sub);
+  // W_v's fragments load after the first batch of partials, so the merge
+  // waits for those alone
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 wf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) wf[ks] = *reinterpret_cast<const u32x4*>(wrow + 32 * ks);
+  if (live && sub < a.nsplit) {
+    fold_batch();
+    for (int s0 = sub + U * wpb; s0 < a.nsplit; s0 += U * wpb) {
+      load_batch(s0);
+      fold_batch();
     }
   }
   *reinterpret_cast<f32x4*>(&part[wave][4 * lane]) = o0;
@@ -677,12 +696,20 @@ hipError_t launch_latent_decode(const LatentArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(latent_attn_kernel<1>, dim3(a.B * a.nsplit * a.head_groups), dim3(256), 0, stream, a);
   // merge + up-projection: C workgroups per (head, eight sequences), about 256 in all
   const int groups = (a.B + OUT_BG - 1) / OUT_BG * a.H;
-  if (groups >= 256)
-    hipLaunchKernelGGL(latent_out_kernel<1>, dim3(groups), dim3(512), 0, stream, a);
-  else if (groups >= 128)
-    hipLaunchKernelGGL(latent_out_kernel<2>, dim3(groups * 2), dim3(512), 0, stream, a);
-  else
-    hipLaunchKernelGGL(latent_out_kernel<4>, dim3(groups * 4), dim3(512), 0, stream, a);
+  // splits each wave merges when a workgroup holds min(B, 8) sequences
+  const int nb = a.B < OUT_BG ? a.B : OUT_BG;
+  const int wpb = OUT_WAVES / (nb > 4 ? 8 : (nb > 2 ? 4 : nb));
+  const bool u8 = (a.nsplit + wpb - 1) / wpb > 4;
+  if (groups >= 256) {
+    if (u8) hipLaunchKernelGGL((latent_out_kernel<1, 8>), dim3(groups), dim3(512), 0, stream, a);
+    else hipLaunchKernelGGL((latent_out_kernel<1, 4>), dim3(groups), dim3(512), 0, stream, a);
+  } else if (groups >= 128) {
+    if (u8) hipLaunchKernelGGL((latent_out_kernel<2, 8>), dim3(groups * 2), dim3(512), 0, stream, a);
+    else hipLaunchKernelGGL((latent_out_kernel<2, 4>), dim3(groups * 2), dim3(512), 0, stream, a);
+  } else {
+    if (u8) hipLaunchKernelGGL((latent_out_kernel<4, 8>), dim3(groups * 4), dim3(512), 0, stream, a);
+    else hipLaunchKernelGGL((latent_out_kernel<4, 4>), dim3(groups * 4), dim3(512), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
