@@ -217,3 +217,28 @@ def test_full_size_workload_sampled():
     for b in range(wl.B):
         assert not torch.any(out[b, :, int(tq[b]):] != 0).item(), b
     assert torch.isfinite(out).all().item()
+
+
+def _random_prefill_varlen_cases(n, seed):
+    g = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        B, H = int(g.integers(1, 5)), int(g.integers(1, 17))
+        Tmax = int(g.integers(1, 301))
+        Smax = Tmax + int(g.integers(0, 1201))
+        tq = [int(v) for v in g.integers(0, Tmax + 1, size=B)]
+        pp = [int(g.integers(0, Smax - t + 1)) for t in tq]
+        cases.append((B, H, Tmax, Smax, tq, pp))
+    return cases
+
+
+@pytest.mark.parametrize("B,H,Tmax,Smax,tq,pp", _random_prefill_varlen_cases(6, 2030))
+def test_random_shapes(B, H, Tmax, Smax, tq, pp):
+    """Seeded random padded shapes and per-sequence lengths, padded rows NaN."""
+    log(f"case prefill varlen random B={B} H={H} Tmax={Tmax} Smax={Smax} q={tq} past={pp}")
+    x = _inputs(B, H, Tmax, Smax, B * 31 + H + Tmax + Smax, tq, pp)
+    out = _gpu(upload(x), tq, pp)
+    bits = to_host_bits(out)
+    for b in range(B):
+        assert not np.any(bits[b, :, tq[b]:]), b
+    assert_parity(to_host_f64(out), _oracle(x, tq, pp), "prefill varlen random")

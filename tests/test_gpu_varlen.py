@@ -172,3 +172,27 @@ def test_varlen_batched_full_size_sampled():
                                           np.array([L]), ALPHA, [(0, 0)])[0])
         got.append(to_host_f64(out[b, h, 0]))
     assert_parity(np.stack(got), np.stack(ref), "varlen batched sampled")
+
+
+def _random_varlen_cases(n, seed):
+    g = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        B, H, cap = int(g.integers(1, 13)), int(g.integers(1, 65)), int(g.integers(1, 3001))
+        lens = [int(v) for v in g.integers(-2, cap + 3, size=B)]  # a few outside [0, cap]: clamped
+        cases.append((B, H, cap, lens))
+    return cases
+
+
+@pytest.mark.parametrize("B,H,cap,lens", _random_varlen_cases(8, 2029))
+def test_varlen_random_shapes(B, H, cap, lens):
+    """Seeded random batch sizes, head counts, cache lengths and per-sequence
+    lengths (max_seq_len = cache length), rows past each length NaN."""
+    log(f"case varlen random B={B} H={H} cap={cap} lens={lens}")
+    eff = [max(0, min(L, cap)) for L in lens]
+    x = _cache(B, H, cap, B * 13 + H * 7 + cap, eff)
+    out = _gpu(upload(x), lens, cap)
+    assert_parity(to_host_f64(out), _oracle(x, eff), f"varlen random {B},{H},{cap}")
+    for b, L in enumerate(eff):
+        if L == 0:
+            assert not np.any(to_host_bits(out)[b])
