@@ -200,3 +200,29 @@ def test_paged_batched_full_size_sampled():
         assert np.array_equal(to_host_bits(d["k_nope_pages"][blk, h, row]), sub["k_nope_new"][0, 0, 0])
         assert np.array_equal(to_host_bits(d["k_pe_pages"][blk, row]), sub["k_pe_new"][0, 0, 0])
     assert_parity(np.stack(got), np.stack(ref), "paged batched sampled")
+
+
+def _random_paged_cases(n, seed):
+    g = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        B, H = int(g.integers(1, 7)), int(g.integers(1, 65))
+        bs = 32 * int(g.integers(1, 5))
+        lens = [int(v) for v in g.integers(0, 2500, size=B)]
+        cases.append((lens, H, bs, bool(g.integers(0, 2))))
+    return cases
+
+
+@pytest.mark.parametrize("lens,H,bs,append", _random_paged_cases(6, 2031))
+def test_paged_random_shapes(lens, H, bs, append):
+    """Seeded random lengths, head counts and block sizes (multiples of 32),
+    with and without the fused append; rows no sequence owns hold NaN."""
+    seed = sum(lens) + 3 * H + bs
+    x, table, N = _setup(lens, H, bs, seed)
+    log(f"case paged random lens={lens} H={H} bs={bs} blocks={N} append={append}")
+    d = upload(x)
+    out = _call(d, table, lens, max(max(lens), 1), append)
+    ref, pages = _oracle(x, table, lens, append)
+    assert_parity(to_host_f64(out), ref, f"paged random {lens} H={H} bs={bs} append={append}")
+    for k, want in zip(PAGE_KEYS, pages):
+        assert np.array_equal(to_host_bits(d[k]), want), f"{k} after the call"
