@@ -47,10 +47,13 @@ def test_latent_decode_as_on_the_pages():
 # group part-filled at 63); 8 sequences take the placement that keeps a
 # sequence's splits and head groups on one XCD. From five sequences on, the
 # absorb stages query and output rows through LDS: 5 (the first such batch)
-# and 17 (a second group of 16 holding one sequence).
+# and 17 (a second group of 16 holding one sequence). More sequences than
+# CUs: 300 (all-heads workgroups, one split each, a part-filled last group of
+# eight in the merge) and 264 x 64 heads (one head group per workgroup, 1056
+# workgroups).
 EDGE = [(1, 16, 0), (1, 64, 30), (2, 32, 31), (1, 48, 32), (3, 64, 777), (2, 16, 4095), (4, 64, 2000),
         (2, 8, 500), (3, 1, 40), (1, 20, 63), (1, 63, 1000), (8, 64, 1000), (1, 64, 0), (5, 64, 40),
-        (17, 8, 100)]
+        (17, 8, 100), (300, 8, 40), (264, 64, 31)]
 
 
 @pytest.mark.parametrize("B,H,P", EDGE)
