@@ -519,14 +519,16 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
     // kWindow groups at a time: the window's query tiles heaviest first
     // across its groups, so its K/V streams through that XCD's L2 while it
     // runs. (One group at a time left the heaviest tiles of each XCD's last
-    // groups to start near the end: windows of four took the 2D-mask prefill
-    // from 1.065 to 1.019 ms and the padded batch from 4.15 to 4.00 ms, outputs
-    // bit-identical; windows of 16 groups, or all of an XCD's, lost that again
-    // to K/V re-read past L2.)
+    // groups to start near the end. Windows of four took the 2D-mask prefill
+    // from 1.065 to 1.019 ms (HBM reads +23%); on the padded batch, whose
+    // sequences are four times longer, windows of two gain 3% (reads +17%)
+    // where four read 65% more for no more gain. Outputs bit-identical.
+    // Windows of 16 groups, or all of an XCD's, lose it all to K/V re-read
+    // past L2.)
     // With a 2D mask the padding, and so the work, differs by sequence in a
     // way the grid cannot see: the groups are dealt round-robin over the XCDs
     // the same way, in index order.
-    constexpr int kWindow = 4;
+    constexpr int kWindow = MASKED ? 4 : 2;
     const int G = a.B * a.H;
     int gi, t;
     if (G % (8 * kWindow) == 0) {
