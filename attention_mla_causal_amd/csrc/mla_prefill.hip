@@ -508,8 +508,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   // Each XCD (wg % 8) takes a contiguous range of heads. When query tiles
   // differ a lot in work (few cached keys: the causal triangle dominates), the
   // XCD dispatches its tiles heaviest first across all of its heads
-  // (longest-job-first); otherwise head by head, heaviest tile first, so a
-  // head's K/V streams through the XCD's L2 for all its tiles at once.
+  // (longest-job-first); otherwise heaviest first across windows of eight
+  // heads, so the window's K/V streams through the XCD's L2 together.
   int bh, qt, sp = 0;
   const bool uneven = 2 * (a.past_len + (int64_t)BM) < a.past_len + (int64_t)a.T;
   if (VARLEN || MASKED) {
@@ -555,10 +555,17 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
       const int rest = logical / a.nsplit;
       bh = rest / a.ntiles;
       qt = a.ntiles - 1 - rest % a.ntiles;
-    } else if (nwg % 8 == 0 && per % a.ntiles == 0 && uneven) {
+    } else if (nwg % 8 == 0 && per % a.ntiles == 0 && (uneven || (per / a.ntiles) % 8 == 0)) {
+      // heaviest tile first across all of the XCD's heads (uneven tiles), or
+      // across windows of eight heads (near-equal tiles: the window's K/V
+      // streams through L2 together; head by head left the lightest tiles of
+      // the last head to the end: 2048 queries over 14336 cached keys, 64
+      // heads, 1196 -> 1168 us, same process, outputs bit-identical)
       const int nh = per / a.ntiles;
-      bh = (wg % 8) * nh + i % nh;
-      qt = a.ntiles - 1 - i / nh;
+      const int W = uneven ? nh : 8;
+      const int r = i % (W * a.ntiles);
+      bh = (wg % 8) * nh + (i / (W * a.ntiles)) * W + r % W;
+      qt = a.ntiles - 1 - r / W;
     } else {
       const int logical = (nwg % 8 == 0) ? (wg % 8) * per + i : wg;
       bh = logical / a.ntiles;
