@@ -508,7 +508,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   // Each XCD (wg % 8) takes a contiguous range of heads. When query tiles
   // differ a lot in work (few cached keys: the causal triangle dominates), the
   // XCD dispatches its tiles heaviest first across all of its heads
-  // (longest-job-first); otherwise heaviest first across windows of eight
+  // (longest-job-first); otherwise heaviest first across windows of four
   // heads, so the window's K/V streams through the XCD's L2 together.
   int bh, qt, sp = 0;
   const bool uneven = 2 * (a.past_len + (int64_t)BM) < a.past_len + (int64_t)a.T;
@@ -555,14 +555,18 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
       const int rest = logical / a.nsplit;
       bh = rest / a.ntiles;
       qt = a.ntiles - 1 - rest % a.ntiles;
-    } else if (nwg % 8 == 0 && per % a.ntiles == 0 && (uneven || (per / a.ntiles) % 8 == 0)) {
+    } else if (nwg % 8 == 0 && per % a.ntiles == 0 && (uneven || (per / a.ntiles) % 4 == 0)) {
       // heaviest tile first across all of the XCD's heads (uneven tiles), or
-      // across windows of eight heads (near-equal tiles: the window's K/V
-      // streams through L2 together; head by head left the lightest tiles of
-      // the last head to the end: 2048 queries over 14336 cached keys, 64
-      // heads, 1196 -> 1168 us, same process, outputs bit-identical)
+      // across windows of four heads (near-equal tiles). Every tile of an
+      // XCD is resident at once and the XCD deals them to its 32 CUs in turn,
+      // so windows of four put two tiles of one head on each CU. Against head
+      // by head (four heads per CU) this took 2048 queries over 14336 cached
+      // keys, 64 heads, from 1203 to 1185 us in the same process, outputs
+      // bit-identical, with 60% more L2 misses (still under a tenth of HBM
+      // peak); windows of eight were no faster and missed L2 three times as
+      // often as head by head, windows of two no faster than head by head.
       const int nh = per / a.ntiles;
-      const int W = uneven ? nh : 8;
+      const int W = uneven ? nh : 4;
       const int r = i % (W * a.ntiles);
       bh = (wg % 8) * nh + (i / (W * a.ntiles)) * W + r % W;
       qt = a.ntiles - 1 - r / W;
