@@ -505,11 +505,12 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   // ---- which (batch, head, query tile) this workgroup owns
   const int nwg = gridDim.x;
   const int wg = blockIdx.x;
-  // Each XCD (wg % 8) takes a contiguous range of heads. When query tiles
-  // differ a lot in work (few cached keys: the causal triangle dominates), the
-  // XCD dispatches its tiles heaviest first across all of its heads
-  // (longest-job-first); otherwise heaviest first across windows of four
-  // heads, so the window's K/V streams through the XCD's L2 together.
+  // Each XCD (wg % 8) takes a contiguous range of heads and dispatches their
+  // query tiles heaviest first (longest-job-first) across windows of four
+  // heads, so the window's K/V streams through the XCD's L2 together; when
+  // the XCD's head count is not a multiple of four, across all of its heads
+  // if the tiles differ a lot in work (few cached keys: the causal triangle
+  // dominates), else head by head.
   int bh, qt, sp = 0;
   const bool uneven = 2 * (a.past_len + (int64_t)BM) < a.past_len + (int64_t)a.T;
   if (VARLEN || MASKED) {
@@ -556,17 +557,17 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
       bh = rest / a.ntiles;
       qt = a.ntiles - 1 - rest % a.ntiles;
     } else if (nwg % 8 == 0 && per % a.ntiles == 0 && (uneven || (per / a.ntiles) % 4 == 0)) {
-      // heaviest tile first across all of the XCD's heads (uneven tiles), or
-      // across windows of four heads (near-equal tiles). Every tile of an
-      // XCD is resident at once and the XCD deals them to its 32 CUs in turn,
-      // so windows of four put two tiles of one head on each CU. Against head
-      // by head (four heads per CU) this took 2048 queries over 14336 cached
-      // keys, 64 heads, from 1203 to 1185 us in the same process, outputs
-      // bit-identical, with 60% more L2 misses (still under a tenth of HBM
-      // peak); windows of eight were no faster and missed L2 three times as
-      // often as head by head, windows of two no faster than head by head.
+      // An XCD deals its workgroups to its 32 CUs in turn, two resident per
+      // CU, so a window of four heads puts two tiles of one head on each CU
+      // of the first round. Same process, outputs bit-identical: 2048 queries
+      // over 14336 cached keys, 64 heads: 1203 us head by head (four heads
+      // per CU), 1185 us in windows of four (L2 misses +60%, still under a
+      // tenth of HBM peak); windows of two no faster than head by head,
+      // windows of eight no faster than four with three times the misses of
+      // head by head. 4096 queries, no cached keys: windows of four 1%
+      // faster than all eight heads of the XCD at once, 35% fewer L2 misses.
       const int nh = per / a.ntiles;
-      const int W = uneven ? nh : 4;
+      const int W = nh % 4 == 0 ? 4 : nh;
       const int r = i % (W * a.ntiles);
       bh = (wg % 8) * nh + (i / (W * a.ntiles)) * W + r % W;
       qt = a.ntiles - 1 - r / W;
