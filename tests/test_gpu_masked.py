@@ -71,11 +71,15 @@ def _left_pad_mask(S, pads):
 
 # (B, H, T, P, left pads per sequence): pads inside the cache, pads reaching
 # into the new queries (their first rows see nothing and give 0), no pad, a
-# whole sequence of padding; several query tiles with a ragged tail.
+# whole sequence of padding; several query tiles with a ragged tail. The
+# (batch, head) groups take each branch of the workgroup order: 12 and 4
+# (not a multiple of 8: index order), 24 (a multiple of 8 but not of 32: one
+# group at a time per XCD), 64 (windows of four groups per XCD).
 PREFILL_LEFT = [
     (3, 4, 200, 77, [0, 40, 150]),
     (2, 2, 130, 0, [5, 130]),
     (1, 64, 33, 100, [99]),
+    (3, 8, 300, 60, [0, 200, 5]),
 ]
 
 

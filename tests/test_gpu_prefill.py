@@ -62,6 +62,32 @@ def test_edge_shapes(B, H, T, P):
     assert_parity(to_host_f64(out), _oracle(x, P), f"edge {B},{H},{T},{P}")
 
 
+# (B, H, T, past_len) through each branch of the workgroup order, whose grid is
+# a multiple of 8 (every XCD holds whole heads): tiles of uneven work (the
+# causal triangle dominates) over 3, 4, 5 and 8 heads per XCD (all of them at
+# once when not a multiple of four, else windows of four); near-equal tiles
+# over 2 heads per XCD (head by head), 4, 8 and 12 (windows of four, one to
+# three of them).
+PLACEMENT_SHAPES = [
+    (1, 24, 384, 0),
+    (1, 32, 384, 0),
+    (1, 40, 512, 0),
+    (1, 64, 384, 0),
+    (1, 16, 256, 1500),
+    (1, 32, 256, 1500),
+    (1, 64, 256, 1500),
+    (2, 48, 130, 20),
+]
+
+
+@pytest.mark.parametrize("B,H,T,P", PLACEMENT_SHAPES)
+def test_placement_branches(B, H, T, P):
+    log(f"case placement B={B} H={H} T={T} P={P}")
+    x = random_inputs(B, H, T, P, seed=B * 7 + H * 5 + T * 3 + P)
+    out = _gpu_prefill(x, P)
+    assert_parity(to_host_f64(out), _oracle(x, P), f"placement {B},{H},{T},{P}")
+
+
 @pytest.mark.parametrize("std", [2.0, 4.0])
 def test_sharp_softmax(std):
     """Large logits (scaled-logit std 2 and 4): stresses the running max."""

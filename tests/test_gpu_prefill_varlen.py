@@ -69,13 +69,15 @@ def test_mixed_lengths_with_nan_padding():
 # (B, H, Tmax, Smax, q_lens, past_lens): ragged query tiles and key tiles,
 # sequences with no queries, one query, a cache that is and is not a multiple
 # of the 32-key tile, and lengths outside their ranges (clamped on the device:
-# T_b to [0, Tmax], P_b to [0, Smax - T_b]).
+# T_b to [0, Tmax], P_b to [0, Smax - T_b]); 24 (batch, head) groups, a
+# multiple of 8 but not of 16 (one group at a time per XCD, not windows).
 EDGE = [
     (2, 3, 129, 129, [129, 128], [0, 1]),
     (3, 2, 257, 600, [1, 256, 257], [599, 32, 343]),
     (2, 5, 64, 1000, [0, 64], [0, 936]),
     (1, 64, 17, 17, [17], [0]),
     (3, 4, 200, 400, [300, -3, 150], [0, 7, 9999]),
+    (3, 8, 300, 700, [300, 1, 170], [400, 0, 77]),
 ]
 
 
