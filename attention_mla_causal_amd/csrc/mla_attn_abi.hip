@@ -237,7 +237,6 @@ mla_status mla_attn_prefill_ws(const void* q_nope, const void* q_pe, const void*
   a.ntiles = (int32_t)((T + mla::prefill_block_m() - 1) / mla::prefill_block_m());
   a.scale_log2 = softmax_scale * kLog2e;
   a.nsplit = (int32_t)plan.nsplit;
-  a.tiles_per_split = (int32_t)plan.tiles_per_split;
   if (plan.nsplit > 1) {
     char* ws = static_cast<char*>(workspace);
     a.ws_o = reinterpret_cast<float*>(ws);

@@ -182,14 +182,16 @@ inline CheckResult check_common(const void* q_nope, const void* q_pe, const void
 // Prefill key-range split: when B*H*ceil(T/block_m) workgroups would leave
 // the GPU part-empty (it holds two per CU), each query tile's keys are split
 // over several workgroups, each writing an fp32 partial that a second kernel
-// merges.
+// merges. The plan fixes the number of ranges from the whole key count; the
+// kernel cuts the keys each query tile sees into that many near-equal ranges
+// (no longer than tiles_per_split).
 constexpr int64_t kPrefillTargetWorkgroups = 512;
 constexpr int64_t kPrefillMinTilesPerSplit = 16;  // 512 keys: pipeline fill and drain stay small
 constexpr int64_t kPrefillMaxSplits = 16;  // the merge kernel holds at most 16 partials per row
 
 struct PrefillPlan {
   int64_t nsplit = 1;           // key ranges per query tile
-  int64_t tiles_per_split = 0;  // key tiles (kPrefillKeyTile keys) per range
+  int64_t tiles_per_split = 0;  // key tiles (kPrefillKeyTile keys) per range of the whole key count
   size_t ws_o_bytes = 0;        // fp32 [B*H*T, nsplit, 128]
   size_t ws_ml_bytes = 0;       // fp32 [B*H*T, nsplit, 2]
   size_t workspace_bytes = 0;

@@ -21,10 +21,10 @@ struct PrefillArgs {
   int32_t B, H, T, S, past_len;
   int32_t ntiles;          // ceil(T / prefill_block_m())
   float scale_log2;        // softmax_scale * log2(e)
-  // Key-range split: nsplit > 1 gives each workgroup key tiles
-  // [sp * tiles_per_split, +tiles_per_split) of its query tile; it writes an
-  // fp32 partial, merged by a second kernel into out.
-  int32_t nsplit, tiles_per_split;
+  // Key-range split: nsplit > 1 cuts the key tiles a query tile sees into
+  // nsplit near-equal ranges, one per workgroup; each writes an fp32
+  // partial, merged by a second kernel into out.
+  int32_t nsplit;
   float* ws_o;             // [B*H*T, nsplit, 128] partial outputs (unnormalised)
   float* ws_ml;            // [B*H*T, nsplit, 2] partial (max, sum), max in the scaled log2 domain
   // Padded variable-length batch (both null otherwise): T and S are then the

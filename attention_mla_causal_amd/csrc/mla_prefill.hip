@@ -550,12 +550,18 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
     const int per = nwg / 8, i = wg / 8;
     if (SPLIT) {
       // key-range splits of one query tile are adjacent (same XCD when the
-      // grid is a multiple of 8), then query tiles, then heads
+      // grid is a multiple of 8), then query tiles, then heads. A head's
+      // query tiles run heaviest first over the first half of its positions
+      // and lightest first over the second, so the two workgroups an XCD
+      // deals to one CU (positions k and k + 32 of its 64) pair a heavy tile
+      // with a light one (plain heaviest first: 4096 queries without cached
+      // keys, 8 heads, 75.0 -> 70.5 us, same process).
       const int logical = (nwg % 8 == 0) ? (wg % 8) * per + i : wg;
       sp = logical % a.nsplit;
       const int rest = logical / a.nsplit;
       bh = rest / a.ntiles;
-      qt = a.ntiles - 1 - rest % a.ntiles;
+      const int k = rest % a.ntiles, h1 = (a.ntiles + 1) / 2;
+      qt = k < h1 ? a.ntiles - 1 - k : k - h1;
     } else if (nwg % 8 == 0 && per % a.ntiles == 0 && (uneven || (per / a.ntiles) % 4 == 0)) {
       // An XCD deals its workgroups to its 32 CUs in turn, two resident per
       // CU, so a window of four heads puts two tiles of one head on each CU
@@ -606,8 +612,12 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   const int nblocks_all = (int)((past + q_last + 1 + BN - 1) / BN);
   int kt0 = 0, kt1 = nblocks_all;
   if (SPLIT) {
-    kt0 = sp * a.tiles_per_split;
-    kt1 = kt0 + a.tiles_per_split < nblocks_all ? kt0 + a.tiles_per_split : nblocks_all;
+    // the tile's visible key tiles in nsplit near-equal ranges (ranges of the
+    // whole key count left the last range of every tile light: 4096 queries
+    // without cached keys, 8 heads, 79.8 -> 75.0 us, same process)
+    const int tps = (nblocks_all + a.nsplit - 1) / a.nsplit;
+    kt0 = sp * tps;
+    kt1 = kt0 + tps < nblocks_all ? kt0 + tps : nblocks_all;
   }
   if (MASKED) {
     // only the tiles between the first and the last key the 2D mask keeps
