@@ -34,12 +34,11 @@
 //    64-byte column blocks whose 16-byte chunks are XOR-swizzled by row, which
 //    keeps both the copies and the operand reads free of bank conflicts and
 //    makes every operand read an immediate offset from two base registers.
-//  * Workgroup order: all query tiles of one head are placed on one XCD; with
-//    many cached keys they are dispatched head by head (K/V blocks stream
-//    through that XCD's L2 once for all of a head's tiles), and when the causal
-//    triangle dominates, heaviest tile first across the XCD's heads. In a
-//    padded batch of sequences of different lengths, (batch, head) pairs are
-//    dealt round-robin over the XCDs and run longest sequence first.
+//  * Workgroup order: all query tiles of one head are placed on one XCD and
+//    dispatched heaviest tile first across windows of four heads, whose K/V
+//    blocks stream through that XCD's L2 together. In a padded batch of
+//    sequences of different lengths, (batch, head) pairs are dealt round-robin
+//    over the XCDs and run longest sequence first, in windows of a few pairs.
 //  * Four instantiations of one body: all keys per query tile (the common
 //    case), key-range splits merged by a second kernel (small grids), a padded
 //    variable-length batch (lengths read on the device), and the caller's 2D

@@ -94,9 +94,10 @@ size_t mla_attn_prefill_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t
 /*
  * mla_attn_prefill with a workspace: the same result (up to the order of
  * rounding). When B*H*ceil(T/128) workgroups would leave the GPU part-empty
- * (fewer than 512: it holds two per CU), the keys of each query tile are split
- * into ranges of whole 32-key tiles (at least 512 keys, at most 16 ranges),
- * each range's workgroup writes an fp32 partial (unnormalised output, max and
+ * (fewer than 512: it holds two per CU), the keys each query tile sees are
+ * split into near-equal ranges of whole 32-key tiles (as many ranges as
+ * 512-key pieces of S, at most 16, and no more than fill the GPU); each
+ * range's workgroup writes an fp32 partial (unnormalised output, max and
  * sum per query) to the workspace, and a second kernel merges the partials by
  * log-sum-exp into out. Otherwise it is exactly mla_attn_prefill.
  * workspace: caller-owned device scratch of at least
