@@ -87,13 +87,15 @@ typedef __attribute__((address_space(3))) void lds_void;
 // [S, ROWBYTES/2] bf16 tensor. Loads past the last row return zeros (hardware
 // range check), so the tile copies need no clamping. Built from uniform values
 // only: scalar instructions.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* slice, int64_t kb,
-                                                           int64_t S, int rowbytes) {
-  // (S * rowbytes < 2^31: the host caps S, so the byte count fits 32 bits)
-  const int64_t left = S - kb;
-  const int records = left > 0 ? (int)(left * rowbytes) : 0;
-  return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)slice + kb * rowbytes), (short)0,
-                                           records, 0x00020000);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* slice, int kb, int S,
+                                                           int rowbytes) {
+  // 32-bit scalar arithmetic (a 64-bit compare would go through the VALU):
+  // S * rowbytes < 2^31 (the host caps S) and kb <= S + 2 * BN, so the row
+  // offset kb * rowbytes fits 32 bits unsigned.
+  const int left = S - kb;
+  const int records = left > 0 ? left * rowbytes : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)slice + (uint32_t)kb * (uint32_t)rowbytes), (short)0, records, 0x00020000);
 }
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
@@ -162,7 +164,7 @@ struct Region {
       voff[u] = r * ROWLEN * 2 + (cb * 4 + c4) * 16;
     }
   }
-  __device__ __forceinline__ void copy(const uint16_t* slice, int64_t kb, int64_t S, char* lds,
+  __device__ __forceinline__ void copy(const uint16_t* slice, int kb, int S, char* lds,
                                        int wave) const {
     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(slice, kb, S, ROWLEN * 2);
 #pragma unroll
@@ -177,6 +179,7 @@ struct Geo {
   const uint16_t* kp_g;
   const uint16_t* v_g;
   int64_t S, P;
+  int S32;  // S as a 32-bit count, for the copies' scalar arithmetic
   int wave, lane;
   Region<DN, 4> kn;
   Region<DR, 2> kp;
@@ -184,13 +187,13 @@ struct Geo {
 };
 
 __device__ __forceinline__ void copy_k(const Geo& g, int j, char* kbuf) {
-  const int64_t kb = (int64_t)j * BN;
-  g.kn.copy(g.kn_g, kb, g.S, kbuf, g.wave);
-  g.kp.copy(g.kp_g, kb, g.S, kbuf + KN_BYTES, g.wave);
+  const int kb = j * BN;
+  g.kn.copy(g.kn_g, kb, g.S32, kbuf, g.wave);
+  g.kp.copy(g.kp_g, kb, g.S32, kbuf + KN_BYTES, g.wave);
 }
 
 __device__ __forceinline__ void copy_v(const Geo& g, int j, char* vbuf) {
-  g.vv.copy(g.v_g, (int64_t)j * BN, g.S, vbuf, g.wave);
+  g.vv.copy(g.v_g, j * BN, g.S32, vbuf, g.wave);
 }
 
 // Per-lane LDS operand offsets (bytes) for the region layout above.
@@ -642,6 +645,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   // query sees no key of this range).
   const int64_t k0 = (int64_t)kt0 * BN;
   geo.S = S_seq - k0;
+  geo.S32 = (int)geo.S;
   geo.P = past - k0;
   geo.kn_g = a.k_nope + (int64_t)bh * Sst * DN + k0 * DN;
   geo.kp_g = a.k_pe + (int64_t)b * Sst * DR + k0 * DR;
