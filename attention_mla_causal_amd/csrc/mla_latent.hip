@@ -209,13 +209,15 @@ __device__ __forceinline__ int tile_swz(int r) {
 
 // Buffer resource over rows [kb, end) of one sequence's row-major
 // [S, rowbytes/2] bf16 tensor; rows at or past `end` read as zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* seq, int64_t kb,
-                                                           int64_t end, int rowbytes) {
-  // (end * rowbytes < 2^31: the host caps S, so the byte count fits 32 bits)
-  const int64_t left = end - kb;
-  const int records = left > 0 ? (int)(left * rowbytes) : 0;
-  return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)seq + kb * rowbytes), (short)0,
-                                           records, 0x00020000);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* seq, int kb, int end,
+                                                           int rowbytes) {
+  // 32-bit scalar arithmetic (a 64-bit compare would go through the VALU):
+  // end * rowbytes < 2^31 (the host caps S) and kb <= end + 2 * BN, so the
+  // row offset kb * rowbytes fits 32 bits unsigned.
+  const int left = end - kb;
+  const int records = left > 0 ? left * rowbytes : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)seq + (uint32_t)kb * (uint32_t)rowbytes), (short)0, records, 0x00020000);
 }
 
 // The softmax takes the running max of the unscaled scores and scales it by
@@ -290,9 +292,10 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, j = lane & 15;
   const int64_t S = a.S, H = a.H;
-  const int64_t k0 = (int64_t)split * a.keys_per_split;
-  const int64_t k1 = (k0 + a.keys_per_split < S) ? k0 + a.keys_per_split : S;
-  const int ntiles = (int)((k1 - k0 + BN - 1) / BN);
+  // key counts fit 32 bits (the host caps S); per-lane key tests stay 32-bit
+  const int k0 = split * (int)a.keys_per_split;
+  const int k1 = (k0 + (int)a.keys_per_split < (int)S) ? k0 + (int)a.keys_per_split : (int)S;
+  const int ntiles = (k1 - k0 + BN - 1) / BN;
   const uint16_t* c_seq = a.c_kv + (int64_t)b * S * R;
   const uint16_t* kp_seq = a.k_pe + (int64_t)b * S * DR;
 
@@ -328,7 +331,7 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
   // k1 read as zeros), so every phase costs each wave exactly NCOPY copies and
   // one vmcnt bound serves every phase.
   auto copy_tile = [&](int t, char* dst) {
-    const int64_t kb = k0 + (int64_t)t * BN;
+    const int kb = k0 + t * BN;
     const __amdgpu_buffer_rsrc_t rc = rows_rsrc(c_seq, kb, k1, R * 2);
     const __amdgpu_buffer_rsrc_t rp = rows_rsrc(kp_seq, kb, k1, DR * 2);
 #pragma unroll
@@ -378,7 +381,7 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
       }
     }
     if (do_scores && scoring) {
-      const int64_t kb = k0 + (int64_t)p * BN;
+      const int kb = k0 + p * BN;
       // scores S^T: keys kb + kt*16 + 4g + r, head 16 (hg0 + w) + j
       f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -389,7 +392,7 @@ __global__ __launch_bounds__(256, 1) void latent_attn_kernel(LatentArgs a) {
         s1 = mfma16(a1, qf[ks], s1);
       }
       // keys past this split's end (or the sequence's) take no weight
-      const int64_t lim = k1 - kb;  // keys kb .. kb + lim - 1 are visible (lim >= 1)
+      const int lim = k1 - kb;  // keys kb .. kb + lim - 1 are visible (lim >= 1)
       float x[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
