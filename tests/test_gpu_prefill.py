@@ -177,10 +177,15 @@ def test_chunked_prefill_matches_full_prefill_suffix():
 
 # (B, H, T, P): grids too small to fill the GPU, so the keys of each query
 # tile split over several workgroups: several ranges, a ragged last range,
-# causal tiles that see no key of the later ranges, 2..16 ranges (16, the
-# most the merge holds per row, for the last two).
+# 2..16 ranges (16, the most the merge holds per row, for the 100-query
+# cases). Each query tile's visible keys are cut into the plan's number of
+# near-equal ranges, so with few cached keys the first tiles see fewer key
+# tiles than there are ranges and their last ranges are empty: 2 x 2560
+# queries (5 ranges; tile 0 sees 4 key tiles), and 2500 queries over 60
+# cached keys (a ragged last tile; tile 0 sees 6). 7 query tiles (777
+# queries) give an odd count for the heavy-light pairing order.
 SPLIT = [(1, 2, 256, 3840), (1, 1, 100, 5000), (2, 4, 1024, 0), (1, 3, 777, 2000), (1, 8, 129, 1023),
-         (1, 1, 128, 8192), (1, 1, 100, 16000)]
+         (1, 1, 128, 8192), (1, 1, 100, 16000), (1, 2, 2560, 0), (1, 2, 2500, 60)]
 
 
 @pytest.mark.parametrize("B,H,T,P", SPLIT)
