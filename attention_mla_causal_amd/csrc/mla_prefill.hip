@@ -566,11 +566,11 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
       qt = k < h1 ? a.ntiles - 1 - k : k - h1;
     } else if (nwg % 8 == 0 && per % a.ntiles == 0 && (uneven || (per / a.ntiles) % 4 == 0)) {
       // An XCD deals its workgroups to its 32 CUs in turn, two resident per
-      // CU, so a window of four heads puts two tiles of one head on each CU
-      // of the first round. Same process, outputs bit-identical: 2048 queries
-      // over 14336 cached keys, 64 heads: 1203 us head by head (four heads
-      // per CU), 1185 us in windows of four (L2 misses +60%, still under a
-      // tenth of HBM peak); windows of two no faster than head by head,
+      // CU; the first window's tiles fill the first round and the next
+      // window's start heaviest first as slots free. Same process, outputs
+      // bit-identical: 2048 queries over 14336 cached keys, 64 heads: 1203 us
+      // head by head, 1185 us in windows of four (L2 misses +60%, still under
+      // a tenth of HBM peak); windows of two no faster than head by head,
       // windows of eight no faster than four with three times the misses of
       // head by head. 4096 queries, no cached keys: windows of four 1%
       // faster than all eight heads of the XCD at once, 35% fewer L2 misses.
