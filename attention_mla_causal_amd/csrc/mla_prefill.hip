@@ -763,9 +763,13 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   auto step = [&](int j, f32x16& cur, f32x16& nxt, bf16x8 (&pcur)[2],
                   const bf16x8 (&pprev)[2], const char* knxt, const char* vprev, char* kfree,
                   char* vfree, uint32_t& km_apply, uint32_t& km_load) {
-    // The two workgroups sharing a CU take turns at the higher issue priority.
-    // Left to age-based arbitration, the older one runs ~25% faster per step,
-    // and the round of workgroups that follows ends unevenly.
+    // Issue priority toggles with the parity of step and workgroup index, so
+    // workgroups sharing a CU take turns once their steps drift apart. Left
+    // to age-based arbitration, the older one ran ~25% faster per step and
+    // the round of workgroups that follows ended unevenly. (Same process: no
+    // s_setprio 1.7% slower on the chunked prefill; keying the parity so the
+    // two workgroups a CU receives first alternate from the start, 0.8%
+    // slower.)
     if ((j + blockIdx.x) & 1)
       __builtin_amdgcn_s_setprio(1);
     else
